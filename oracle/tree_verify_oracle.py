@@ -1,0 +1,294 @@
+"""CPU oracle for the tree-verification pass.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import or call this module; the product path (the HIP
+library and its Python binding) never does and shares no code with it.
+
+It is deliberately plain and slow: Python sets and loops for the tree logic,
+numpy float64 for attention, one (node, head) at a time, no blocking, no
+fusion, no reordering beyond what the definitions state.
+
+Pages followed:
+  [TSD] "Tree-Structured Speculative Decoding: How Multi-Candidate Trees and
+        Tree Attention Accelerate LLM Serving" (llms.blog), sections
+        "Tree Representation of Speculative Candidates", "The Tree Attention
+        Mechanism" (parts 1 Tree Flattening, 2 2D Causal Tree Mask,
+        3 Tree Positional IDs), "Verification and Acceptance Algorithms"
+        (Greedy Tree Verification) and "KV Cache Rollback".
+  [DT]  "DominoTree: Conditional Tree-Structured Drafting with Domino for
+        Speculative Decoding" (arXiv 2607.08642), section 2.1 and Appendix B.
+
+Readings taken where the pages leave a step open (each is also listed in the
+design notes):
+  * parent[i] == -1 means "child of the implicit root", the last verified
+    token; parents must precede children (parent[i] < i).
+  * level(i) = number of nodes on the root->i path (1 for a root child);
+    PosID(root) = P_b - 1 with 0-based positions, so pos[i] = P_b + level(i) - 1.
+  * the ancestor mask is packed LSB-first: bit (j & 63) of word (j >> 6) of
+    node i's row is set iff node j is i or an ancestor of i.
+  * tree node j's K/V live at cache row kv_start[b] + P_b + j (appended after
+    the prefix); a query head h reads KV head h // (Hq/Hkv).
+  * the greedy walk takes the lowest-index matching child; a negative draft
+    token (a dead leaf) never matches.
+  * compaction writes the accepted path's K/V to rows P_b .. P_b+L-1, in path
+    order, and leaves every other row untouched.
+
+Parity pins: every function here is checked in tests/test_oracle_pins.py
+against closed forms, hand-made fixtures from the pages' worked example,
+brute force on small inputs and invariants the pages fix.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# device-error encoding shared by contract with the C ABI: (code << 24) | index
+ERR_BAD_PARENT = 1   # parent[v] not in [-1, v)
+ERR_TOO_DEEP = 2     # level(i) > max_depth
+ERR_BAD_REQUEST = 3  # request sizes inconsistent with the host maxima / buffers
+
+
+def _enc(code: int, index: int) -> int:
+    return (code << 24) | (index & 0xFFFFFF)
+
+
+# ---------------------------------------------------------------------------
+# O-mask: ancestor sets, levels, position ids  ([TSD] "2D Causal Tree Mask",
+# "Tree Positional IDs")
+# ---------------------------------------------------------------------------
+
+def ancestor_set(parent, i: int) -> set:
+    """anc(i) = {i} U anc(parent[i]), anc(-1) = {} -- the set of tree nodes
+    node i may attend to ([TSD] "2D Causal Tree Mask": an ancestor or itself)."""
+    out = set()
+    v = int(i)
+    while v >= 0:
+        out.add(v)
+        v = int(parent[v])
+    return out
+
+
+def mask_build(parent, cu_nodes, prefix_len, max_nodes: int, max_depth: int):
+    """Packed ancestor bitmask, levels and position ids for a batch of trees.
+
+    Returns (anc uint64 [T, W], level int32 [T], pos int32 [T], err int) with
+    W = ceil(max_nodes / 64).  err is 0, or the largest encoded error
+    (code << 24 | global node index) over all nodes, where a node's walk to
+    the root reports the first bad parent it meets, or ERR_TOO_DEEP when its
+    level would exceed max_depth.  A request with more than max_nodes nodes
+    reports (ERR_BAD_REQUEST, b) and gets no outputs.
+    """
+    parent = np.asarray(parent)
+    cu = np.asarray(cu_nodes)
+    B = cu.shape[0] - 1
+    T = int(cu[-1]) if B >= 0 else 0
+    W = (max_nodes + 63) // 64
+    anc = np.zeros((T, W), dtype=np.uint64)
+    level = np.zeros(T, dtype=np.int32)
+    pos = np.zeros(T, dtype=np.int32)
+    err = 0
+    for b in range(B):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        n = hi - lo
+        if n < 0 or n > max_nodes:
+            err = max(err, _enc(ERR_BAD_REQUEST, b))
+            continue
+        par = parent[lo:hi]
+        for i in range(n):
+            # the walk toward the root, checking each parent pointer it follows
+            members = []
+            v = i
+            bad = None
+            while True:
+                members.append(v)
+                if len(members) > max_depth:
+                    bad = _enc(ERR_TOO_DEEP, lo + i)
+                    break
+                p = int(par[v])
+                if not (-1 <= p < v):
+                    bad = _enc(ERR_BAD_PARENT, lo + v)
+                    break
+                if p < 0:
+                    break
+                v = p
+            if bad is not None:
+                err = max(err, bad)
+                continue
+            words = [0] * W
+            for j in members:
+                words[j >> 6] |= 1 << (j & 63)
+            anc[lo + i] = np.array(words, dtype=np.uint64)
+            level[lo + i] = len(members)
+            pos[lo + i] = int(prefix_len[b]) + len(members) - 1
+    return anc, level, pos, err
+
+
+def unpack_mask(anc_row, n: int) -> np.ndarray:
+    """Bool vector of length n from one packed row (LSB-first words)."""
+    out = np.zeros(n, dtype=bool)
+    for j in range(n):
+        out[j] = (int(anc_row[j >> 6]) >> (j & 63)) & 1
+    return out
+
+
+# ---------------------------------------------------------------------------
+# O-attn: per-node tree attention  ([TSD] "The Tree Attention Mechanism")
+# ---------------------------------------------------------------------------
+
+def key_rows(parent, b_kv_start: int, b_prefix: int, i: int) -> np.ndarray:
+    """Cache rows node i attends to: the whole prefix, then its own
+    ancestors-or-self among the tree rows appended after the prefix."""
+    tree = sorted(ancestor_set(parent, i))
+    return np.array(list(range(b_kv_start, b_kv_start + b_prefix))
+                    + [b_kv_start + b_prefix + j for j in tree], dtype=np.int64)
+
+
+def attention_row(q_vec, k_rows, v_rows, scale: float) -> np.ndarray:
+    """softmax_t(scale * q . k_t) weighted sum of v_t, all in float64."""
+    q = np.asarray(q_vec, dtype=np.float64)
+    K = np.asarray(k_rows, dtype=np.float64)
+    V = np.asarray(v_rows, dtype=np.float64)
+    s = scale * (K @ q)
+    s = s - s.max()
+    p = np.exp(s)
+    p = p / p.sum()
+    return p @ V
+
+
+def tree_attention(q, k, v, parent, cu_nodes, kv_start, prefix_len, scale: float,
+                   rows=None) -> np.ndarray:
+    """o[t, h] for every global node t and query head h (or only for the
+    (t, h) pairs listed in `rows`, returned in that order as [len(rows), d]).
+
+    q [T, Hq, d]; k, v [kv_rows, Hkv, d]; KV head of h is h // (Hq // Hkv).
+    """
+    q = np.asarray(q)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    cu = np.asarray(cu_nodes)
+    owner = np.searchsorted(cu, np.arange(T), side="right") - 1
+    if rows is None:
+        rows = [(t, h) for t in range(T) for h in range(Hq)]
+        out = np.zeros((T, Hq, d), dtype=np.float64)
+        full = True
+    else:
+        out = np.zeros((len(rows), d), dtype=np.float64)
+        full = False
+    cache = {}
+    for n, (t, h) in enumerate(rows):
+        b = int(owner[t])
+        i = int(t - cu[b])
+        g = h // G
+        key = (t, g)
+        if key not in cache:
+            cache.clear()
+            idx = key_rows(parent[int(cu[b]):int(cu[b + 1])], int(kv_start[b]), int(prefix_len[b]), i)
+            cache[key] = (np.asarray(k[idx, g, :], np.float64), np.asarray(v[idx, g, :], np.float64))
+        K, V = cache[key]
+        o = attention_row(q[t, h, :], K, V, scale)
+        if full:
+            out[t, h] = o
+        else:
+            out[n] = o
+    return out
+
+
+# ---------------------------------------------------------------------------
+# O-accept: greedy acceptance  ([TSD] "Verification and Acceptance
+# Algorithms", Greedy Tree Verification)
+# ---------------------------------------------------------------------------
+
+def accept_walk_one(parent, draft, target, root_target: int, max_depth: int):
+    """The greedy walk for one request: starting at the implicit root with the
+    target's choice there, repeatedly look for a child (lowest index first)
+    whose draft token equals the target's current choice; stop when none does
+    or the node is a leaf.  Returns (path node indices, next token)."""
+    n = len(parent)
+    want = int(root_target)
+    cur = -1
+    path = []
+    while len(path) < max_depth:
+        kids = [j for j in range(n) if int(parent[j]) == cur]
+        match = None
+        for c in kids:                      # ascending index
+            if int(draft[c]) >= 0 and int(draft[c]) == want:
+                match = c
+                break
+        if match is None:
+            break
+        path.append(match)
+        cur = match
+        want = int(target[match])
+    return path, want
+
+
+def accept_bruteforce_one(parent, draft, target, root_target: int):
+    """Independent formulation: a node is 'valid' iff every node u on its
+    root->node path carries the token the target chose at u's parent (the
+    root's choice for a root child).  The accepted node is the deepest valid
+    node, lowest index among equals; next token = its target (or the root's
+    choice when nothing is valid).  With distinct sibling tokens the valid set
+    is a chain and this equals the walk."""
+    n = len(parent)
+    best = None
+    best_len = 0
+    for v in range(n):
+        chain = []
+        u = v
+        while u >= 0:
+            chain.append(u)
+            u = int(parent[u])
+        chain.reverse()
+        ok = True
+        for u in chain:
+            p = int(parent[u])
+            want = int(root_target) if p < 0 else int(target[p])
+            if int(draft[u]) < 0 or int(draft[u]) != want:
+                ok = False
+                break
+        if ok and len(chain) > best_len:
+            best, best_len = chain, len(chain)
+    if best is None:
+        return [], int(root_target)
+    return best, int(target[best[-1]])
+
+
+def accept_greedy(parent, draft, target, root_target, cu_nodes, max_depth: int):
+    """Batched walk.  Returns (accept_len [B], accept_idx [B, max_depth] padded
+    with -1, next_token [B]); indices are request-local."""
+    cu = np.asarray(cu_nodes)
+    B = cu.shape[0] - 1
+    alen = np.zeros(B, dtype=np.int32)
+    aidx = np.full((B, max_depth), -1, dtype=np.int32)
+    nxt = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        path, tok = accept_walk_one(parent[lo:hi], draft[lo:hi], target[lo:hi],
+                                    int(root_target[b]), max_depth)
+        alen[b] = len(path)
+        aidx[b, :len(path)] = path
+        nxt[b] = tok
+    return alen, aidx, nxt
+
+
+# ---------------------------------------------------------------------------
+# O-compact: KV rollback as a physical gather  ([TSD] "KV Cache Rollback")
+# ---------------------------------------------------------------------------
+
+def kv_compact(k, v, kv_start, prefix_len, accept_len, accept_idx):
+    """Copy of the caches where, for each request, row P+j (j < L) holds what
+    row P+idx[j] held before the call; every other row is unchanged.
+    Returns (k', v', new_kv_len [B])."""
+    k2 = np.array(k, copy=True)
+    v2 = np.array(v, copy=True)
+    B = len(prefix_len)
+    new_len = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        base = int(kv_start[b]) + int(prefix_len[b])
+        L = int(accept_len[b])
+        for j in range(L):
+            src = base + int(accept_idx[b][j])
+            k2[base + j] = k[src]
+            v2[base + j] = v[src]
+        new_len[b] = int(prefix_len[b]) + L
+    return k2, v2, new_len
