@@ -1,0 +1,274 @@
+"""Benchmark of the tree-verification pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+
+One step = the whole pass over one batch of synthetic inputs already resident
+in HBM: tree_mask_build -> tree_attn_verify -> tree_accept_greedy ->
+kv_compact_path, each through the C ABI.  The default workload is the
+Qwen3-8B-shaped layer (c3: 32 query / 8 KV heads, head_dim 128, prefix 4096,
+best-first tree of 128 nodes), the configuration whose description includes
+all four steps; --workload c2/c4/c5 measure the others the same way.
+
+Timing:
+  * cold cache: inputs rotate over R copies with R x footprint >= 512 MiB, so
+    the 256 MiB Infinity Cache cannot hold them between uses;
+  * a spin kernel queued ahead of the timed region keeps the GPU busy while
+    the host enqueues every timed step, so the steps (and the HIP events
+    around each tree_attn_verify call, on the launching stream) measure GPU
+    time rather than Python launch gaps;
+  * value = verified tree tokens (tree nodes) per second over the K steps.
+
+The printed JSON line carries the roofline of tree_attn_verify (algorithmic
+bytes and flops per call over its measured average duration, against the
+MI355X peaks) and the CPU oracle's rate on a bounded sample ('cpu_baseline').
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from tree_attention_verification_bitmask_amd import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+METRIC = "verified tree-tokens/sec per GPU; % of HBM-BW / bf16-MFMA roofline"
+COLD_BYTES = 512 << 20
+
+
+def algorithmic_work(wl):
+    """Bytes and flops the method itself must move / compute per call of
+    tree_attn_verify: K+V of every key row read once, Q read and O written
+    once; 2 flops per multiply-add for Q.K and P.V over each node's own key
+    set (prefix plus ancestors-or-self)."""
+    es = 2 if wl.dtype == "bf16" else 4
+    byts = 0
+    flops = 0
+    for b in range(wl.batch):
+        n = int(wl.cu_nodes[b + 1] - wl.cu_nodes[b])
+        P = int(wl.prefix_len[b])
+        levels = int(W._depths(wl.parent[wl.nodes_of(b)]).sum()) if n else 0
+        byts += (P + n) * wl.hkv * wl.d * 2 * es + 2 * n * wl.hq * wl.d * es
+        flops += 4 * wl.hq * wl.d * (n * P + levels)
+    return byts, flops
+
+
+def cpu_baseline(wl, budget_s: float = 15.0):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    mask, acceptance and compaction for the whole batch, and attention for as
+    many whole nodes (all heads) as fit in about budget_s seconds."""
+    from oracle import tree_verify_oracle as O
+    try:
+        import threadpoolctl
+        blas = [p for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+        threads = max([p["num_threads"] for p in blas] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    t0 = time.perf_counter()
+    O.mask_build(wl.parent, wl.cu_nodes, wl.prefix_len, wl.max_nodes, wl.max_depth)
+    alen, aidx, _ = O.accept_greedy(wl.parent, wl.draft, wl.target, wl.root_target, wl.cu_nodes, wl.max_depth)
+    O.kv_compact(wl.k, wl.v, wl.kv_start, wl.prefix_len, alen, aidx)
+    t_rest = time.perf_counter() - t0
+    done = 0
+    t1 = time.perf_counter()
+    while done < wl.total_nodes and time.perf_counter() - t1 < budget_s:
+        O.tree_attention(wl.q, wl.k, wl.v, wl.parent, wl.cu_nodes, wl.kv_start, wl.prefix_len, wl.scale,
+                         rows=[(done, h) for h in range(wl.hq)])
+        done += 1
+    t_attn = time.perf_counter() - t1
+    per_node = t_attn / done + t_rest / wl.total_nodes
+    return {"value": 1.0 / per_node, "unit": "tree-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"{wl.name} seed {wl.seed}: float64 oracle attention for nodes 0..{done - 1} of "
+                       f"{wl.total_nodes} (all {wl.hq} heads, {t_attn:.1f} s) plus mask, acceptance and "
+                       f"compaction of the whole batch ({t_rest:.2f} s, charged per node)"),
+            "os_cpu_count": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c3", choices=sorted(W.CONFIGS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this pass is built and timed on a single MI355X); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+
+    import torch
+    from tree_attention_verification_bitmask_amd import binding as BND
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    L = BND.lib()  # raises if the HIP library is missing
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    wl = W.make_workload(args.workload, seed=args.seed, force_path=True)
+    fdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    code = BND.TV_BF16 if wl.dtype == "bf16" else BND.TV_F32
+    es = 2 if wl.dtype == "bf16" else 4
+    T, B = wl.total_nodes, wl.batch
+
+    def i32(x):
+        return torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(dev)
+
+    parent, cu, P, ks = i32(wl.parent), i32(wl.cu_nodes), i32(wl.prefix_len), i32(wl.kv_start)
+    draft, target, root = i32(wl.draft), i32(wl.target), i32(wl.root_target)
+    q0 = torch.from_numpy(wl.q).to(dev).to(fdt).contiguous()
+    k0 = torch.from_numpy(wl.k).to(dev).to(fdt).contiguous()
+    v0 = torch.from_numpy(wl.v).to(dev).to(fdt).contiguous()
+    footprint = (q0.numel() + k0.numel() + v0.numel() + q0.numel()) * es
+    R = max(1, math.ceil(COLD_BYTES / footprint))
+    sets = [(q0.clone(), k0.clone(), v0.clone()) for _ in range(R)]
+    del q0, k0, v0
+    words = (wl.max_nodes + 63) // 64
+    anc = torch.empty((T, words), dtype=torch.int64, device=dev)
+    level = torch.empty(T, dtype=torch.int32, device=dev)
+    pos = torch.empty(T, dtype=torch.int32, device=dev)
+    outs = [torch.empty((T, wl.hq, wl.d), dtype=fdt, device=dev) for _ in range(R)]
+    alen = torch.empty(B, dtype=torch.int32, device=dev)
+    aidx = torch.empty((B, wl.max_depth), dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    newlen = torch.empty(B, dtype=torch.int32, device=dev)
+    err = torch.zeros(4, dtype=torch.int32, device=dev)
+    ws_bytes = BND.tree_attn_verify_workspace_size(B, T, wl.max_nodes, wl.max_prefix, wl.hq, wl.hkv, wl.d, code)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = C_void(stream.cuda_stream)
+
+    # raw C calls with pre-marshalled arguments (the binding's checks are
+    # done once here, by the shapes above)
+    P_ = lambda t: C_void(t.data_ptr())  # noqa: E731
+    mask_args = (P_(parent), P_(cu), P_(P), B, T, wl.max_nodes, wl.max_depth, P_(anc), P_(level), P_(pos),
+                 C_void(err.data_ptr()), sp)
+    attn_args = []
+    for (q, k, v), o in zip(sets, outs):
+        attn_args.append((P_(q), P_(k), P_(v), P_(cu), P_(ks), P_(P), P_(anc), B, T, wl.max_nodes, wl.max_prefix,
+                          k.shape[0], wl.hq, wl.hkv, wl.d, float(wl.scale), code, P_(o), P_(ws), ws.numel(),
+                          C_void(err.data_ptr() + 4), sp))
+    acc_args = (P_(parent), P_(draft), P_(target), P_(root), P_(cu), B, T, wl.max_depth, P_(alen), P_(aidx),
+                P_(nxt), C_void(err.data_ptr() + 8), sp)
+    cmp_args = [(P_(k), P_(v), P_(cu), P_(ks), P_(P), P_(alen), P_(aidx), B, T, wl.max_depth, k.shape[0], wl.hkv,
+                 wl.d, code, P_(newlen), C_void(err.data_ptr() + 12), sp) for (q, k, v) in sets]
+
+    def step(i, ev=None):
+        r = i % R
+        st = L.tree_mask_build(*mask_args)
+        if ev is not None:
+            ev[0].record(stream)
+        st |= L.tree_attn_verify(*attn_args[r])
+        if ev is not None:
+            ev[1].record(stream)
+        st |= L.tree_accept_greedy(*acc_args)
+        st |= L.kv_compact_path(*cmp_args[r])
+        return st
+
+    for i in range(args.warmup):
+        if step(i):
+            raise RuntimeError("a call was rejected during warmup")
+    torch.cuda.synchronize()
+    if int(err.abs().sum().item()) != 0:
+        raise RuntimeError(f"device error words {err.tolist()}")
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # calibrate the spin kernel, then queue enough spin to cover the host's
+    # enqueue time of the timed steps (measured during warmup, with margin)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    torch.cuda._sleep(1 << 22)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    cycles_per_ms = (1 << 22) / max(c0.elapsed_time(c1), 1e-3)
+    t0 = time.perf_counter()
+    for i in range(8):
+        step(i)
+    torch.cuda.synchronize()
+    host_ms_per_step = (time.perf_counter() - t0) * 1e3 / 8
+    spin_ms = min(5000.0, max(20.0, 3.0 * K * host_ms_per_step))
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(cycles_per_ms * spin_ms))
+    start.record(stream)
+    t_host0 = time.perf_counter()
+    status = 0
+    for i in range(K):
+        status |= step(args.warmup + i, evs[i])
+    end.record(stream)
+    t_host_enq = time.perf_counter() - t_host0
+    torch.cuda.synchronize()
+    if status:
+        raise RuntimeError("a call was rejected in the timed region")
+    if int(err.abs().sum().item()) != 0:
+        raise RuntimeError(f"device error words {err.tolist()}")
+    total_ms = start.elapsed_time(end)
+    attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_step = total_ms / K
+    attn_us = float(attn_ms.mean() * 1e3)
+
+    byts, flops = algorithmic_work(wl)
+    ai = flops / byts
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if wl.dtype == "bf16" and ai >= ridge:
+        roof = {"bound": "mfma", "achieved": flops / (attn_us * 1e-6) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": byts / (attn_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof.update({"kernel": "tree_attn_verify", "avg_us": attn_us,
+                 "p10_us": float(np.percentile(attn_ms, 10) * 1e3),
+                 "p90_us": float(np.percentile(attn_ms, 90) * 1e3),
+                 "alg_bytes": byts, "alg_flops": flops, "arith_intensity": ai,
+                 "achieved_gbs": byts / (attn_us * 1e-6) / 1e9,
+                 "achieved_tflops": flops / (attn_us * 1e-6) / 1e12})
+
+    line = {
+        "metric": METRIC,
+        "value": T / (ms_step * 1e-3),
+        "unit": "tree-tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {W.CONFIGS[wl.name]['desc']}", "seed": wl.seed, "batch": B,
+                   "tree_nodes": T, "max_prefix": wl.max_prefix, "hq": wl.hq, "hkv": wl.hkv,
+                   "head_dim": wl.d, "max_depth": wl.max_depth, "cold_cache_sets": R,
+                   "workspace_bytes": ws_bytes, "host_enqueue_ms": t_host_enq * 1e3,
+                   "spin_ahead_ms": spin_ms},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def C_void(x):
+    import ctypes
+    return ctypes.c_void_p(x)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,212 @@
+/*
+ * treeverify.h -- C ABI of libtreeverify, the MI355X (gfx950) tree-verification
+ * pass of tree-structured speculative decoding.
+ *
+ * Pages cited:
+ *   [TSD] "Tree-Structured Speculative Decoding: How Multi-Candidate Trees and
+ *         Tree Attention Accelerate LLM Serving" (llms.blog).
+ *   [DT]  "DominoTree: Conditional Tree-Structured Drafting with Domino for
+ *         Speculative Decoding" (arXiv 2607.08642).
+ *
+ * A batch holds B requests.  Request b owns:
+ *   - draft-tree nodes cu_nodes[b] .. cu_nodes[b+1]-1 of every per-node array
+ *     (T = cu_nodes[B] nodes in total; N_b = cu_nodes[b+1] - cu_nodes[b]);
+ *   - cache rows kv_start[b] .. kv_start[b] + P_b + N_b - 1 of the K and V
+ *     caches: first its prefix (P_b = prefix_len[b] cached tokens), then its
+ *     tree node j at row kv_start[b] + P_b + j (tree K/V are appended after the
+ *     prefix, [TSD] "KV Cache Rollback").
+ * parent[] holds request-local indices: parent[i] < i, or -1 when node i hangs
+ * directly under the implicit root, the last verified token ([TSD] "Tree
+ * Representation of Speculative Candidates"; parents precede children as in
+ * [DT] Appendix B, "Frontier ledger and selection").  A tree whose own root is
+ * a node (a bonus token verified in the same pass) is node 0 with parent -1.
+ *
+ * Conventions for every call:
+ *   - All array pointers are caller-owned DEVICE memory on the current HIP
+ *     device, contiguous, in the layouts stated.  The library allocates
+ *     nothing and keeps no state; calls are thread-safe across streams.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on it and returns; nothing synchronises with the host.
+ *   - Sizes the host knows (batch, totals, maxima) are passed by value so the
+ *     launch needs no device-to-host copy.  Arguments are checked on the host
+ *     BEFORE anything is enqueued; a non-zero tv_status means nothing was
+ *     enqueued and no output was touched.
+ *   - Device-side checks (values held in device arrays) report through the
+ *     optional int32 `err` word: 0 = no error, else (code << 24) | index with
+ *     the TV_DEVERR_* codes below; when several errors occur the word ends up
+ *     holding the largest encoded value (an atomic max), so the result does
+ *     not depend on thread timing.  The caller zeroes it beforehand.  A
+ *     request that fails a device-side check gets unspecified outputs, but
+ *     every memory access stays inside the buffers the sizes describe.
+ *   - Element types: tv_dtype selects fp32 or bf16 (bf16 = the upper 16 bits
+ *     of an IEEE float32, round-to-nearest-even on output).  Attention
+ *     accumulates in fp32 for both.
+ */
+#ifndef TREEVERIFY_H
+#define TREEVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TV_OK = 0,
+    TV_ERR_NULL = 1,      /* a required pointer is NULL                              */
+    TV_ERR_SHAPE = 2,     /* inconsistent or negative sizes (e.g. hq % hkv != 0)      */
+    TV_ERR_DTYPE = 3,     /* unsupported dtype / head_dim                             */
+    TV_ERR_LIMIT = 4,     /* a size above a library limit (TV_MAX_*)                  */
+    TV_ERR_WORKSPACE = 5, /* workspace smaller than tree_attn_verify_workspace_size() */
+    TV_ERR_LAUNCH = 6,    /* the HIP runtime refused a launch                         */
+    TV_ERR_ALIGN = 7      /* a pointer breaks the stated alignment                    */
+} tv_status;
+
+typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
+
+#define TV_MAX_NODES 1024          /* nodes per request                   */
+#define TV_MAX_DEPTH 64            /* levels per tree / accepted tokens   */
+#define TV_MAX_TOTAL_NODES 16777215 /* nodes per batch (24-bit error index) */
+
+/* device error codes (the top byte of the err word) */
+#define TV_DEVERR_BAD_PARENT 1  /* parent[v] not in [-1, v); index = global node v       */
+#define TV_DEVERR_TOO_DEEP 2    /* level(i) > max_depth; index = global node i           */
+#define TV_DEVERR_BAD_REQUEST 3 /* request sizes disagree with the host sizes; index = b */
+#define TV_DEVERR_BAD_PATH 4    /* accepted path entry out of range; index = b           */
+
+/* Human-readable name of a tv_status value (static string). */
+const char *tv_status_string(int status);
+
+/* Version of this ABI; bumped on any signature change. */
+int tv_abi_version(void);
+
+/*
+ * tree_mask_build -- packed ancestor mask, levels and position ids.
+ *
+ * Defines: [TSD] "The Tree Attention Mechanism", part 2 "2D Causal Tree Mask"
+ * (node i may attend to node j iff j is i or an ancestor of i) and part 3
+ * "Tree Positional IDs" (a node's position is the root's position plus its
+ * depth).  With the root at position P_b - 1 (the last cached token, 0-based),
+ * pos[i] = P_b + level[i] - 1, where level[i] counts the nodes on the
+ * root->i path (1 for a root child); a chain gets P_b, P_b+1, ..., the
+ * ordinary autoregressive positions.
+ *
+ * In:  parent [T] int32, cu_nodes [B+1] int32, prefix_len [B] int32.
+ *      batch = B >= 0; total_nodes = T (the length of the per-node arrays);
+ *      max_nodes >= every N_b, 1 <= max_nodes <= TV_MAX_NODES;
+ *      1 <= max_depth <= TV_MAX_DEPTH.
+ * Out: anc_bits [T, W] uint64 with W = ceil(max_nodes / 64): bit (j & 63) of
+ *      word (j >> 6) of row t is set iff request-local node j is t's node or
+ *      one of its ancestors (LSB first; no bit at or beyond N_b);
+ *      level [T] int32; pos_ids [T] int32.  8-byte aligned anc_bits.
+ * err: BAD_PARENT, TOO_DEEP (the node's walk meets them in that order, the
+ *      depth check first at each step), BAD_REQUEST (cu_nodes not
+ *      non-decreasing within [0, T], N_b > max_nodes, or P_b < 0).
+ *      A node with an error gets zero bits, level 0 and pos 0.
+ */
+tv_status tree_mask_build(const int32_t *parent, const int32_t *cu_nodes, const int32_t *prefix_len,
+                          int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_depth,
+                          uint64_t *anc_bits, int32_t *level, int32_t *pos_ids, int32_t *err,
+                          void *stream);
+
+/*
+ * tree_attn_verify_workspace_size -- bytes of device workspace the call below
+ * needs for these host sizes (0 when it needs none).  Pure host arithmetic.
+ */
+size_t tree_attn_verify_workspace_size(int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                                       int32_t max_prefix, int32_t hq, int32_t hkv, int32_t head_dim,
+                                       tv_dtype dtype);
+
+/*
+ * tree_attn_verify -- attention of every tree node over its request's prefix
+ * and its own ancestors-or-self.
+ *
+ * Defines: [TSD] "The Tree Attention Mechanism": the flattened tree is
+ * processed in one pass next to the prefix KV cache (part 1 "Tree
+ * Flattening"); every node sees the shared prompt history and the nodes on its
+ * own branch, never a sibling branch (part 2 "2D Causal Tree Mask"); [DT]
+ * section 2.4 calls this verification with an ancestor-only mask.  For node i
+ * of request b and query head h, with KV head g = h / (hq / hkv):
+ *   out[i,h] = sum_t softmax_t(scale * q[i,h] . k[t,g]) v[t,g]
+ *   over t in {kv_start[b] + 0 .. P_b-1} U {kv_start[b] + P_b + j : j in anc(i)}.
+ * Q and K arrive with positions already applied (pos_ids above feed the
+ * caller's RoPE).
+ *
+ * In:  q [T, hq, head_dim]; k_cache, v_cache [kv_rows, hkv, head_dim]
+ *      (dtype elements, 16-byte aligned); cu_nodes, kv_start, prefix_len
+ *      as above; anc_bits from tree_mask_build with the same max_nodes.
+ *      max_prefix >= every P_b; kv_rows = rows of each cache.
+ *      head_dim in {64, 128}; hq % hkv == 0; scale > 0 (usually 1/sqrt(d)).
+ * Out: out [T, hq, head_dim] in dtype (16-byte aligned).
+ * workspace: at least tree_attn_verify_workspace_size(...) bytes, 256-byte
+ *      aligned (may be NULL when that size is 0); contents on entry do not
+ *      matter and are scratch afterwards.  Calls sharing one workspace must
+ *      be ordered on one stream.
+ * err: BAD_REQUEST for a request whose N_b > max_nodes, P_b > max_prefix,
+ *      P_b < 0, or rows beyond kv_rows; its output rows are not written.
+ */
+tv_status tree_attn_verify(const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *cu_nodes, const int32_t *kv_start, const int32_t *prefix_len,
+                           const uint64_t *anc_bits, int32_t batch, int32_t total_nodes,
+                           int32_t max_nodes, int32_t max_prefix, int64_t kv_rows, int32_t hq,
+                           int32_t hkv, int32_t head_dim, float scale, tv_dtype dtype, void *out,
+                           void *workspace, size_t workspace_bytes, int32_t *err, void *stream);
+
+/*
+ * tree_accept_greedy -- temperature-0 acceptance walk.
+ *
+ * Defines: [TSD] "Verification and Acceptance Algorithms", greedy tree
+ * verification: from the root, look among the current node's children for
+ * the one whose draft token equals the target's argmax at the current node;
+ * on a match append it and move there, otherwise (or at a leaf) stop; the
+ * next starting token is the target's argmax at the last node reached.
+ * Readings: the root is implicit and its argmax is root_target[b]; among
+ * several matching siblings the lowest index wins; a negative draft token
+ * (a dead leaf, [DT] Appendix B) never matches; the walk stops after
+ * max_depth accepted nodes.
+ *
+ * In:  parent, draft_tokens, target_tokens [T] int32 (target_tokens[t] = the
+ *      target's argmax after node t); root_target [B]; cu_nodes [B+1].
+ * Out: accept_len [B] int32 (0..max_depth); accept_idx [B, max_depth] int32,
+ *      request-local node indices in path order, -1 after the path;
+ *      next_token [B] int32.
+ * err: BAD_REQUEST (cu_nodes outside [0, T] or decreasing).
+ */
+tv_status tree_accept_greedy(const int32_t *parent, const int32_t *draft_tokens,
+                             const int32_t *target_tokens, const int32_t *root_target,
+                             const int32_t *cu_nodes, int32_t batch, int32_t total_nodes,
+                             int32_t max_depth, int32_t *accept_len, int32_t *accept_idx,
+                             int32_t *next_token, int32_t *err, void *stream);
+
+/*
+ * kv_compact_path -- commit the accepted path's K/V, discard the rest.
+ *
+ * Defines: [TSD] "KV Cache Rollback": the tree's K/V were appended to the
+ * cache for the pass; afterwards the unaccepted nodes are dropped.  Done here
+ * as a physical gather so the cache ends up as token-by-token decoding of the
+ * accepted path would have left it: for j < L_b = accept_len[b], row
+ * kv_start[b] + P_b + j receives (all hkv heads) what row
+ * kv_start[b] + P_b + accept_idx[b, j] held before the call.  No other row is
+ * written.  Not idempotent: a second call on the same cache gathers again.
+ * new_kv_len[b] = P_b + L_b.
+ *
+ * In/out: k_cache, v_cache [kv_rows, hkv, head_dim] (16-byte aligned).
+ * In:  cu_nodes, kv_start, prefix_len, accept_len [B], accept_idx
+ *      [B, max_depth] as produced by tree_accept_greedy.
+ * Out: new_kv_len [B] int32.
+ * err: BAD_REQUEST (sizes as for tree_attn_verify, or L_b outside
+ *      [0, max_depth]); BAD_PATH (an accept_idx entry outside [0, N_b)).
+ *      Such a request is left untouched.
+ */
+tv_status kv_compact_path(void *k_cache, void *v_cache, const int32_t *cu_nodes,
+                          const int32_t *kv_start, const int32_t *prefix_len,
+                          const int32_t *accept_len, const int32_t *accept_idx, int32_t batch,
+                          int32_t total_nodes, int32_t max_depth, int64_t kv_rows, int32_t hkv,
+                          int32_t head_dim, tv_dtype dtype, int32_t *new_kv_len, int32_t *err,
+                          void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TREEVERIFY_H */

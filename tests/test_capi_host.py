@@ -1,0 +1,139 @@
+"""The C-ABI library on the host: it loads, exports every function the header
+declares, and rejects bad arguments before enqueuing anything (these checks
+never reach the HIP runtime, so they run without a GPU).  Pointers passed
+here are never dereferenced: every call either fails a host check or has an
+empty batch."""
+import ctypes as C
+import os
+
+import pytest
+
+from tree_attention_verification_bitmask_amd import binding as BND
+
+OK, NULL, SHAPE, DTYPE, LIMIT, WS, LAUNCH, ALIGN = range(8)
+FAKE = C.c_void_p(0x10000)      # aligned, never dereferenced
+FAKE_ODD = C.c_void_p(0x10004)  # 4-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(BND.LIB_PATH):
+        from tree_attention_verification_bitmask_amd import build
+        build.build()
+    return BND.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = BND.header_functions()
+    assert set(names) >= {"tree_mask_build", "tree_attn_verify", "tree_accept_greedy",
+                          "kv_compact_path", "tree_attn_verify_workspace_size",
+                          "tv_status_string", "tv_abi_version"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.tv_abi_version() == 1
+    assert L.tv_status_string(0) == b"TV_OK"
+    assert b"NULL" in L.tv_status_string(NULL)
+
+
+def mask(L, parent=FAKE, cu=FAKE, P=FAKE, B=1, T=16, max_nodes=16, max_depth=8, anc=FAKE,
+         lev=FAKE, pos=FAKE):
+    return L.tree_mask_build(parent, cu, P, B, T, max_nodes, max_depth, anc, lev, pos, None, None)
+
+
+def test_mask_build_host_checks(L):
+    assert mask(L, cu=None) == NULL
+    assert mask(L, parent=None) == NULL
+    assert mask(L, anc=None) == NULL
+    assert mask(L, B=-1) == SHAPE
+    assert mask(L, T=-1) == SHAPE
+    assert mask(L, max_nodes=0) == SHAPE
+    assert mask(L, max_depth=0) == SHAPE
+    assert mask(L, max_nodes=1025) == LIMIT
+    assert mask(L, max_depth=65) == LIMIT
+    assert mask(L, T=1 << 24) == LIMIT
+    assert mask(L, anc=FAKE_ODD) == ALIGN
+    assert mask(L, B=0) == OK                    # empty batch: nothing to do
+    assert mask(L, parent=None, anc=None, lev=None, pos=None, T=0) == OK
+
+
+def attn(L, q=FAKE, k=FAKE, v=FAKE, cu=FAKE, ks=FAKE, P=FAKE, anc=FAKE, B=1, T=128, max_nodes=128,
+         max_prefix=4096, rows=4224, hq=32, hkv=8, d=128, scale=0.088, dtype=1, out=FAKE, ws=FAKE,
+         ws_bytes=1 << 40):
+    return L.tree_attn_verify(q, k, v, cu, ks, P, anc, B, T, max_nodes, max_prefix, rows, hq, hkv, d,
+                              scale, dtype, out, ws, ws_bytes, None, None)
+
+
+def test_attn_host_checks(L):
+    assert attn(L, q=None) == NULL
+    assert attn(L, out=None) == NULL
+    assert attn(L, anc=None) == NULL
+    assert attn(L, k=None) == NULL
+    assert attn(L, cu=None) == NULL
+    assert attn(L, hq=30) == SHAPE               # hq % hkv != 0
+    assert attn(L, hkv=0) == SHAPE
+    assert attn(L, scale=0.0) == SHAPE
+    assert attn(L, scale=float("nan")) == SHAPE
+    assert attn(L, max_prefix=-1) == SHAPE
+    assert attn(L, rows=-5) == SHAPE
+    assert attn(L, d=96) == DTYPE
+    assert attn(L, dtype=7) == DTYPE
+    assert attn(L, max_nodes=2048) == LIMIT
+    assert attn(L, q=FAKE_ODD) == ALIGN
+    assert attn(L, out=FAKE_ODD) == ALIGN
+    need = L.tree_attn_verify_workspace_size(1, 128, 128, 4096, 32, 8, 128, 1)
+    assert need > 0
+    assert attn(L, ws=None, ws_bytes=0) == WS
+    assert attn(L, ws_bytes=need - 1) == WS
+    assert attn(L, ws=C.c_void_p(0x10010), ws_bytes=need) == ALIGN
+    assert attn(L, B=0, T=0) == OK
+
+
+def test_workspace_sizes(L):
+    # fp32 and tiny trees take the VALU path, which needs no workspace
+    assert L.tree_attn_verify_workspace_size(1, 16, 16, 128, 2, 1, 64, 0) == 0
+    assert L.tree_attn_verify_workspace_size(1, 4, 4, 128, 8, 8, 128, 1) == 0   # 4 rows per KV head
+    # bf16 Qwen3-shaped layers split the key axis and need fp32 partials
+    for B, T, n, P in ((1, 64, 64, 1024), (1, 128, 128, 4096), (1, 256, 256, 8192), (8, 1024, 128, 8192)):
+        ws = L.tree_attn_verify_workspace_size(B, T, n, P, 32, 8, 128, 1)
+        assert ws % 8 == 0 and ws >= 0
+    # invalid sizes report 0
+    assert L.tree_attn_verify_workspace_size(1, 16, 16, 128, 3, 2, 64, 1) == 0
+
+
+def accept(L, parent=FAKE, dr=FAKE, tg=FAKE, root=FAKE, cu=FAKE, B=1, T=16, D=16, alen=FAKE,
+           aidx=FAKE, nxt=FAKE):
+    return L.tree_accept_greedy(parent, dr, tg, root, cu, B, T, D, alen, aidx, nxt, None, None)
+
+
+def test_accept_host_checks(L):
+    assert accept(L, parent=None) == NULL
+    assert accept(L, root=None) == NULL
+    assert accept(L, aidx=None) == NULL
+    assert accept(L, D=0) == SHAPE
+    assert accept(L, D=65) == LIMIT
+    assert accept(L, B=-2) == SHAPE
+    assert accept(L, B=0) == OK
+
+
+def compact(L, k=FAKE, v=FAKE, cu=FAKE, ks=FAKE, P=FAKE, alen=FAKE, aidx=FAKE, B=1, T=16, D=16,
+            rows=1000, hkv=8, d=128, dtype=1, nl=FAKE):
+    return L.kv_compact_path(k, v, cu, ks, P, alen, aidx, B, T, D, rows, hkv, d, dtype, nl, None, None)
+
+
+def test_compact_host_checks(L):
+    assert compact(L, k=None) == NULL
+    assert compact(L, aidx=None) == NULL
+    assert compact(L, nl=None) == NULL
+    assert compact(L, d=80) == DTYPE
+    assert compact(L, dtype=5) == DTYPE
+    assert compact(L, D=0) == SHAPE
+    assert compact(L, D=100) == LIMIT
+    assert compact(L, k=FAKE_ODD) == ALIGN
+    assert compact(L, B=0) == OK
+
+
+def test_binding_refuses_cpu_tensors(L):
+    import torch
+    x = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        BND.tree_mask_build(x, x, x, 4, 4)

@@ -1,0 +1,213 @@
+"""Thin ctypes binding of libtreeverify (include/treeverify.h).
+
+Each function has the C entry point's name and only marshals arguments:
+torch tensors -> device pointers, the current HIP stream -> hipStream_t, and
+a non-zero tv_status -> TreeVerifyError.  Output tensors are allocated with
+torch when not passed in.  Every step of the pass runs in the HIP library;
+there is no fallback: if libtreeverify.so is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libtreeverify.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "treeverify.h")
+
+TV_F32, TV_BF16 = 0, 1
+TV_MAX_NODES, TV_MAX_DEPTH = 1024, 64
+DEVERR_BAD_PARENT, DEVERR_TOO_DEEP, DEVERR_BAD_REQUEST, DEVERR_BAD_PATH = 1, 2, 3, 4
+
+
+class TreeVerifyError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load libtreeverify.so (once) and declare the signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m tree_attention_verification_bitmask_amd.build`")
+    L = C.CDLL(LIB_PATH)
+    i32, i64, f32, sz, vp = C.c_int32, C.c_int64, C.c_float, C.c_size_t, C.c_void_p
+    L.tv_status_string.argtypes = [C.c_int]
+    L.tv_status_string.restype = C.c_char_p
+    L.tv_abi_version.argtypes = []
+    L.tv_abi_version.restype = C.c_int
+    L.tree_mask_build.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.tree_mask_build.restype = C.c_int
+    L.tree_attn_verify_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, C.c_int]
+    L.tree_attn_verify_workspace_size.restype = sz
+    L.tree_attn_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32, i32,
+                                   f32, C.c_int, vp, vp, sz, vp, vp]
+    L.tree_attn_verify.restype = C.c_int
+    L.tree_accept_greedy.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.tree_accept_greedy.restype = C.c_int
+    L.kv_compact_path.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, C.c_int,
+                                  vp, vp, vp]
+    L.kv_compact_path.restype = C.c_int
+    _lib = L
+    return L
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/treeverify.h declares."""
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise TreeVerifyError(fn, status, lib().tv_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return TV_F32
+    if t.dtype == torch.bfloat16:
+        return TV_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _need(t, name, dtype=None, numel=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+
+
+def tree_mask_build(parent, cu_nodes, prefix_len, max_nodes: int, max_depth: int,
+                    anc=None, level=None, pos=None, err=None, stream=None):
+    """-> (anc uint64-as-int64 [T, W], level int32 [T], pos int32 [T], err int32 [1])."""
+    import torch
+    B = cu_nodes.numel() - 1
+    T = parent.numel()
+    W = (max_nodes + 63) // 64
+    dev = parent.device
+    for t, n in ((parent, "parent"), (cu_nodes, "cu_nodes"), (prefix_len, "prefix_len")):
+        _need(t, n, torch.int32)
+    anc = torch.empty((T, W), dtype=torch.int64, device=dev) if anc is None else anc
+    level = torch.empty(T, dtype=torch.int32, device=dev) if level is None else level
+    pos = torch.empty(T, dtype=torch.int32, device=dev) if pos is None else pos
+    err = torch.zeros(1, dtype=torch.int32, device=dev) if err is None else err
+    _need(anc, "anc", torch.int64, T * W)
+    _need(level, "level", torch.int32, T)
+    _need(pos, "pos", torch.int32, T)
+    _check("tree_mask_build", lib().tree_mask_build(
+        _ptr(parent), _ptr(cu_nodes), _ptr(prefix_len), B, T, max_nodes, max_depth,
+        _ptr(anc), _ptr(level), _ptr(pos), _ptr(err), _stream(stream)))
+    return anc, level, pos, err
+
+
+def tree_attn_verify_workspace_size(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim,
+                                    dtype_code) -> int:
+    return int(lib().tree_attn_verify_workspace_size(batch, total_nodes, max_nodes, max_prefix, hq,
+                                                     hkv, head_dim, dtype_code))
+
+
+def tree_attn_verify(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc, max_nodes: int,
+                     max_prefix: int, scale: float | None = None, out=None, workspace=None,
+                     err=None, stream=None):
+    """q [T, hq, d]; k_cache / v_cache [rows, hkv, d] -> out [T, hq, d] (same dtype)."""
+    import torch
+    T, hq, d = q.shape
+    rows, hkv, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q / k_cache / v_cache shapes disagree")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share a dtype")
+    code = _dtype_code(q)
+    B = cu_nodes.numel() - 1
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n)
+    for t, n in ((cu_nodes, "cu_nodes"), (kv_start, "kv_start"), (prefix_len, "prefix_len")):
+        _need(t, n, torch.int32)
+    _need(anc, "anc", torch.int64, T * ((max_nodes + 63) // 64))
+    out = torch.empty_like(q) if out is None else out
+    _need(out, "out", q.dtype, q.numel())
+    err = torch.zeros(1, dtype=torch.int32, device=q.device) if err is None else err
+    ws_bytes = tree_attn_verify_workspace_size(B, T, max_nodes, max_prefix, hq, hkv, d, code)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = d ** -0.5
+    _check("tree_attn_verify", lib().tree_attn_verify(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_nodes), _ptr(kv_start), _ptr(prefix_len),
+        _ptr(anc), B, T, max_nodes, max_prefix, rows, hq, hkv, d, float(scale), code, _ptr(out),
+        _ptr(workspace), ws_have, _ptr(err), _stream(stream)))
+    return out
+
+
+def tree_accept_greedy(parent, draft_tokens, target_tokens, root_target, cu_nodes, max_depth: int,
+                       accept_len=None, accept_idx=None, next_token=None, err=None, stream=None):
+    """-> (accept_len int32 [B], accept_idx int32 [B, max_depth], next_token int32 [B], err)."""
+    import torch
+    B = cu_nodes.numel() - 1
+    T = parent.numel()
+    dev = parent.device
+    for t, n in ((parent, "parent"), (draft_tokens, "draft_tokens"), (target_tokens, "target_tokens"),
+                 (root_target, "root_target"), (cu_nodes, "cu_nodes")):
+        _need(t, n, torch.int32)
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    accept_idx = (torch.empty((B, max_depth), dtype=torch.int32, device=dev)
+                  if accept_idx is None else accept_idx)
+    next_token = torch.empty(B, dtype=torch.int32, device=dev) if next_token is None else next_token
+    err = torch.zeros(1, dtype=torch.int32, device=dev) if err is None else err
+    _need(accept_idx, "accept_idx", torch.int32, B * max_depth)
+    _check("tree_accept_greedy", lib().tree_accept_greedy(
+        _ptr(parent), _ptr(draft_tokens), _ptr(target_tokens), _ptr(root_target), _ptr(cu_nodes),
+        B, T, max_depth, _ptr(accept_len), _ptr(accept_idx), _ptr(next_token), _ptr(err),
+        _stream(stream)))
+    return accept_len, accept_idx, next_token, err
+
+
+def kv_compact_path(k_cache, v_cache, cu_nodes, kv_start, prefix_len, accept_len, accept_idx,
+                    max_depth: int, total_nodes: int, new_kv_len=None, err=None, stream=None):
+    """Gathers the accepted rows in place; -> (new_kv_len int32 [B], err)."""
+    import torch
+    rows, hkv, d = k_cache.shape
+    code = _dtype_code(k_cache)
+    B = cu_nodes.numel() - 1
+    _need(k_cache, "k_cache")
+    _need(v_cache, "v_cache", k_cache.dtype, k_cache.numel())
+    for t, n in ((cu_nodes, "cu_nodes"), (kv_start, "kv_start"), (prefix_len, "prefix_len"),
+                 (accept_len, "accept_len"), (accept_idx, "accept_idx")):
+        _need(t, n, torch.int32)
+    new_kv_len = torch.empty(B, dtype=torch.int32, device=k_cache.device) if new_kv_len is None else new_kv_len
+    err = torch.zeros(1, dtype=torch.int32, device=k_cache.device) if err is None else err
+    _check("kv_compact_path", lib().kv_compact_path(
+        _ptr(k_cache), _ptr(v_cache), _ptr(cu_nodes), _ptr(kv_start), _ptr(prefix_len),
+        _ptr(accept_len), _ptr(accept_idx), B, total_nodes, max_depth, rows, hkv, d, code,
+        _ptr(new_kv_len), _ptr(err), _stream(stream)))
+    return new_kv_len, err

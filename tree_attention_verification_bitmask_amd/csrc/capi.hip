@@ -1,0 +1,172 @@
+// C ABI of libtreeverify: host-side argument checks, then dispatch to the
+// kernels.  Every check runs before any HIP runtime call, so a rejected call
+// enqueues nothing (and the checks can be exercised on a machine without a
+// GPU).  The definitions each call implements are cited in treeverify.h.
+#include <stdint.h>
+
+#include "treeverify.h"
+#include "tv_launch.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+tv_status launch_status(hipError_t e) { return e == hipSuccess ? TV_OK : TV_ERR_LAUNCH; }
+
+tv_status check_batch(int32_t batch, int32_t total_nodes) {
+    if (batch < 0 || total_nodes < 0) return TV_ERR_SHAPE;
+    if (total_nodes > TV_MAX_TOTAL_NODES) return TV_ERR_LIMIT;
+    if (batch > 65535) return TV_ERR_LIMIT;
+    return TV_OK;
+}
+
+tv_status check_attn_sizes(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_prefix,
+                           int32_t hq, int32_t hkv, int32_t head_dim, tv_dtype dtype) {
+    tv_status st = check_batch(batch, total_nodes);
+    if (st != TV_OK) return st;
+    if (max_nodes < 1 || max_prefix < 0 || hq < 1 || hkv < 1) return TV_ERR_SHAPE;
+    if (hq % hkv != 0) return TV_ERR_SHAPE;
+    if (max_nodes > TV_MAX_NODES) return TV_ERR_LIMIT;
+    if (hq > 65535) return TV_ERR_LIMIT;
+    if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_DTYPE;
+    if (head_dim != 64 && head_dim != 128) return TV_ERR_DTYPE;
+    // the key axis of one request must fit int32 arithmetic comfortably
+    if ((int64_t)max_prefix + max_nodes > (1ll << 30)) return TV_ERR_LIMIT;
+    return TV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tv_status_string(int status) {
+    switch (status) {
+        case TV_OK: return "TV_OK";
+        case TV_ERR_NULL: return "TV_ERR_NULL: a required pointer is NULL";
+        case TV_ERR_SHAPE: return "TV_ERR_SHAPE: inconsistent or negative sizes";
+        case TV_ERR_DTYPE: return "TV_ERR_DTYPE: unsupported dtype or head_dim";
+        case TV_ERR_LIMIT: return "TV_ERR_LIMIT: a size exceeds a library limit";
+        case TV_ERR_WORKSPACE: return "TV_ERR_WORKSPACE: workspace too small or misaligned";
+        case TV_ERR_LAUNCH: return "TV_ERR_LAUNCH: the HIP runtime refused a launch";
+        case TV_ERR_ALIGN: return "TV_ERR_ALIGN: a pointer breaks the required alignment";
+        default: return "unknown tv_status";
+    }
+}
+
+int tv_abi_version(void) { return 1; }
+
+tv_status tree_mask_build(const int32_t *parent, const int32_t *cu_nodes, const int32_t *prefix_len,
+                          int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_depth,
+                          uint64_t *anc_bits, int32_t *level, int32_t *pos_ids, int32_t *err,
+                          void *stream) {
+    tv_status st = check_batch(batch, total_nodes);
+    if (st != TV_OK) return st;
+    if (max_nodes < 1 || max_depth < 1) return TV_ERR_SHAPE;
+    if (max_nodes > TV_MAX_NODES || max_depth > TV_MAX_DEPTH) return TV_ERR_LIMIT;
+    if (!cu_nodes || !prefix_len) return TV_ERR_NULL;
+    if (total_nodes > 0 && (!parent || !anc_bits || !level || !pos_ids)) return TV_ERR_NULL;
+    if (!aligned(anc_bits, 8)) return TV_ERR_ALIGN;
+    if (batch == 0 || total_nodes == 0) return TV_OK;
+    return launch_status(tv::launch_mask_build(parent, cu_nodes, prefix_len, batch, total_nodes,
+                                               max_nodes, max_depth, anc_bits, level, pos_ids, err,
+                                               (hipStream_t)stream));
+}
+
+size_t tree_attn_verify_workspace_size(int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                                       int32_t max_prefix, int32_t hq, int32_t hkv, int32_t head_dim,
+                                       tv_dtype dtype) {
+    if (check_attn_sizes(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype) != TV_OK)
+        return 0;
+    const tv::MfmaPlan plan =
+        tv::plan_attn_mfma(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype);
+    return plan.use ? plan.ws_bytes : 0;
+}
+
+tv_status tree_attn_verify(const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *cu_nodes, const int32_t *kv_start, const int32_t *prefix_len,
+                           const uint64_t *anc_bits, int32_t batch, int32_t total_nodes,
+                           int32_t max_nodes, int32_t max_prefix, int64_t kv_rows, int32_t hq,
+                           int32_t hkv, int32_t head_dim, float scale, tv_dtype dtype, void *out,
+                           void *workspace, size_t workspace_bytes, int32_t *err, void *stream) {
+    tv_status st = check_attn_sizes(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype);
+    if (st != TV_OK) return st;
+    if (kv_rows < 0) return TV_ERR_SHAPE;
+    if (!(scale > 0.f) || scale != scale) return TV_ERR_SHAPE;
+    if (!cu_nodes || !kv_start || !prefix_len) return TV_ERR_NULL;
+    if (total_nodes > 0 && (!q || !out || !anc_bits)) return TV_ERR_NULL;
+    if (kv_rows > 0 && (!k_cache || !v_cache)) return TV_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+        !aligned(anc_bits, 8))
+        return TV_ERR_ALIGN;
+    const tv::MfmaPlan plan =
+        tv::plan_attn_mfma(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype);
+    if (plan.use && plan.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < plan.ws_bytes) return TV_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return TV_ERR_ALIGN;
+    }
+    if (batch == 0 || total_nodes == 0) return TV_OK;
+    tv::AttnArgs a;
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.cu_nodes = cu_nodes;
+    a.kv_start = kv_start;
+    a.prefix_len = prefix_len;
+    a.anc = anc_bits;
+    a.batch = batch;
+    a.total_nodes = total_nodes;
+    a.max_nodes = max_nodes;
+    a.max_prefix = max_prefix;
+    a.kv_rows = kv_rows;
+    a.hq = hq;
+    a.hkv = hkv;
+    a.head_dim = head_dim;
+    a.scale = scale;
+    a.dtype = dtype;
+    a.out = out;
+    a.err = err;
+    if (plan.use) return launch_status(tv::launch_attn_mfma(a, plan, workspace, (hipStream_t)stream));
+    return launch_status(tv::launch_attn_valu(a, (hipStream_t)stream));
+}
+
+tv_status tree_accept_greedy(const int32_t *parent, const int32_t *draft_tokens,
+                             const int32_t *target_tokens, const int32_t *root_target,
+                             const int32_t *cu_nodes, int32_t batch, int32_t total_nodes,
+                             int32_t max_depth, int32_t *accept_len, int32_t *accept_idx,
+                             int32_t *next_token, int32_t *err, void *stream) {
+    tv_status st = check_batch(batch, total_nodes);
+    if (st != TV_OK) return st;
+    if (max_depth < 1) return TV_ERR_SHAPE;
+    if (max_depth > TV_MAX_DEPTH) return TV_ERR_LIMIT;
+    if (!cu_nodes || !root_target || !accept_len || !accept_idx || !next_token) return TV_ERR_NULL;
+    if (total_nodes > 0 && (!parent || !draft_tokens || !target_tokens)) return TV_ERR_NULL;
+    if (batch == 0) return TV_OK;
+    return launch_status(tv::launch_accept_greedy(parent, draft_tokens, target_tokens, root_target,
+                                                  cu_nodes, batch, total_nodes, max_depth, accept_len,
+                                                  accept_idx, next_token, err, (hipStream_t)stream));
+}
+
+tv_status kv_compact_path(void *k_cache, void *v_cache, const int32_t *cu_nodes,
+                          const int32_t *kv_start, const int32_t *prefix_len,
+                          const int32_t *accept_len, const int32_t *accept_idx, int32_t batch,
+                          int32_t total_nodes, int32_t max_depth, int64_t kv_rows, int32_t hkv,
+                          int32_t head_dim, tv_dtype dtype, int32_t *new_kv_len, int32_t *err,
+                          void *stream) {
+    tv_status st = check_batch(batch, total_nodes);
+    if (st != TV_OK) return st;
+    if (max_depth < 1 || hkv < 1 || kv_rows < 0) return TV_ERR_SHAPE;
+    if (max_depth > TV_MAX_DEPTH || hkv > 65535) return TV_ERR_LIMIT;
+    if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_DTYPE;
+    if (head_dim != 64 && head_dim != 128) return TV_ERR_DTYPE;
+    if (!cu_nodes || !kv_start || !prefix_len || !accept_len || !accept_idx || !new_kv_len)
+        return TV_ERR_NULL;
+    if (kv_rows > 0 && (!k_cache || !v_cache)) return TV_ERR_NULL;
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16)) return TV_ERR_ALIGN;
+    if (batch == 0) return TV_OK;
+    return launch_status(tv::launch_kv_compact(k_cache, v_cache, cu_nodes, kv_start, prefix_len,
+                                               accept_len, accept_idx, batch, total_nodes, max_depth,
+                                               kv_rows, hkv, head_dim, dtype, new_kv_len, err,
+                                               (hipStream_t)stream));
+}
+
+}  // extern "C"

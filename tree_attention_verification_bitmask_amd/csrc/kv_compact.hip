@@ -1,0 +1,97 @@
+// kv_compact_path: gather the accepted path's K/V rows into place.
+//
+// [TSD] = "Tree-Structured Speculative Decoding: How Multi-Candidate Trees and
+// Tree Attention Accelerate LLM Serving" (llms.blog), section "KV Cache
+// Rollback".
+//
+// One workgroup per (request, KV head).  The destination rows P+j and the
+// source rows P+idx[j] overlap (a path [0, 2, 5] reads row P+2 and also
+// writes it), so the workgroup first reads every source row of its head slice
+// into LDS, waits on a barrier, and only then writes.  Different KV heads
+// touch disjoint bytes, so workgroups never race.  Rows already in place
+// (idx[j] == j) are skipped.
+#include "tv_device.h"
+#include "tv_launch.h"
+
+namespace tv {
+namespace {
+
+constexpr int kCompactThreads = 256;
+
+// ROW_BYTES = head_dim * element size: 128, 256 or 512 bytes.
+template <int ROW_BYTES>
+__global__ void __launch_bounds__(kCompactThreads) kv_compact_kernel(
+    uint8_t *__restrict__ kc, uint8_t *__restrict__ vc, const int32_t *__restrict__ cu_nodes,
+    const int32_t *__restrict__ kv_start, const int32_t *__restrict__ prefix_len,
+    const int32_t *__restrict__ accept_len, const int32_t *__restrict__ accept_idx, int total_nodes,
+    int max_depth, int64_t kv_rows, int hkv, int32_t *__restrict__ new_len, int32_t *__restrict__ err) {
+    constexpr int V16 = ROW_BYTES / 16;  // 16-byte vectors per row
+    extern __shared__ uint4 stage[];     // [2][max_depth][V16]
+    const int b = blockIdx.x;
+    const int g = blockIdx.y;
+    const int tid = threadIdx.x;
+    int lo;
+    const int n = request_nodes(cu_nodes, b, total_nodes, total_nodes, &lo);
+    const int P = prefix_len[b];
+    const int64_t ks = kv_start[b];
+    const int L = accept_len[b];
+    if (n < 0 || P < 0 || ks < 0 || ks + P + n > kv_rows || L < 0 || L > max_depth) {
+        if (g == 0 && tid == 0) report(err, TV_DEVERR_BAD_REQUEST, b);
+        return;
+    }
+    const int32_t *idx = accept_idx + (int64_t)b * max_depth;
+    for (int j = 0; j < L; ++j) {
+        const int s = idx[j];
+        if (s < 0 || s >= n) {
+            if (g == 0 && tid == 0) report(err, TV_DEVERR_BAD_PATH, b);
+            return;  // uniform across the workgroup: every thread reads the same idx
+        }
+    }
+    const int64_t row_stride = (int64_t)hkv * ROW_BYTES;  // bytes per cache row
+    const int64_t base = (ks + P) * row_stride + (int64_t)g * ROW_BYTES;
+    uint4 *sk = stage;
+    uint4 *sv = stage + (size_t)max_depth * V16;
+    const int work = L * V16;
+    for (int e = tid; e < work; e += kCompactThreads) {
+        const int j = e / V16, c = e % V16;
+        const int64_t off = base + (int64_t)idx[j] * row_stride + c * 16;
+        sk[e] = *reinterpret_cast<const uint4 *>(kc + off);
+        sv[e] = *reinterpret_cast<const uint4 *>(vc + off);
+    }
+    __syncthreads();
+    for (int e = tid; e < work; e += kCompactThreads) {
+        const int j = e / V16, c = e % V16;
+        if (idx[j] == j) continue;
+        const int64_t off = base + (int64_t)j * row_stride + c * 16;
+        *reinterpret_cast<uint4 *>(kc + off) = sk[e];
+        *reinterpret_cast<uint4 *>(vc + off) = sv[e];
+    }
+    if (g == 0 && tid == 0) new_len[b] = P + L;
+}
+
+}  // namespace
+
+hipError_t launch_kv_compact(void *k, void *v, const int32_t *cu_nodes, const int32_t *kv_start,
+                             const int32_t *prefix_len, const int32_t *accept_len,
+                             const int32_t *accept_idx, int batch, int total_nodes, int max_depth,
+                             int64_t kv_rows, int hkv, int head_dim, tv_dtype dtype, int32_t *new_len,
+                             int32_t *err, hipStream_t stream) {
+    if (batch == 0) return hipSuccess;
+    const int row_bytes = head_dim * (dtype == TV_F32 ? 4 : 2);
+    const size_t shmem = 2 * (size_t)max_depth * row_bytes;
+    dim3 grid(batch, hkv);
+#define TV_COMPACT(RB)                                                                           \
+    hipLaunchKernelGGL(kv_compact_kernel<RB>, grid, dim3(kCompactThreads), shmem, stream,          \
+                       (uint8_t *)k, (uint8_t *)v, cu_nodes, kv_start, prefix_len, accept_len,      \
+                       accept_idx, total_nodes, max_depth, kv_rows, hkv, new_len, err)
+    switch (row_bytes) {
+        case 128: TV_COMPACT(128); break;
+        case 256: TV_COMPACT(256); break;
+        case 512: TV_COMPACT(512); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef TV_COMPACT
+    return hipGetLastError();
+}
+
+}  // namespace tv

@@ -1,0 +1,59 @@
+// Internal launchers behind the C ABI (capi.hip).  Arguments are already
+// validated on the host when these run; each returns the hipError_t of its
+// launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "treeverify.h"
+
+namespace tv {
+
+hipError_t launch_mask_build(const int32_t *parent, const int32_t *cu_nodes, const int32_t *prefix_len,
+                             int batch, int total_nodes, int max_nodes, int max_depth, uint64_t *anc,
+                             int32_t *level, int32_t *pos, int32_t *err, hipStream_t stream);
+
+hipError_t launch_accept_greedy(const int32_t *parent, const int32_t *draft, const int32_t *target,
+                                const int32_t *root_target, const int32_t *cu_nodes, int batch,
+                                int total_nodes, int max_depth, int32_t *accept_len, int32_t *accept_idx,
+                                int32_t *next_token, int32_t *err, hipStream_t stream);
+
+hipError_t launch_kv_compact(void *k, void *v, const int32_t *cu_nodes, const int32_t *kv_start,
+                             const int32_t *prefix_len, const int32_t *accept_len,
+                             const int32_t *accept_idx, int batch, int total_nodes, int max_depth,
+                             int64_t kv_rows, int hkv, int head_dim, tv_dtype dtype, int32_t *new_len,
+                             int32_t *err, hipStream_t stream);
+
+// Problem description shared by the attention kernels.
+struct AttnArgs {
+    const void *q, *k, *v;
+    const int32_t *cu_nodes, *kv_start, *prefix_len;
+    const uint64_t *anc;
+    int batch, total_nodes, max_nodes, max_prefix;
+    int64_t kv_rows;
+    int hq, hkv, head_dim;
+    float scale;
+    tv_dtype dtype;
+    void *out;
+    int32_t *err;
+};
+
+// Generic VALU path: one wavefront per (node, query head); fp32 or bf16.
+hipError_t launch_attn_valu(const AttnArgs &a, hipStream_t stream);
+
+// Plan of the MFMA path (split over the key axis, fp32 partials, combine).
+struct MfmaPlan {
+    bool use = false;      // MFMA path selected for these sizes
+    int rows_per_tile = 0; // query rows (node x GQA-head pairs) per workgroup
+    int row_tiles = 0;     // per (request, KV head), sized for max_nodes
+    int splits = 0;        // key-axis splits per row tile (1 = no combine)
+    int keys_per_split = 0;
+    size_t ws_bytes = 0;
+};
+MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefix, int hq, int hkv,
+                        int head_dim, tv_dtype dtype);
+hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *workspace,
+                            hipStream_t stream);
+
+}  // namespace tv
