@@ -32,6 +32,14 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source extra flags.  The attention kernel takes row maxima with fmax on
+# values that are never NaN (products of finite bf16 inputs, or -inf for masked
+# keys); -fno-honor-nans lets fmax skip the NaN-quieting instructions.
+FILE_FLAGS = {
+    "attn_mfma.hip": ["-fno-honor-nans"],
+}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -45,7 +53,7 @@ def sources() -> list[str]:
 
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
