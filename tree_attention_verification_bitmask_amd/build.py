@@ -34,9 +34,13 @@ COMMON_FLAGS = [
 
 # Per-source extra flags.  The attention kernel takes row maxima with fmax on
 # values that are never NaN (products of finite bf16 inputs, or -inf for masked
-# keys); -fno-honor-nans lets fmax skip the NaN-quieting instructions.
+# keys); -fno-honor-nans lets fmax skip the NaN-quieting instructions.  Its
+# matrix products keep their accumulators in ordinary VGPRs
+# (-amdgpu-mfma-vgpr-form): the kernel fits in 256 of them, and the rare
+# rescale of the output accumulator by vector instructions then needs no
+# copies between the accumulator and vector register files.
 FILE_FLAGS = {
-    "attn_mfma.hip": ["-fno-honor-nans"],
+    "attn_mfma.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

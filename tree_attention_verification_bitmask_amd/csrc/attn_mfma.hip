@@ -8,27 +8,31 @@
 // Rows and tiles.  For one request b and KV head g the query rows are the
 // (node, head-in-group) pairs r = node * G + j, G = hq / hkv: the G heads that
 // share a KV head are stacked so that one K/V stream serves N*G rows.  A
-// workgroup takes a tile of 128 rows and one slice of the key axis.  Its eight
-// wavefronts form four row groups of 32 rows times two key phases: the two
-// waves of a row group take alternate 32-key chunks of the slice, each keeping
-// its own online-softmax state, and merge through LDS at the end.
+// workgroup takes a tile of 256 rows and one slice of the key axis; each of
+// its eight wavefronts owns 32 rows (two per SIMD) and keeps its own
+// online-softmax state for them over the whole slice.
 //
-// Software pipeline.  Each wave's chunk i goes through S = Q K^T at step i and
-// the softmax plus O += P V at step i + 1.  The two waves of a row group share
-// a SIMD and order their steps oppositely (products first / softmax first),
-// so one keeps the matrix core busy while the other runs the vector ALU.  A
-// workgroup barrier separates the steps.
+// K/V staging.  The slice is cut into chunks of 32 keys.  Each chunk's K and
+// V are copied HBM -> LDS by the LDS-DMA form of the global load (16 bytes per
+// lane, no registers) into two rings of eight stages; the eight waves split a
+// chunk's copies between them.  The copy of chunk c is issued at step
+// c - kAhead.  The DMA is issued from inline assembly (the compiler would
+// otherwise make every LDS read wait for all outstanding DMA) and the waits
+// are explicit: before the barrier of step i each wave waits for its own part
+// of chunk i + 2, so after the barrier chunk i + 2 is whole in LDS.  Each
+// 16-byte granule of a cached K/V row lands at an XOR-swizzled position in its
+// LDS row so the matrix-operand reads below are free of bank conflicts.
 //
-// K/V staging.  Chunks of 32 keys are copied HBM -> LDS by the LDS-DMA form of
-// the global load (16 bytes per lane, no registers) into two rings of eight
-// stages, one for K and one for V.  The K of a chunk is fetched three steps
-// before its Q K^T and the V three steps before its P V, so every DMA has
-// three steps to land.  The DMA is issued from inline assembly: the compiler
-// would otherwise make every LDS read wait for all outstanding DMA, which
-// serialises the rings.  The waits are explicit (vmcnt, then the step's
-// barrier).  Each 16-byte granule of a cached K/V row lands at an
-// XOR-swizzled position in its LDS row so the matrix-operand reads below are
-// free of bank conflicts.
+// Per-wave software pipeline.  Step i of a wave runs, in this order,
+//   S(i+1) = Q K(i+1)^T   (eight MFMAs, K(i+1) already in registers),
+//   the softmax of chunk i on S(i) (computed one step earlier),
+//   reads of K(i+2) from LDS into registers (for the next step),
+//   O += P(i) V(i)        (eight MFMAs, V(i) already in registers),
+//   reads of V(i+1) from LDS into registers.
+// Operands are read one step ahead, so LDS latency never stalls a matrix
+// product, and the vector work of the softmax has the products of the other
+// wave on the SIMD (and its own S(i+1) chain) to hide behind.  The steady
+// state is unrolled by eight so every ring offset is an immediate.
 //
 // Transposed products.  S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = 32 keys
 // x 16 channels of K read from LDS, B = Q^T held in registers.  LDS row i of a
@@ -46,11 +50,12 @@
 // rescaled only then.  The row sum adds the bf16-rounded weights (v_dot2 with
 // ones), i.e. exactly the weights the P V product uses.
 //
-// The ancestor mask is applied per lane, on chunks that reach the tree tail:
-// the lane takes the 16 bits of its node's packed row (staged in LDS) that
-// cover its 16 keys.  Prefix keys are always visible; keys at or past the end
-// of the slice never are (their LDS rows hold a clamped, valid cache row, so
-// the P V product never multiplies a zero weight by stale data).
+// The ancestor mask is applied per lane, on chunks that reach the tree tail
+// or the end of the slice: the lane takes the 16 bits of its node's packed
+// row (staged in LDS) that cover its 16 keys.  Prefix keys are always
+// visible; keys at or past the end of the slice never are (their LDS rows hold
+// a clamped, valid cache row, so the P V product never multiplies a zero
+// weight by stale data).
 //
 // Split key axis.  The host picks `splits` slices of `keys_per_split` keys so
 // that the grid fills the chip.  With one slice the kernel writes the
@@ -75,41 +80,41 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowGroups = 4;                 // 32-row groups per tile
-constexpr int kPhases = kWaves / kRowGroups;  // waves per row group (alternate chunks)
-constexpr int kTileRows = 32 * kRowGroups;    // query rows per workgroup
-constexpr int kChunk = 32;                    // keys per LDS stage
-constexpr int kStages = 8;                    // stages per ring (K ring, V ring)
-constexpr int kAhead = 3;                     // steps between a DMA and its use
+constexpr int kTileRows = 32 * kWaves;  // query rows per workgroup
+constexpr int kChunk = 32;              // keys per LDS stage
+constexpr int kStages = 8;              // stages per ring (K ring, V ring)
+constexpr int kAhead = 6;               // the DMA of chunk c is issued at step c - kAhead
 constexpr int kXcds = 8;
 constexpr int kMaxWords = (TV_MAX_NODES + 63) / 64;
 constexpr int kAncBytes = kTileRows * kMaxWords * 8;  // packed rows of the tile's nodes
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleLog2 = 8.f;           // lazy-rescale threshold (log2 units)
-static_assert(kPhases == 2, "two key phases");
-// K of chunk c lives in K stage c % kStages from step c/2 - kAhead to step c/2;
-// V from step c/2 + 1 - kAhead to step c/2 + 1.  Both fit eight stages:
-static_assert(kStages >= kPhases * (kAhead + 1), "ring depth");
-// The main loop is unrolled by kStages / kPhases steps so that stage indices
-// are compile-time constants.
-static_assert(kStages == 4 * kPhases, "unroll of the main loop");
+constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
+// Step i reads K(i+2) and V(i+1); the copy issued at step i overwrites the
+// stage of chunk i + kAhead - kStages, whose last read (its V) was at step
+// i + kAhead - kStages - 1 <= i - 1.  K(i+2) must have been issued before
+// step i, i.e. kAhead >= 3.
+static_assert(kAhead >= 3 && kAhead <= kStages, "ring depth");
+static_assert(kStages == 8, "the main loop is unrolled by the ring depth");
 
 template <int D>
 struct Geo {
-    static constexpr int kRowBytes = 2 * D;                  // one head of one cache row
-    static constexpr int kGran = D / 8;                      // 16-byte granules per row
-    static constexpr int kHalf = kChunk * kRowBytes;         // K (or V) bytes per chunk
-    static constexpr int kDmaPerHalf = kHalf / 1024;         // 1 KB per wave-wide DMA
-    static constexpr int kDmaPerWave = kDmaPerHalf / (kWaves / kPhases);  // per chunk half and wave
-    static constexpr int kKS = D / 16;                       // k-steps of Q K^T
-    static constexpr int kDB = D / 32;                       // 32-channel blocks of O
-    static constexpr int kRingBytes = 2 * kStages * kHalf;   // K ring + V ring
-    static_assert(kDmaPerWave >= 1 && kDmaPerHalf % (kWaves / kPhases) == 0, "DMA split");
-    static_assert(kRowGroups * kDB * 16 * 64 * 4 + kRowGroups * 64 * 8 <= kRingBytes, "merge buffer");
+    static constexpr int kRowBytes = 2 * D;                 // one head of one cache row
+    static constexpr int kGran = D / 8;                     // 16-byte granules per row
+    static constexpr int kHalf = kChunk * kRowBytes;        // K (or V) bytes per chunk
+    static constexpr int kDmaPerHalf = kHalf / 1024;        // 1 KB per wave-wide DMA
+    static constexpr int kDmaPerWave = kDmaPerHalf / (kWaves / 2);  // per chunk and wave
+    static constexpr int kKS = D / 16;                      // k-steps of Q K^T
+    static constexpr int kDB = D / 32;                      // 32-channel blocks of O
+    static constexpr int kRingBytes = 2 * kStages * kHalf;  // K ring + V ring
+    static_assert(kDmaPerWave >= 1 && kDmaPerHalf % (kWaves / 2) == 0, "DMA split over a wave group");
+    // V ring offsets: the lane's base (>= K ring size) lives in a register, the
+    // stage and sub-block offsets in the 16-bit immediate of the LDS read.
+    static_assert((kStages - 1) * kHalf + 12 * kRowBytes < 65536, "LDS immediate range");
 };
 
 // LDS row `slot` (0..31) of a 32-key block holds key key_of_slot(slot): in the
@@ -147,6 +152,19 @@ __device__ __forceinline__ void dma16(const char *base, uint32_t voff, uint32_t 
         : "v"(voff), "s"(base), "s"(lds)
         : "memory");
 }
+// The same with 4 bytes per lane (to lds + 4 * lane).
+__device__ __forceinline__ void dma4(const char *base, uint32_t voff, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(base), "s"(lds)
+        : "memory");
+}
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
@@ -157,14 +175,15 @@ __device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-// vmcnt wait allowing n outstanding DMA instructions of this wave, n a
-// multiple of PW between 0 and 4 PW.
-template <int PW>
-__device__ __forceinline__ void wait_dma(int n) {
-    if (n >= 4 * PW) wait_vm<4 * PW>();
-    else if (n >= 3 * PW) wait_vm<3 * PW>();
-    else if (n >= 2 * PW) wait_vm<2 * PW>();
-    else if (n >= PW) wait_vm<PW>();
+// Wait until at most PW * clamp(n, 0, CAP) of this wave's DMA instructions
+// are outstanding (each chunk costs a wave PW instructions).
+template <int PW, int CAP>
+__device__ __forceinline__ void wait_chunks(int n) {
+    static_assert(CAP >= 0 && CAP <= 4, "wait_chunks covers up to four chunks in flight");
+    if (CAP >= 4 && n >= 4) wait_vm<PW * (CAP >= 4 ? 4 : 0)>();
+    else if (CAP >= 3 && n >= 3) wait_vm<PW * (CAP >= 3 ? 3 : 0)>();
+    else if (CAP >= 2 && n >= 2) wait_vm<PW * (CAP >= 2 ? 2 : 0)>();
+    else if (CAP >= 1 && n >= 1) wait_vm<PW * (CAP >= 1 ? 1 : 0)>();
     else wait_vm<0>();
 }
 
@@ -186,8 +205,8 @@ struct KParams {
 // Bits e = 0..15 set iff key (key0 + e) is visible to the node whose packed
 // ancestor row (in LDS) is `arow`: prefix keys (< P) always, tree key P + j iff
 // bit j, nothing at or past `key_hi`.
-__device__ __forceinline__ uint32_t visible16(const uint64_t *arow, int words, int key0, int P,
-                                              int key_hi) {
+typedef __attribute__((address_space(3))) const uint64_t lds_u64_t;
+__device__ __forceinline__ uint32_t visible16(lds_u64_t *arow, int words, int key0, int P, int key_hi) {
     uint32_t bits;
     const int j0 = key0 - P;
     if (j0 <= -16) {
@@ -229,41 +248,11 @@ __device__ __forceinline__ bool decode_task(const KParams &p, int wid, Task *t) 
     return true;
 }
 
-// DMA of one half (K or V) of chunk `cidx` of the slice: the four waves of
-// key phase cidx & 1 each copy kDmaPerWave KB (part `part` of the half).
-// Lane offsets `voff` (bytes from the chunk's first cache row) are
-// precomputed; a chunk that runs past k_hi recomputes them with the keys
-// clamped to k_hi - 1, so every source row is a valid row of the request.
-template <int D>
-__device__ __forceinline__ void issue_half(const char *base, int64_t row_stride, int k_lo, int k_hi, int cidx,
-                                           bool isv, int part, int lane, const uint32_t *voff,
-                                           uint32_t ring_lds) {
-    using Gm = Geo<D>;
-    const int key0 = k_lo + cidx * kChunk;
-    const char *cbase = base + (int64_t)key0 * row_stride;
-    const uint32_t lds = ring_lds + (isv ? kStages * Gm::kHalf : 0) + (cidx % kStages) * Gm::kHalf +
-                         part * Gm::kDmaPerWave * 1024;
-    const bool clamp = key0 + kChunk > k_hi;
-#pragma unroll
-    for (int i = 0; i < Gm::kDmaPerWave; ++i) {
-        uint32_t off = voff[i];
-        if (clamp) {
-            const int byte = (part * Gm::kDmaPerWave + i) * 1024 + lane * 16;
-            const int row = byte / Gm::kRowBytes;
-            const int pos = (byte % Gm::kRowBytes) >> 4;
-            const int key = isv ? row : key_of_slot(row);
-            const int gran = pos ^ (isv ? v_swz<D>(row) : k_swz<D>(row));
-            const int kk = min(key0 + key, k_hi - 1) - key0;
-            off = (uint32_t)(kk * row_stride) + (uint32_t)(gran << 4);
-        }
-        dma16(cbase, off, lds + i * 1024);
-    }
-}
-
 template <int D>
 __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
     using Gm = Geo<D>;
     constexpr int KS = Gm::kKS, DB = Gm::kDB, PW = Gm::kDmaPerWave;
+    constexpr uint32_t kHalf = Gm::kHalf;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Gm::kRingBytes + kAncBytes];
 
     Task tk;
@@ -271,15 +260,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
     const int b = tk.b, g = tk.g, s = tk.s, rt = tk.rt;
 
     int lo;
-    const int n = request_nodes(p.cu_nodes, b, p.total_nodes, p.max_nodes, &lo);
+    const int n_nodes = request_nodes(p.cu_nodes, b, p.total_nodes, p.max_nodes, &lo);
     const int P = p.prefix_len[b];
     const int64_t ks = p.kv_start[b];
-    if (n < 0 || P < 0 || P > p.max_prefix || ks < 0 || ks + P + n > p.kv_rows) {
+    if (n_nodes < 0 || P < 0 || P > p.max_prefix || ks < 0 || ks + P + n_nodes > p.kv_rows) {
         if (g == 0 && rt == 0 && s == 0 && threadIdx.x == 0) report(p.err, TV_DEVERR_BAD_REQUEST, b);
         return;
     }
     const int G = p.hq / p.hkv;
-    const int rows_b = n * G;
+    const int rows_b = n_nodes * G;
     const int row0 = rt * kTileRows;
     if (row0 >= rows_b) return;
     const int row_end = min(rows_b, row0 + kTileRows);
@@ -289,183 +278,244 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
     const int k_lo = s * p.keys_per_split;
     if (k_lo >= key_end) return;
     const int k_hi = min(k_lo + p.keys_per_split, key_end);
-    const int nchunks = (k_hi - k_lo + kChunk - 1) / kChunk;
+    const int n = (k_hi - k_lo + kChunk - 1) / kChunk;  // chunks of the slice (>= 1)
+    // chunks i < c_mask lie wholly in the prefix and below k_hi: no mask
+    const int c_mask = max(0, (min(P, k_hi) - k_lo) / kChunk);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lane = tid & 63;
-    const int rg = wave % kRowGroups;
-    const int ph = wave / kRowGroups;
-    const int col = lane & 31;  // query row within the row group
+    const int col = lane & 31;  // query row within the wave's 32
     const int half = lane >> 5;
 
     const int64_t row_stride = (int64_t)p.hkv * D * 2;  // bytes per cache row
-    const char *kbase = reinterpret_cast<const char *>(p.k) + ks * row_stride + (int64_t)g * D * 2;
-    const char *vbase = reinterpret_cast<const char *>(p.v) + ks * row_stride + (int64_t)g * D * 2;
+    const int64_t chunk_bytes = kChunk * row_stride;
+    const char *kbase = reinterpret_cast<const char *>(p.k) + (ks + k_lo) * row_stride + (int64_t)g * D * 2;
+    const char *vbase = reinterpret_cast<const char *>(p.v) + (ks + k_lo) * row_stride + (int64_t)g * D * 2;
     const uint32_t ring = (uint32_t)(uintptr_t)smem;
 
-    // ---- DMA lane offsets: this wave copies part `rg` of the K and V halves of
-    // the chunks of key phase `ph` (chunk-relative source byte offsets).
-    uint32_t koffd[PW], voffd[PW];
-#pragma unroll
-    for (int i = 0; i < PW; ++i) {
-        const int byte = (rg * PW + i) * 1024 + lane * 16;
+    // ---- DMA role: group A (waves 0 .. kWaves/2 - 1) copies the K half of
+    // every chunk, group B the V half; wave w copies parts part0 .. part0 +
+    // PW - 1 of its half.  Lane offsets are chunk-relative source bytes; for
+    // the last chunk the keys are clamped to the slice, so every source row is
+    // a valid row of the request.
+    const bool grp_b = wave >= kWaves / 2;
+    const bool dv = grp_b;
+    const int part0 = (wave % (kWaves / 2)) * PW;
+    const char *dbase = dv ? vbase : kbase;
+    const uint32_t dlds = ring + (dv ? kStages * kHalf : 0u) + part0 * 1024;
+    const int last_keys = (k_hi - k_lo) - (n - 1) * kChunk;  // 1..32
+    // Source offset of lane `lane` in copy j of this wave, keys clamped to
+    // key_cap (the last chunk passes last_keys - 1, the others 31).
+    auto dma_off = [&](int j, int key_cap, int ln) {
+        const int byte = (part0 + j) * 1024 + ln * 16;
         const int row = byte / Gm::kRowBytes;
         const int pos = (byte % Gm::kRowBytes) >> 4;
-        koffd[i] = (uint32_t)(key_of_slot(row) * row_stride) + ((pos ^ k_swz<D>(row)) << 4);
-        voffd[i] = (uint32_t)(row * row_stride) + ((pos ^ v_swz<D>(row)) << 4);
+        const int key = dv ? row : key_of_slot(row);
+        const int gran = pos ^ (dv ? v_swz<D>(row) : k_swz<D>(row));
+        return (uint32_t)(min(key, key_cap) * row_stride) + (uint32_t)(gran << 4);
+    };
+    const int clamp_c = last_keys < kChunk ? n - 1 : -1;  // the chunk that needs clamping
+    uint32_t doff[PW];
+#pragma unroll
+    for (int j = 0; j < PW; ++j) doff[j] = dma_off(j, kChunk - 1, lane);
+    // Copy jj of this wave's part of chunk c into ring stage `stage`.
+    auto issue1 = [&](int c, uint32_t stage, int jj) {
+        const char *src = dbase + (int64_t)c * chunk_bytes;
+        const uint32_t lds = __builtin_amdgcn_readfirstlane(dlds + stage * kHalf + jj * 1024);
+        if (c == clamp_c) {
+            // (lane made opaque: the clamped offset is formed here instead of
+            // being hoisted and kept live across the loop)
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            dma16(src, dma_off(jj, last_keys - 1, ln), lds);
+        } else {
+            dma16(src, doff[jj], lds);
+        }
+    };
+    // Copy chunk c into ring stage `stage`.
+    auto issue = [&](int c, uint32_t stage) {
+#pragma unroll
+        for (int jj = 0; jj < PW; ++jj) issue1(c, stage, jj);
+    };
+
+    // ---- prologue --------------------------------------------------------------
+    // (1) the packed ancestor rows of the tile's nodes -> LDS, if the slice
+    // reaches the tree tail (4 bytes per lane; offsets clamped into the rows).
+    uint64_t *anc_lds = reinterpret_cast<uint64_t *>(smem + Gm::kRingBytes);
+    if (k_hi > P) {
+        const int nbytes = (node_last - node_first + 1) * p.words * 8;
+        const char *src = reinterpret_cast<const char *>(p.anc + ((int64_t)lo + node_first) * p.words);
+        const int nblk = (nbytes + 255) / 256;
+        for (int blk = wave; blk < nblk; blk += kWaves) {
+            const uint32_t off = (uint32_t)min(blk * 256 + lane * 4, nbytes - 4);
+            dma4(src, off, __builtin_amdgcn_readfirstlane(ring + Gm::kRingBytes + blk * 256));
+        }
     }
-    // DMA schedule: at step j (j = -kAhead .. -1 in the prologue) the K of
-    // chunks 2 (j + kAhead) + {0, 1} and the V of chunks 2 (j + kAhead - 1) +
-    // {0, 1}; this wave copies its part of the chunk of its own phase.
-    auto issue_step = [&](int j) {
-        const int ck = kPhases * (j + kAhead) + ph;
-        if (ck < nchunks)
-            issue_half<D>(kbase, row_stride, k_lo, k_hi, ck, false, rg, lane, koffd, ring);
-        const int cv = kPhases * (j + kAhead - 1) + ph;
-        if (cv >= 0 && cv < nchunks)
-            issue_half<D>(vbase, row_stride, k_lo, k_hi, cv, true, rg, lane, voffd, ring);
-    };
-    auto issued_at = [&](int j) {  // DMA instructions this wave issues at step j
-        const int ck = kPhases * (j + kAhead) + ph;
-        const int cv = kPhases * (j + kAhead - 1) + ph;
-        return PW * ((ck < nchunks ? 1 : 0) + (cv >= 0 && cv < nchunks ? 1 : 0));
-    };
-
-    // ---- prologue: start the rings first, so their latency overlaps the loads
-    // of Q and of the ancestor rows below.
-    for (int j = -kAhead; j < 0; ++j) issue_step(j);
-
-    // ---- this lane's query row -------------------------------------------------
-    const int r = row0 + rg * 32 + col;
+    // (2) this lane's query row -> registers (asynchronous; waited below).
+    const int r = row0 + wave * 32 + col;
     const bool row_ok = r < row_end;
-    const int node = row_ok ? r / G : node_last;
+    const bool active = row0 + wave * 32 < row_end;  // wave-uniform: the wave has rows
+    const int node = row_ok ? r / G : node_last;      // rows past the tile repeat a valid one
     const int head = g * G + (row_ok ? r % G : 0);
     const int64_t t = (int64_t)lo + node;
     bf16x8_t qb[KS];
     {
         const uint16_t *qrow = p.q + (t * p.hq + head) * D + 8 * half;
 #pragma unroll
-        for (int k16 = 0; k16 < KS; ++k16) {
-            uint4 x = *reinterpret_cast<const uint4 *>(qrow + 16 * k16);
-            if (!row_ok) x = make_uint4(0, 0, 0, 0);
-            qb[k16] = __builtin_bit_cast(bf16x8_t, x);
-        }
+        for (int k16 = 0; k16 < KS; ++k16)
+            asm volatile("global_load_dwordx4 %0, %1, off offset:%2"
+                         : "=v"(qb[k16])
+                         : "v"(qrow), "n"(32 * k16)
+                         : "memory");
     }
-
-    // ---- packed ancestor rows of the tile's nodes -> LDS (only if the slice
-    // reaches the tree tail).  Visible to every wave after the first barrier.
-    uint64_t *anc_lds = reinterpret_cast<uint64_t *>(smem + Gm::kRingBytes);
-    if (k_hi > P) {
-        const int cnt = (node_last - node_first + 1) * p.words;
-        const uint64_t *src = p.anc + ((int64_t)lo + node_first) * p.words;
-        for (int i = tid; i < cnt; i += kThreads) anc_lds[i] = src[i];
-    }
-    // Make the Q registers live here (the compiler waits for all loads so far,
-    // DMA included, once, instead of inside the loop).
+    // (3) the first kAhead chunks.  After the wait everything but chunks
+    // 2 .. kAhead-1 has landed.
+#pragma unroll
+    for (int c = 0; c < kAhead; ++c)
+        if (c < n) issue(c, c);
+    wait_chunks<PW, kAhead - 2>(min(n, kAhead) - 2);
 #pragma unroll
     for (int k16 = 0; k16 < KS; ++k16) asm volatile("" : "+v"(qb[k16]));
+    lds_barrier();
 
     // ---- per-lane LDS read offsets ----------------------------------------------
-    // K (A of S^T): LDS row col, logical granule 2*k16 + half.  The phase's
-    // chunks sit in the odd or even stages, hence the ph * kHalf.
-    uint32_t koff[KS];
-#pragma unroll
-    for (int k16 = 0; k16 < KS; ++k16)
-        koff[k16] = ph * Gm::kHalf + col * Gm::kRowBytes + (((2 * k16 + half) ^ k_swz<D>(col)) << 4);
+    // K (A of S^T): LDS row col, logical granule 2*k16 + half, stored at
+    // granule (2*k16 + half) ^ k_swz(col); as a byte offset that is
+    // kb + ((32 * k16) ^ kt) (the low bit of the swizzle only flips `half`).
+    const uint32_t kt = (uint32_t)(k_swz<D>(col) >> 1) << 5;
+    const uint32_t kb = col * Gm::kRowBytes + ((half ^ (k_swz<D>(col) & 1)) << 4);
     // V (A of O^T via the transposing read): lane l = 16 q + 4 j + rr reads 4
     // channels of key row 16 (q >> 1) + j (+ 4 e + 8 tt), channels
-    // 32 db + 16 (q & 1) + 4 rr.
-    uint32_t voff[DB];
+    // 32 db + 16 (q & 1) + 4 rr, i.e. logical granule 4 db + 2 (q & 1) +
+    // (rr >> 1); the swizzle v_swz(row) is a multiple of 4, so the stored
+    // offset is vb + ((64 * db) ^ vt).
+    uint32_t vb, vt;
     {
         const int q = lane >> 4, j = (lane >> 2) & 3, rr = lane & 3;
         const int vrow = 16 * (q >> 1) + j;
+        vt = (uint32_t)(v_swz<D>(vrow) >> 2) << 6;
+        vb = kStages * kHalf + vrow * Gm::kRowBytes + ((2 * (q & 1) + (rr >> 1)) << 4) + (rr & 1) * 8;
+    }
+    // The swizzle terms are made opaque at each use (empty asm) so that the
+    // compiler forms the addresses in the loop (one v_xad each) instead of
+    // keeping one hoisted register per address live across the loop.
+    // Single operands: K granule pair k16 and the V^T operand (tt, db).
+    auto read_k1 = [&](uint32_t base, uint32_t t, int k16) {
+        return *reinterpret_cast<const bf16x8_t *>(smem + (((32u * k16) ^ t) + base));
+    };
+    auto read_v1 = [&](uint32_t base, uint32_t t, int tt, int db) {
+        const uint32_t a0 = ((64u * db) ^ t) + base + (8 * tt) * Gm::kRowBytes;
+        const bf16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(smem + a0));
+        const bf16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(smem + a0 + 4 * Gm::kRowBytes));
+        return bf16x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    };
+    auto read_k = [&](bf16x8_t(&kk)[KS], uint32_t st) {
+        const uint32_t base = kb + st;
+        uint32_t t = kt;
+        asm volatile("" : "+v"(t));
+#pragma unroll
+        for (int k16 = 0; k16 < KS; ++k16)
+            kk[k16] = *reinterpret_cast<const bf16x8_t *>(smem + (((32u * k16) ^ t) + base));
+    };
+    auto read_v = [&](bf16x8_t(&vv)[2][DB], uint32_t st) {
+        const uint32_t base = vb + st;
+        uint32_t t = vt;
+        asm volatile("" : "+v"(t));
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const int gran = 4 * db + 2 * (q & 1) + (rr >> 1);
-            voff[db] = (kStages + ph) * Gm::kHalf + vrow * Gm::kRowBytes + ((gran ^ v_swz<D>(vrow)) << 4) +
-                       (rr & 1) * 8;
+            const uint32_t a = ((64u * db) ^ t) + base;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const uint32_t a0 = a + (8 * tt) * Gm::kRowBytes;
+                const bf16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(smem + a0));
+                const bf16x4_t hi4 =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(smem + a0 + 4 * Gm::kRowBytes));
+                vv[tt][db] = bf16x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+            }
         }
+    };
+
+    // ---- ping-pong schedule -------------------------------------------------------
+    // Group A = waves 0 .. kWaves/2 - 1, group B = the others; every SIMD holds
+    // one wave of each.  For chunk j a wave runs
+    //   V(j): the softmax of S(j) -> P(j) (vector work only);
+    //   M(j): O += P(j) V(j) and S(j+1) = Q K(j+1)^T (16 products), plus the
+    //         reads of V(j+1) and K(j+2) from LDS into registers and its
+    //         copies (K for A, V for B) of chunk j + kAhead.
+    // Every wave runs V(0) M(0) V(1) M(1) ... with a barrier after each item;
+    // group B first passes one barrier alone, so it runs one item behind and
+    // on each SIMD one wave feeds the matrix core while the other runs the
+    // exponentials.  Barrier 2j+1 starts A's M(j): before it A waits for its
+    // part of K(j+2) and B (at the end of its M(j-1)) for its part of V(j+1).
+    // A copy issued in M(j) overwrites the stage of chunk j + kAhead - 8,
+    // whose last reads were consumed at least two items earlier.
+    auto copy_ahead = [&](int j) {
+        if (j + kAhead < n) issue(j + kAhead, (uint32_t)((j + kAhead) % kStages));
+    };
+    auto copy_ahead1 = [&](int j, int jj) {
+        if (j + kAhead < n) issue1(j + kAhead, (uint32_t)((j + kAhead) % kStages), jj);
+    };
+    // Waits ahead of the barrier that opens A's M(j) (A: K(j+2)) and the one
+    // that opens A's M(j+1) (B, after its M(j): V(j+2)).
+    auto wait_before_m = [&](int j) {
+        if (!grp_b) wait_chunks<PW, kAhead - 3>(n - (j + 3));
+    };
+    auto wait_after_m = [&](int j) {
+        if (grp_b) wait_chunks<PW, kAhead - 2>(n - (j + 3));
+    };
+    if (!active) {
+        // A wave without rows only keeps the copy schedule and the barriers.
+        if (grp_b) lds_barrier();
+        for (int j = 0; j < n; ++j) {
+            wait_before_m(j);
+            lds_barrier();
+            if (!grp_b) copy_ahead(j);
+            if (grp_b) copy_ahead(j);
+            wait_after_m(j);
+            lds_barrier();
+        }
+        if (!grp_b) lds_barrier();
+        return;
     }
 
     f32x16_t oacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-    f32x16_t s_new, s_old;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s_new[i] = s_old[i] = 0.f;
+        for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+    const f32x16_t zero16 = {};
     float m_run = -INFINITY, l_run = 0.f;
+    float nb = 0.f;           // -m_ref * c
     const float c = p.c;
     const float thr = kRescaleLog2 / c;
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-    const uint64_t *arow = anc_lds + (node - node_first) * p.words;
+    lds_u64_t *arow = reinterpret_cast<lds_u64_t *>(
+        (uint32_t)(uintptr_t)anc_lds + (uint32_t)((node - node_first) * p.words * 8));
 
-    // ---- main loop ------------------------------------------------------------------
-    // Step k: this wave (phase ph) runs Q K^T of its chunk k and the softmax
-    // and P V of its chunk k - 1 (its chunk i is chunk 2 i + ph of the slice).
-    // Before the barrier every wave waits for the DMA it issued kAhead steps
-    // ago (the K of chunks 2k, 2k+1 and the V of chunks 2k-2, 2k-1); after it,
-    // it issues the DMA of step k.
-    const int my_n = (nchunks + 1 - ph) / 2;
-    const int nsteps = (nchunks + 1) / 2 + 1;
-    // One step.  U = k % 4 is a compile-time constant (the loop below is
-    // unrolled by four), which makes every LDS read offset an immediate: the
-    // phase's chunk 2k + ph sits in stage 2 U + ph of the K ring, chunk
-    // 2(k-1) + ph in stage 2 ((U + 3) % 4) + ph of the V ring.  s_new / s_old
-    // alternate between two register sets.
-    auto step = [&](auto U_, int k, f32x16_t &s_new, f32x16_t &s_old) {
-        constexpr int U = decltype(U_)::value;
-        constexpr uint32_t kst = 2 * U * Gm::kHalf;
-        constexpr uint32_t vst = 2 * ((U + 3) & 3) * Gm::kHalf;
-        wait_dma<PW>(issued_at(k - 1) + issued_at(k - 2));
-        lds_barrier();
-        issue_step(k);
-        const bool qk = k < my_n;                 // S = Q K^T for chunk k
-        const bool sp = k >= 1 && k - 1 < my_n;   // softmax and O += P V for chunk k - 1
-
-        // All LDS operand reads of the step first, so their latency overlaps.
-        bf16x8_t va[2][DB], ka[KS];
-        if (sp) {
+    auto qk = [&](const bf16x8_t(&kk)[KS]) {
+        f32x16_t acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[0], qb[0], zero16, 0, 0, 0);
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const uint32_t a0 = vst + voff[db] + (8 * tt) * Gm::kRowBytes;
-                    const bf16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(smem + a0));
-                    const bf16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        (lds_bf16x4_t *)(smem + a0 + 4 * Gm::kRowBytes));
-                    va[tt][db] = bf16x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-                }
-        }
-        if (qk) {
-#pragma unroll
-            for (int k16 = 0; k16 < KS; ++k16) ka[k16] = *reinterpret_cast<const bf16x8_t *>(smem + kst + koff[k16]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (qk) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) s_new[e] = 0.f;
-#pragma unroll
-            for (int k16 = 0; k16 < KS; ++k16)
-                s_new = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[k16], qb[k16], s_new, 0, 0, 0);
-        }
-        if (!sp) return;
-        // softmax of chunk k - 1 (its S is s_old), then O += P V
-        const int c0 = k_lo + (2 * (k - 1) + ph) * kChunk;
-        if (c0 + kChunk > P || c0 + kChunk > k_hi) {
-            const uint32_t vis = visible16(arow, p.words, c0 + 16 * half, P, k_hi);
+        for (int k16 = 1; k16 < KS; ++k16) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[k16], qb[k16], acc, 0, 0, 0);
+        return acc;
+    };
+    // Softmax of chunk i, first part: mask, row max, and (rarely) a raise of
+    // the reference m with the rescale of l and O.
+    auto prep = [&](f32x16_t &sv, int i) {
+        if (i >= c_mask) {
+            const uint32_t vis = visible16(arow, p.words, k_lo + i * kChunk + 16 * half, P, k_hi);
             if (vis != 0xFFFFu) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
-                    if (!((vis >> e) & 1u)) s_old[e] = -INFINITY;
+                    if (!((vis >> e) & 1u)) sv[e] = -INFINITY;
             }
         }
-        float mx = fmaxf(s_old[0], s_old[1]);
-#pragma unroll
-        for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s_old[e], s_old[e + 1]));
-        mx = halves_max(mx);
+        // row max over the lane's 16 scores as a three-level tree of max3
+        const float a0 = fmaxf(fmaxf(sv[0], sv[1]), sv[2]), a1 = fmaxf(fmaxf(sv[3], sv[4]), sv[5]);
+        const float a2 = fmaxf(fmaxf(sv[6], sv[7]), sv[8]), a3 = fmaxf(fmaxf(sv[9], sv[10]), sv[11]);
+        const float a4 = fmaxf(fmaxf(sv[12], sv[13]), sv[14]);
+        const float b0 = fmaxf(fmaxf(a0, a1), a2), b1 = fmaxf(fmaxf(a3, a4), sv[15]);
+        const float mx = halves_max(fmaxf(b0, b1));
         if (__builtin_amdgcn_ballot_w64(mx > m_run + thr) != 0) {
             const float mn = fmaxf(m_run, mx);
             const float mref = (mn == -INFINITY) ? 0.f : mn;
@@ -476,75 +526,111 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
             m_run = mn;
+            nb = -mref * c;
         }
-        const float nb = (m_run == -INFINITY) ? 0.f : -m_run * c;
-        bf16x8_t pw[2];
+    };
+    // Second part: the weights 2^(s c - m c), rounded to bf16, and their sum.
+    // (Two partial sums halve the dependent chain of the row sum.)
+    auto weights = [&](const f32x16_t &sv, bf16x8_t(&pw)[2]) {
+        float l0 = 0.f, l1 = 0.f;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
             for (int j2 = 0; j2 < 4; ++j2) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(s_old[8 * tt + 2 * j2], c, nb));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(s_old[8 * tt + 2 * j2 + 1], c, nb));
-                bf16x2_t pp;
-                pp[0] = (__bf16)p0;
-                pp[1] = (__bf16)p1;
-                l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
+                const f32x2_t pf = {__builtin_amdgcn_exp2f(fmaf(sv[8 * tt + 2 * j2], c, nb)),
+                                    __builtin_amdgcn_exp2f(fmaf(sv[8 * tt + 2 * j2 + 1], c, nb))};
+                const bf16x2_t pp = __builtin_convertvector(pf, bf16x2_t);
+                if (j2 & 1) l1 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l1, false);
+                else l0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l0, false);
                 pw[tt][2 * j2] = pp[0];
                 pw[tt][2 * j2 + 1] = pp[1];
             }
         }
+        l_run += l0 + l1;
+    };
+    auto pv = [&](const bf16x8_t(&vv)[2][DB], const bf16x8_t(&pw)[2]) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int db = 0; db < DB; ++db)
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[tt][db], pw[tt], oacc[db], 0, 0, 0);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv[tt][db], pw[tt], oacc[db], 0, 0, 0);
     };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
-    f32x16_t sa = s_new, sb = s_old;
-    for (int k0 = 0; k0 < nsteps; k0 += 4) {
-        step(I0{}, k0, sa, sb);
-        if (k0 + 1 >= nsteps) break;
-        step(I1{}, k0 + 1, sb, sa);
-        if (k0 + 2 >= nsteps) break;
-        step(I2{}, k0 + 2, sa, sb);
-        if (k0 + 3 >= nsteps) break;
-        step(I3{}, k0 + 3, sb, sa);
-    }
 
-    // ---- merge the two key phases of each row group through LDS ---------------
-    l_run = halves_sum(l_run);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // all LDS reads returned
-    lds_barrier();
-    float *xo = reinterpret_cast<float *>(smem);                                       // [rg][DB*16][64]
-    float2 *xml = reinterpret_cast<float2 *>(smem + kRowGroups * DB * 16 * 64 * 4);  // [rg][64]
-    if (ph == 1) {
+    // Prologue products: S(0), and the operands K(1), V(0).
+    bf16x8_t kr[KS], vr[2][DB], pw[2];
+    read_k(kr, 0);
+    f32x16_t sv = qk(kr);
+    if (n > 1) read_k(kr, kHalf);
+    read_v(vr, 0);
+    auto vphase = [&](int j) {
+        prep(sv, j);
+        weights(sv, pw);
+    };
+    // M(j): each product is followed by the read that refills the operand
+    // registers it consumed (V(j+1) after the P V products, K(j+2) after the
+    // Q K^T products), so the reads hide under the matrix core and each
+    // operand set stays single.  Group A issues its copies of chunk
+    // j + kAhead one per product.  STEADY: j + 2 < n (both refills exist).
+    auto mphase = [&](auto steady_, int j) {
+        constexpr bool STEADY = decltype(steady_)::value;
+        const bool nx1 = STEADY || j + 1 < n, nx2 = STEADY || j + 2 < n;
+        const uint32_t vbase = vb + (uint32_t)((j + 1) % kStages) * kHalf;
+        const uint32_t kbase = kb + (uint32_t)((j + 2) % kStages) * kHalf;
+        uint32_t vtt = vt, ktt = kt;
+        asm volatile("" : "+v"(vtt), "+v"(ktt));
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) xo[(rg * DB * 16 + db * 16 + i) * 64 + lane] = oacc[db][i];
-        xml[rg * 64 + lane] = make_float2(m_run, l_run);
+            for (int db = 0; db < DB; ++db) {
+                const int idx = tt * DB + db;
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[tt][db], pw[tt], oacc[db], 0, 0, 0);
+                if (STEADY && (idx % (2 * DB / PW)) == 0) copy_ahead1(j, idx / (2 * DB / PW));
+                if (nx1) vr[tt][db] = read_v1(vbase, vtt, tt, db);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        if (nx1) {
+            sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[0], qb[0], zero16, 0, 0, 0);
+            if (nx2) kr[0] = read_k1(kbase, ktt, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k16 = 1; k16 < KS; ++k16) {
+                sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[k16], qb[k16], sv, 0, 0, 0);
+                if (nx2) kr[k16] = read_k1(kbase, ktt, k16);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // Results of the phase are pinned here: register-only work must not
+        // drift across the barriers into the other phase.
+        asm volatile("" : "+v"(sv));
+#pragma unroll
+        for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(oacc[db]));
+    };
+    using Steady = std::true_type;
+    using Tail = std::false_type;
+    auto vphase_pinned = [&](int j) {
+        vphase(j);
+        asm volatile("" : "+v"(pw[0]), "+v"(pw[1]));
+    };
+    if (grp_b) lds_barrier();
+    int j = 0;
+    for (; j < n - 2; ++j) {
+        vphase_pinned(j);
+        wait_before_m(j);
+        lds_barrier();
+        mphase(Steady{}, j);
+        wait_after_m(j);
+        lds_barrier();
     }
-    __syncthreads();
-    if (ph == 1) return;
-    {
-        const float2 o = xml[rg * 64 + lane];
-        const float mn = fmaxf(m_run, o.x);
-        const float mref = (mn == -INFINITY) ? 0.f : mn;
-        const float a0 = __builtin_amdgcn_exp2f((m_run - mref) * c);
-        const float a1 = __builtin_amdgcn_exp2f((o.x - mref) * c);
-        l_run = l_run * a0 + o.y * a1;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                oacc[db][i] = oacc[db][i] * a0 + xo[(rg * DB * 16 + db * 16 + i) * 64 + lane] * a1;
-        m_run = mn;
+    for (; j < n; ++j) {
+        vphase_pinned(j);
+        lds_barrier();
+        mphase(Tail{}, j);
+        lds_barrier();
     }
+    if (!grp_b) lds_barrier();
 
     // ---- epilogue ----------------------------------------------------------------
+    l_run = halves_sum(l_run);
     if (p.splits == 1) {
         if (!row_ok) return;
         const float inv = 1.f / l_run;
@@ -559,9 +645,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
                 *reinterpret_cast<uint2 *>(orow + d) = make_uint2(w0, w1);
             }
     } else {
-        // lane-native partial layout: [tile][split][row group][DB*4 float4][64 lanes]
+        // lane-native partial layout: [tile][split][wave][DB*4 float4][64 lanes]
         const int tile = (b * p.hkv + g) * p.row_tiles + rt;
-        const int64_t unit = ((int64_t)tile * p.splits + s) * kRowGroups + rg;
+        const int64_t unit = ((int64_t)tile * p.splits + s) * kWaves + wave;
         float4 *po = reinterpret_cast<float4 *>(p.ws_o) + unit * (DB * 4 * 64) + lane;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -573,12 +659,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
     }
 }
 
-// Merge the per-slice partials of one (tile, row group, channel block):
+// Merge the per-slice partials of one (tile, 32-row group, channel block):
 // O = sum_s w_s O_s / sum_s w_s l_s with w_s = 2^((m_s - M) c), M = max_s m_s.
 // One wavefront per (tile, row group, 32-channel block); lane layout as the
 // partials.
 template <int D>
-__global__ void __launch_bounds__(256) attn_combine_kernel(KParams p) {
+__global__ void __launch_bounds__(kThreads) attn_combine_kernel(KParams p) {
     constexpr int DB = Geo<D>::kDB;
     const int tile = blockIdx.x;
     const int db = blockIdx.y;
@@ -605,14 +691,14 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(KParams p) {
 
     const int64_t base = (int64_t)tile * p.splits;
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p.ws_ml[((base + s) * kRowGroups + rg) * 32 + col].x);
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p.ws_ml[((base + s) * kWaves + rg) * 32 + col].x);
     const float mref = (M == -INFINITY) ? 0.f : M;
     float L = 0.f;
     float4 acc[4];
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) acc[i4] = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s = 0; s < nsplit; ++s) {
-        const int64_t unit = (base + s) * kRowGroups + rg;
+        const int64_t unit = (base + s) * kWaves + rg;
         const float2 ml = p.ws_ml[unit * 32 + col];
         const float w = __builtin_amdgcn_exp2f((ml.x - mref) * p.c);
         L = fmaf(w, ml.y, L);
@@ -718,11 +804,11 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *works
     if (a.head_dim == 128) {
         hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, p);
         if (plan.splits > 1)
-            hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(tiles, Geo<128>::kDB), dim3(256), 0, stream, p);
+            hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(tiles, Geo<128>::kDB), dim3(kThreads), 0, stream, p);
     } else {
         hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, p);
         if (plan.splits > 1)
-            hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(tiles, Geo<64>::kDB), dim3(256), 0, stream, p);
+            hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(tiles, Geo<64>::kDB), dim3(kThreads), 0, stream, p);
     }
     return hipGetLastError();
 }
