@@ -197,7 +197,7 @@ struct KParams {
     int row_tiles, splits, keys_per_split;
     float c;  // scale * log2(e)
     uint16_t *out;
-    float *ws_o;    // partial O, lane-native layout (see attn_fwd_kernel)
+    uint2 *ws_o;    // partial O / l as bf16, lane-native layout (see attn_fwd_kernel)
     float2 *ws_ml;  // partial (m, l) per row
     int32_t *err;
 };
@@ -441,15 +441,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
     // one wave of each.  For chunk j a wave runs
     //   V(j): the softmax of S(j) -> P(j) (vector work only);
     //   M(j): O += P(j) V(j) and S(j+1) = Q K(j+1)^T (16 products), plus the
-    //         reads of V(j+1) and K(j+2) from LDS into registers and its
-    //         copies (K for A, V for B) of chunk j + kAhead.
+    //         reads of V(j+1) and K(j+2) from LDS into registers.
+    // V(j) starts with the wave's copies (K for A, V for B) of chunk
+    // j + kAhead: the vector phase has issue slots to spare.
     // Every wave runs V(0) M(0) V(1) M(1) ... with a barrier after each item;
     // group B first passes one barrier alone, so it runs one item behind and
     // on each SIMD one wave feeds the matrix core while the other runs the
     // exponentials.  Barrier 2j+1 starts A's M(j): before it A waits for its
     // part of K(j+2) and B (at the end of its M(j-1)) for its part of V(j+1).
-    // A copy issued in M(j) overwrites the stage of chunk j + kAhead - 8,
-    // whose last reads were consumed at least two items earlier.
+    // A copy issued in V(j) overwrites the stage of chunk j + kAhead - 8,
+    // whose last reads (B's M of chunk j + kAhead - 9) were consumed at least
+    // two items earlier.
     auto copy_ahead = [&](int j) {
         if (j + kAhead < n) issue(j + kAhead, (uint32_t)((j + kAhead) % kStages));
     };
@@ -459,7 +461,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
     // Waits ahead of the barrier that opens A's M(j) (A: K(j+2)) and the one
     // that opens A's M(j+1) (B, after its M(j): V(j+2)).
     auto wait_before_m = [&](int j) {
-        if (!grp_b) wait_chunks<PW, kAhead - 3>(n - (j + 3));
+        if (!grp_b) wait_chunks<PW, kAhead - 2>(n - (j + 3));
     };
     auto wait_after_m = [&](int j) {
         if (grp_b) wait_chunks<PW, kAhead - 2>(n - (j + 3));
@@ -468,10 +470,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
         // A wave without rows only keeps the copy schedule and the barriers.
         if (grp_b) lds_barrier();
         for (int j = 0; j < n; ++j) {
+            copy_ahead(j);
             wait_before_m(j);
             lds_barrier();
-            if (!grp_b) copy_ahead(j);
-            if (grp_b) copy_ahead(j);
             wait_after_m(j);
             lds_barrier();
         }
@@ -569,8 +570,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
     // M(j): each product is followed by the read that refills the operand
     // registers it consumed (V(j+1) after the P V products, K(j+2) after the
     // Q K^T products), so the reads hide under the matrix core and each
-    // operand set stays single.  Group A issues its copies of chunk
-    // j + kAhead one per product.  STEADY: j + 2 < n (both refills exist).
+    // operand set stays single.  STEADY: j + 2 < n (both refills exist).
     auto mphase = [&](auto steady_, int j) {
         constexpr bool STEADY = decltype(steady_)::value;
         const bool nx1 = STEADY || j + 1 < n, nx2 = STEADY || j + 2 < n;
@@ -584,7 +584,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
             for (int db = 0; db < DB; ++db) {
                 const int idx = tt * DB + db;
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[tt][db], pw[tt], oacc[db], 0, 0, 0);
-                if (STEADY && (idx % (2 * DB / PW)) == 0) copy_ahead1(j, idx / (2 * DB / PW));
                 if (nx1) vr[tt][db] = read_v1(vbase, vtt, tt, db);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -608,6 +607,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
     using Steady = std::true_type;
     using Tail = std::false_type;
     auto vphase_pinned = [&](int j) {
+        copy_ahead(j);
         vphase(j);
         asm volatile("" : "+v"(pw[0]), "+v"(pw[1]));
     };
@@ -645,30 +645,42 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
                 *reinterpret_cast<uint2 *>(orow + d) = make_uint2(w0, w1);
             }
     } else {
-        // lane-native partial layout: [tile][split][wave][DB*4 float4][64 lanes]
+        // Partial of this slice: O / l rounded to bf16 (a convex combination of
+        // V rows, so bf16 keeps its range) plus the fp32 (m, l).  Lane-native
+        // layout [tile][split][wave][DB*4 x 4 bf16][64 lanes].  A row that sees
+        // no key of the slice has l = 0 and stores zeros.
         const int tile = (b * p.hkv + g) * p.row_tiles + rt;
         const int64_t unit = ((int64_t)tile * p.splits + s) * kWaves + wave;
-        float4 *po = reinterpret_cast<float4 *>(p.ws_o) + unit * (DB * 4 * 64) + lane;
+        uint2 *po = p.ws_o + unit * (DB * 4 * 64) + lane;
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4)
-                po[(db * 4 + i4) * 64] = make_float4(oacc[db][4 * i4 + 0], oacc[db][4 * i4 + 1],
-                                                     oacc[db][4 * i4 + 2], oacc[db][4 * i4 + 3]);
+                po[(db * 4 + i4) * 64] = make_uint2(pack_bf16x2(oacc[db][4 * i4 + 0] * inv, oacc[db][4 * i4 + 1] * inv),
+                                                    pack_bf16x2(oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv));
         if (half == 0) p.ws_ml[unit * 32 + col] = make_float2(m_run, l_run);
     }
 }
 
-// Merge the per-slice partials of one (tile, 32-row group, channel block):
-// O = sum_s w_s O_s / sum_s w_s l_s with w_s = 2^((m_s - M) c), M = max_s m_s.
-// One wavefront per (tile, row group, 32-channel block); lane layout as the
-// partials.
+// Merge the per-slice partials of one row of one (tile, 32-row group, 8
+// channels): O = sum_s w_s O_s / sum_s w_s l_s with w_s = 2^((m_s - M) c),
+// M = max_s m_s.  One wavefront per (tile, row group, 32-channel block, float4
+// slot i4), four per workgroup; lane layout as the partials (lane half h holds
+// channels 32 db + 8 i4 + 4 h .. +3 of row col).  The slices are taken in
+// batches of kCombineBatch whose loads are all issued before any is used, so a
+// batch costs one memory round trip.
+constexpr int kCombineWaves = 4;
+constexpr int kCombineBatch = 16;
 template <int D>
-__global__ void __launch_bounds__(kThreads) attn_combine_kernel(KParams p) {
+__global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParams p) {
     constexpr int DB = Geo<D>::kDB;
-    const int tile = blockIdx.x;
-    const int db = blockIdx.y;
-    const int rg = threadIdx.x >> 6;
+    const int gw = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
+    const int i4 = gw & 3;
+    const int db = (gw >> 2) % DB;
+    const int rg = (gw / (4 * DB)) % kWaves;
+    const int tile = gw / (4 * DB * kWaves);
+    if (tile >= p.batch * p.hkv * p.row_tiles) return;
     const int lane = threadIdx.x & 63;
     const int col = lane & 31, half = lane >> 5;
     const int rt = tile % p.row_tiles;
@@ -682,46 +694,59 @@ __global__ void __launch_bounds__(kThreads) attn_combine_kernel(KParams p) {
     const int G = p.hq / p.hkv;
     const int rows_b = n * G;
     const int row0 = rt * kTileRows;
-    if (row0 >= rows_b) return;
+    if (row0 + rg * 32 >= rows_b) return;  // (wave-uniform) no rows in this group
     const int row_end = min(rows_b, row0 + kTileRows);
     const int key_end = P + (row_end - 1) / G + 1;
     const int nsplit = min(p.splits, (key_end + p.keys_per_split - 1) / p.keys_per_split);
     const int r = row0 + rg * 32 + col;
-    if (r >= row_end) return;
 
     const int64_t base = (int64_t)tile * p.splits;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p.ws_ml[((base + s) * kWaves + rg) * 32 + col].x);
-    const float mref = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f;
-    float4 acc[4];
+    const float2 *ml = p.ws_ml + (base * kWaves + rg) * 32 + col;
+    const uint2 *po = p.ws_o + (base * kWaves + rg) * (DB * 4 * 64) + (db * 4 + i4) * 64 + lane;
+    constexpr int64_t kMlStride = kWaves * 32;                    // per slice
+    constexpr int64_t kOStride = (int64_t)kWaves * DB * 4 * 64;   // per slice
+    float M = -INFINITY, L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < nsplit; s0 += kCombineBatch) {
+        float2 m_l[kCombineBatch];
+        uint2 o[kCombineBatch];
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) acc[i4] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < nsplit; ++s) {
-        const int64_t unit = (base + s) * kWaves + rg;
-        const float2 ml = p.ws_ml[unit * 32 + col];
-        const float w = __builtin_amdgcn_exp2f((ml.x - mref) * p.c);
-        L = fmaf(w, ml.y, L);
-        const float4 *po = reinterpret_cast<const float4 *>(p.ws_o) + unit * (DB * 4 * 64) + db * 4 * 64 + lane;
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-            const float4 o = po[i4 * 64];
-            acc[i4].x = fmaf(w, o.x, acc[i4].x);
-            acc[i4].y = fmaf(w, o.y, acc[i4].y);
-            acc[i4].z = fmaf(w, o.z, acc[i4].z);
-            acc[i4].w = fmaf(w, o.w, acc[i4].w);
+        for (int u = 0; u < kCombineBatch; ++u) {
+            const int sidx = min(s0 + u, nsplit - 1);  // (clamped: past the end repeats a valid slice)
+            m_l[u] = ml[sidx * kMlStride];
+            o[u] = po[sidx * kOStride];
         }
+        float mb = M;
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u)
+            if (s0 + u < nsplit) mb = fmaxf(mb, m_l[u].x);
+        const float mref = (mb == -INFINITY) ? 0.f : mb;
+        const float a = __builtin_amdgcn_exp2f((M - mref) * p.c);  // 0 when M = -inf
+        L *= a;
+        acc.x *= a;
+        acc.y *= a;
+        acc.z *= a;
+        acc.w *= a;
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) {
+            // slice weight times its sum: the partial holds O / l
+            const float wl = (s0 + u < nsplit) ? __builtin_amdgcn_exp2f((m_l[u].x - mref) * p.c) * m_l[u].y : 0.f;
+            L += wl;
+            acc.x = fmaf(wl, bf16_lo(o[u].x), acc.x);
+            acc.y = fmaf(wl, bf16_hi(o[u].x), acc.y);
+            acc.z = fmaf(wl, bf16_lo(o[u].y), acc.z);
+            acc.w = fmaf(wl, bf16_hi(o[u].y), acc.w);
+        }
+        M = mb;
     }
+    if (r >= row_end) return;
     const float inv = 1.f / L;
     const int node = r / G;
     const int head = g * G + r % G;
     uint16_t *orow = p.out + (((int64_t)lo + node) * p.hq + head) * D;
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = db * 32 + 8 * i4 + 4 * half;
-        *reinterpret_cast<uint2 *>(orow + d) = make_uint2(pack_bf16x2(acc[i4].x * inv, acc[i4].y * inv),
-                                                          pack_bf16x2(acc[i4].z * inv, acc[i4].w * inv));
-    }
+    const int d = db * 32 + 8 * i4 + 4 * half;
+    *reinterpret_cast<uint2 *>(orow + d) =
+        make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
 }
 
 int env_int(const char *name, int dflt) {
@@ -759,7 +784,7 @@ MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefi
     plan.splits = (chunks + cps - 1) / cps;
     if (plan.splits > 1) {
         const size_t rows = (size_t)base_tasks * plan.splits * kTileRows;
-        plan.ws_bytes = rows * head_dim * sizeof(float);
+        plan.ws_bytes = rows * head_dim * sizeof(uint16_t);
         plan.ws_bytes = (plan.ws_bytes + 255) & ~(size_t)255;
         plan.ws_bytes += rows * sizeof(float2);
     }
@@ -793,22 +818,24 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *works
     p.ws_ml = nullptr;
     if (plan.splits > 1) {
         const size_t rows = (size_t)a.batch * a.hkv * plan.row_tiles * plan.splits * kTileRows;
-        size_t off = rows * a.head_dim * sizeof(float);
+        size_t off = rows * a.head_dim * sizeof(uint16_t);
         off = (off + 255) & ~(size_t)255;
-        p.ws_o = (float *)workspace;
+        p.ws_o = (uint2 *)workspace;
         p.ws_ml = (float2 *)((char *)workspace + off);
     }
     const long ntasks = (long)a.batch * a.hkv * plan.splits * plan.row_tiles;
     const long grid = ((ntasks + kXcds - 1) / kXcds) * kXcds;
     const long tiles = (long)a.batch * a.hkv * plan.row_tiles;
+    const long cwaves = tiles * kWaves * (a.head_dim / 32) * 4;
+    const long cblocks = (cwaves + kCombineWaves - 1) / kCombineWaves;
     if (a.head_dim == 128) {
         hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, p);
         if (plan.splits > 1)
-            hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(tiles, Geo<128>::kDB), dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(cblocks), dim3(64 * kCombineWaves), 0, stream, p);
     } else {
         hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, p);
         if (plan.splits > 1)
-            hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(tiles, Geo<64>::kDB), dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(cblocks), dim3(64 * kCombineWaves), 0, stream, p);
     }
     return hipGetLastError();
 }
