@@ -21,10 +21,27 @@ Timing:
 The printed JSON line carries the roofline of tree_attn_verify (algorithmic
 bytes and flops per call over its measured average duration, against the
 MI355X peaks) and the CPU oracle's rate on a bounded sample ('cpu_baseline').
+
+Measured HBM traffic (roofline.traffic) comes from two rocprofv3 counter
+passes over this same script (FETCH_SIZE, then WRITE_SIZE), each run with
+--calib-copy-mib so that a device-to-device copy of known size is in the
+same trace:
+
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -o p -- \
+        python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --calib-copy-mib 256
+    (the same with WRITE_SIZE into OUT/write)
+    python3 bench.py --workload c3 --ingest-traffic OUT/fetch OUT/write
+
+The last step writes profiles/tree_attn_verify_<workload>_traffic.md with
+the per-call bytes and the copy's scale factor; later runs report it only
+while the attention source it was taken on is unchanged (SHA-256).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -43,6 +60,107 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 FP32_VECTOR_PEAK_TFLOPS = 157.3
 METRIC = "verified tree-tokens/sec per GPU; % of HBM-BW / bf16-MFMA roofline"
 COLD_BYTES = 512 << 20
+ATTN_SOURCES = ("tree_attention_verification_bitmask_amd/csrc/attn_mfma.hip",)
+ATTN_KERNELS = ("attn_fwd_kernel", "attn_combine_kernel")
+
+
+def attn_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"tree_attn_verify_{workload}_traffic.md")
+
+
+def _counter_rows(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no rocprofv3 counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def ingest_traffic(workload: str, fetch_dir: str, write_dir: str, calib_mib: int) -> str:
+    """Per-call FETCH_SIZE / WRITE_SIZE of tree_attn_verify (its two kernels,
+    summed per call) from two rocprofv3 --pmc runs, scaled by what the same
+    counters read for the calibration copy of calib_mib MiB."""
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _counter_rows(d) if r["Counter_Name"] == counter]
+        per_kernel = {k: [float(r["Counter_Value"]) for r in rows if k in r["Kernel_Name"]] for k in ATTN_KERNELS}
+        calls = len(per_kernel[ATTN_KERNELS[0]])
+        if calls == 0:
+            raise RuntimeError(f"{counter}: no {ATTN_KERNELS[0]} dispatches in {d}")
+        # average KiB per call: the main kernel every call, the combine when it ran
+        kib = sum(sum(v) for v in per_kernel.values()) / calls
+        # the calibration copy is by far the largest copy in the trace; the
+        # counter need not read its true size (that is what the scale is for)
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        target = calib_mib * 1024.0
+        best = max(copies) if copies else None
+        if best is None or not (0.25 * target <= best <= 4.0 * target):
+            raise RuntimeError(f"{counter}: no calibration copy of ~{calib_mib} MiB in {d}")
+        scale = target / best
+        out[counter] = (kib, best, scale, calls)
+    fk, fcopy, fscale, calls = out["FETCH_SIZE"]
+    wk, wcopy, wscale, _ = out["WRITE_SIZE"]
+    fetch_b = fk * 1024.0 * fscale
+    write_b = wk * 1024.0 * wscale
+    text = (
+        f"# HBM traffic of tree_attn_verify: {workload}\n\n"
+        "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch), from two separate\n"
+        "`rocprofv3 --pmc <counter>` runs of bench.py with `--calib-copy-mib "
+        f"{calib_mib}`; run from /tmp on the GPU box:\n\n"
+        "```\n"
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -o p -- python3 $REPO/bench.py "
+        f"--workload {workload} --steps 5 --warmup 2 --no-cpu-baseline --calib-copy-mib {calib_mib}\n"
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/write -o p -- python3 $REPO/bench.py "
+        f"--workload {workload} --steps 5 --warmup 2 --no-cpu-baseline --calib-copy-mib {calib_mib}\n"
+        f"python3 $REPO/bench.py --workload {workload} --ingest-traffic OUT/fetch OUT/write\n"
+        "```\n\n"
+        "A call of tree_attn_verify is attn_fwd_kernel plus attn_combine_kernel; the\n"
+        "figures are their per-call sums averaged over the calls in the trace.  Each\n"
+        f"counter is scaled by {calib_mib} MiB over what it read for the calibration copy.\n\n"
+        "| counter | KiB per call (raw) | calibration copy (KiB raw) | scale | bytes per call |\n"
+        "|---|---|---|---|---|\n"
+        f"| FETCH_SIZE | {fk:.1f} | {fcopy:.1f} | {fscale:.4f} | {fetch_b:.0f} |\n"
+        f"| WRITE_SIZE | {wk:.1f} | {wcopy:.1f} | {wscale:.4f} | {write_b:.0f} |\n\n"
+        f"calls: {calls}\n\n"
+        f"traffic_bytes_per_call: {fetch_b + write_b:.0f}\n"
+        f"fetch_bytes_per_call: {fetch_b:.0f}\n"
+        f"write_bytes_per_call: {write_b:.0f}\n"
+        f"attn_source_sha256: {attn_source_hash()}\n"
+    )
+    path = traffic_path(workload)
+    with open(path, "w") as f:
+        f.write(text)
+    return path
+
+
+def load_traffic(workload: str):
+    """(bytes per call, detail) from the committed traffic summary, or
+    (None, reason) when there is none or the attention source changed since."""
+    path = traffic_path(workload)
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(("#", "|", "`")):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("attn_source_sha256") != attn_source_hash():
+        return None, "kernel changed since the counters were taken"
+    return float(vals["traffic_bytes_per_call"]), {
+        "fetch_bytes": float(vals["fetch_bytes_per_call"]), "write_bytes": float(vals["write_bytes_per_call"]),
+        "source": os.path.relpath(path, ROOT)}
 
 
 def algorithmic_work(wl):
@@ -103,7 +221,15 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB first (counter calibration)")
+    ap.add_argument("--ingest-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic summary from two rocprofv3 --pmc output folders and exit")
     args = ap.parse_args(argv)
+    if args.ingest_traffic:
+        print(ingest_traffic(args.workload, args.ingest_traffic[0], args.ingest_traffic[1],
+                             args.calib_copy_mib or 256))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this pass is built and timed on a single MI355X); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
@@ -118,6 +244,15 @@ def main(argv=None):
     L = BND.lib()  # raises if the HIP library is missing
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+
+    if args.calib_copy_mib > 0:
+        n_el = args.calib_copy_mib << 18  # float32 elements
+        src_c = torch.ones(n_el, dtype=torch.float32, device=dev)
+        dst_c = torch.empty_like(src_c)
+        torch.cuda.synchronize()
+        dst_c.copy_(src_c)
+        torch.cuda.synchronize()
+        del src_c, dst_c
 
     wl = W.make_workload(args.workload, seed=args.seed, force_path=True)
     fdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
@@ -231,7 +366,9 @@ def main(argv=None):
     else:
         roof = {"bound": "hbm", "achieved": byts / (attn_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    traffic, tdetail = load_traffic(args.workload)
+    roof["traffic"] = traffic
+    roof["traffic_detail"] = tdetail
     roof.update({"kernel": "tree_attn_verify", "avg_us": attn_us,
                  "p10_us": float(np.percentile(attn_ms, 10) * 1e3),
                  "p90_us": float(np.percentile(attn_ms, 90) * 1e3),
