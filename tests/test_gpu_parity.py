@@ -314,6 +314,44 @@ def test_accept_edge_rules():
         assert int(nxt.item()) == expect_next
 
 
+def test_accept_requests_across_node_cap():
+    """Requests of 1023..1500 nodes next to small and empty ones.  The call
+    takes no node cap, so a request above 1024 nodes must give the same walk
+    as one below it.  Binary trees over a 3-token vocabulary, with most
+    drafts set to their parent's target token, give paths that end deep in
+    the tree (node 1024 in the two largest requests) and matching
+    siblings, where the lower index must win."""
+    announce("accept across the node cap")
+    rng = np.random.default_rng(47)
+    sizes = [1500, 100, 1025, 0, 1024, 1023, 64, 65]
+    root = rng.integers(0, 3, len(sizes)).astype(np.int32)
+    par, dr, tg = [], [], []
+    for b, n in enumerate(sizes):
+        p = (np.arange(n) - 1) // 2           # binary heap: node i under (i - 1) // 2
+        p[0:1] = -1
+        t = rng.integers(0, 3, n)
+        want = np.where(p < 0, root[b], t[np.maximum(p, 0)])
+        # 70% of the nodes carry the token their parent's target chose
+        d = np.where(rng.random(n) < 0.7, want, rng.integers(-1, 3, n))
+        d[0:1] = root[b]
+        par.append(p)
+        dr.append(d)
+        tg.append(t)
+    parent, draft, target = (np.concatenate(x).astype(np.int32) for x in (par, dr, tg))
+    cu = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    t = {k: torch.tensor(v, dtype=torch.int32, device="cuda") for k, v in
+         (("parent", parent), ("draft", draft), ("target", target), ("root", root), ("cu", cu))}
+    for md in (64, 5):
+        alen, aidx, nxt, err = B().tree_accept_greedy(t["parent"], t["draft"], t["target"], t["root"], t["cu"], md)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        ref = O.accept_greedy(parent, draft, target, root, cu, md)
+        for g, r in zip((to_np(alen), to_np(aidx), to_np(nxt)), ref):
+            assert np.array_equal(g, r)
+        if md == 64:   # this seed's two largest requests end on node 1024
+            assert ref[1][0, ref[0][0] - 1] == 1024 and ref[1][2, ref[0][2] - 1] == 1024
+
+
 @pytest.mark.parametrize("name,seed", [(n, s) for n in W.CONFIGS for s in (0, 1)])
 def test_compact_parity(name, seed):
     announce(f"compact {name} seed {seed}")

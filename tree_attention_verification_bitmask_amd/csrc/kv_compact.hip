@@ -6,10 +6,11 @@
 //
 // One workgroup per (request, KV head).  The destination rows P+j and the
 // source rows P+idx[j] overlap (a path [0, 2, 5] reads row P+2 and also
-// writes it), so the workgroup first reads every source row of its head slice
-// into LDS, waits on a barrier, and only then writes.  Different KV heads
-// touch disjoint bytes, so workgroups never race.  Rows already in place
-// (idx[j] == j) are skipped.
+// writes it), so the workgroup first reads every source row of its head
+// slice into LDS, waits on a barrier, and only then writes.  Different KV heads touch disjoint bytes, so
+// workgroups never race.  Rows already in place (idx[j] == j) are skipped.
+// The path indices are loaded once, one per thread, checked together (one
+// barrier-wide OR), and shared through LDS.
 #include "tv_device.h"
 #include "tv_launch.h"
 
@@ -17,6 +18,7 @@ namespace tv {
 namespace {
 
 constexpr int kCompactThreads = 256;
+static_assert(TV_MAX_DEPTH <= kCompactThreads, "one path entry per thread");
 
 // ROW_BYTES = head_dim * element size: 128, 256 or 512 bytes.
 template <int ROW_BYTES>
@@ -25,8 +27,9 @@ __global__ void __launch_bounds__(kCompactThreads) kv_compact_kernel(
     const int32_t *__restrict__ kv_start, const int32_t *__restrict__ prefix_len,
     const int32_t *__restrict__ accept_len, const int32_t *__restrict__ accept_idx, int total_nodes,
     int max_depth, int64_t kv_rows, int hkv, int32_t *__restrict__ new_len, int32_t *__restrict__ err) {
-    constexpr int V16 = ROW_BYTES / 16;  // 16-byte vectors per row
-    extern __shared__ uint4 stage[];     // [2][max_depth][V16]
+    constexpr int V16 = ROW_BYTES / 16;                                    // 16-byte vectors per row
+    extern __shared__ uint4 stage[];                                       // [2][max_depth][V16]
+    __shared__ int32_t sidx[TV_MAX_DEPTH];
     const int b = blockIdx.x;
     const int g = blockIdx.y;
     const int tid = threadIdx.x;
@@ -39,13 +42,13 @@ __global__ void __launch_bounds__(kCompactThreads) kv_compact_kernel(
         if (g == 0 && tid == 0) report(err, TV_DEVERR_BAD_REQUEST, b);
         return;
     }
-    const int32_t *idx = accept_idx + (int64_t)b * max_depth;
-    for (int j = 0; j < L; ++j) {
-        const int s = idx[j];
-        if (s < 0 || s >= n) {
-            if (g == 0 && tid == 0) report(err, TV_DEVERR_BAD_PATH, b);
-            return;  // uniform across the workgroup: every thread reads the same idx
-        }
+    int s = 0;
+    if (tid < L) s = accept_idx[(int64_t)b * max_depth + tid];
+    const bool bad = tid < L && (s < 0 || s >= n);
+    if (tid < L) sidx[tid] = s;
+    if (__syncthreads_or(bad)) {  // uniform: every thread sees the same OR
+        if (g == 0 && tid == 0) report(err, TV_DEVERR_BAD_PATH, b);
+        return;
     }
     const int64_t row_stride = (int64_t)hkv * ROW_BYTES;  // bytes per cache row
     const int64_t base = (ks + P) * row_stride + (int64_t)g * ROW_BYTES;
@@ -54,14 +57,14 @@ __global__ void __launch_bounds__(kCompactThreads) kv_compact_kernel(
     const int work = L * V16;
     for (int e = tid; e < work; e += kCompactThreads) {
         const int j = e / V16, c = e % V16;
-        const int64_t off = base + (int64_t)idx[j] * row_stride + c * 16;
+        const int64_t off = base + (int64_t)sidx[j] * row_stride + c * 16;
         sk[e] = *reinterpret_cast<const uint4 *>(kc + off);
         sv[e] = *reinterpret_cast<const uint4 *>(vc + off);
     }
     __syncthreads();
     for (int e = tid; e < work; e += kCompactThreads) {
         const int j = e / V16, c = e % V16;
-        if (idx[j] == j) continue;
+        if (sidx[j] == j) continue;
         const int64_t off = base + (int64_t)j * row_stride + c * 16;
         *reinterpret_cast<uint4 *>(kc + off) = sk[e];
         *reinterpret_cast<uint4 *>(vc + off) = sv[e];
@@ -77,11 +80,12 @@ hipError_t launch_kv_compact(void *k, void *v, const int32_t *cu_nodes, const in
                              int64_t kv_rows, int hkv, int head_dim, tv_dtype dtype, int32_t *new_len,
                              int32_t *err, hipStream_t stream) {
     if (batch == 0) return hipSuccess;
+    if (max_depth > TV_MAX_DEPTH) return hipErrorInvalidValue;
     const int row_bytes = head_dim * (dtype == TV_F32 ? 4 : 2);
     const size_t shmem = 2 * (size_t)max_depth * row_bytes;
     dim3 grid(batch, hkv);
 #define TV_COMPACT(RB)                                                                           \
-    hipLaunchKernelGGL(kv_compact_kernel<RB>, grid, dim3(kCompactThreads), shmem, stream,          \
+    hipLaunchKernelGGL(kv_compact_kernel<RB>, grid, dim3(kCompactThreads), shmem, stream,         \
                        (uint8_t *)k, (uint8_t *)v, cu_nodes, kv_start, prefix_len, accept_len,      \
                        accept_idx, total_nodes, max_depth, kv_rows, hkv, new_len, err)
     switch (row_bytes) {
