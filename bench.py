@@ -65,10 +65,16 @@ ATTN_KERNELS = ("attn_fwd_kernel", "attn_combine_kernel")
 
 
 def attn_source_hash() -> str:
+    """SHA-256 of the attention source's code: line comments and blank space
+    are dropped first, so an edit to comments alone keeps the stored counter
+    figures valid while any change to the code voids them."""
     h = hashlib.sha256()
     for rel in ATTN_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].split()
+                if code:
+                    h.update(" ".join(code).encode() + b"\n")
     return h.hexdigest()
 
 

@@ -92,10 +92,11 @@ def test_workspace_sizes(L):
     # fp32 and tiny trees take the VALU path, which needs no workspace
     assert L.tree_attn_verify_workspace_size(1, 16, 16, 128, 2, 1, 64, 0) == 0
     assert L.tree_attn_verify_workspace_size(1, 4, 4, 128, 8, 8, 128, 1) == 0   # 4 rows per KV head
-    # bf16 Qwen3-shaped layers split the key axis and need fp32 partials
+    # bf16 Qwen3-shaped layers split the key axis: bf16 partials (256 B per
+    # row and slice) and fp32 (m, l) per row and slice
     for B, T, n, P in ((1, 64, 64, 1024), (1, 128, 128, 4096), (1, 256, 256, 8192), (8, 1024, 128, 8192)):
         ws = L.tree_attn_verify_workspace_size(B, T, n, P, 32, 8, 128, 1)
-        assert ws % 8 == 0 and ws >= 0
+        assert ws % 8 == 0 and ws >= 8 * 4 * n * 264
     # invalid sizes report 0
     assert L.tree_attn_verify_workspace_size(1, 16, 16, 128, 3, 2, 64, 1) == 0
 
@@ -137,3 +138,14 @@ def test_binding_refuses_cpu_tensors(L):
     x = torch.zeros(4, dtype=torch.int32)
     with pytest.raises(ValueError):
         BND.tree_mask_build(x, x, x, 4, 4)
+
+
+def test_binding_constants_match_header():
+    """The binding's copies of the header's limits and codes are the header's."""
+    import re
+    text = open(os.path.join(os.path.dirname(__file__), "..", "include", "treeverify.h")).read()
+    defs = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (TV_\w+) (\d+)", text)}
+    assert defs["TV_MAX_NODES"] == BND.TV_MAX_NODES
+    assert defs["TV_MAX_DEPTH"] == BND.TV_MAX_DEPTH
+    for name in ("BAD_PARENT", "TOO_DEEP", "BAD_REQUEST", "BAD_PATH"):
+        assert defs["TV_DEVERR_" + name] == getattr(BND, "DEVERR_" + name)

@@ -234,6 +234,34 @@ def test_attn_deterministic():
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+def _attn_call(wl, d, anc, workspace=None):
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = B().tree_attn_verify(d["q"], d["k"], d["v"], d["cu"], d["ks"], d["P"], anc, wl.max_nodes,
+                               wl.max_prefix, err=err, workspace=workspace)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), int(err.item())
+
+
+def test_attn_workspace_reused_across_shapes():
+    """One workspace through calls of different shapes, starting from
+    garbage: each output equals the one with a fresh workspace (its contents
+    on entry do not matter)."""
+    announce("attn workspace reuse")
+    wls = {n: W.make_workload(n, seed=5) for n in ("c3", "c2", "c4")}
+    need = max(B().tree_attn_verify_workspace_size(len(w.cu_nodes) - 1, w.total_nodes, w.max_nodes,
+                                                   w.max_prefix, w.hq, w.hkv, w.d, B().TV_BF16)
+               for w in wls.values())
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    for name in ("c3", "c2", "c4", "c3", "c2"):
+        wl = wls[name]
+        d = dev_workload(wl)
+        anc, _, _, _ = B().tree_mask_build(d["parent"], d["cu"], d["P"], wl.max_nodes, 64)
+        got, e1 = _attn_call(wl, d, anc, workspace=ws)
+        assert e1 == 0
+        ref, e2 = _attn_call(wl, d, anc)
+        assert e2 == 0 and np.array_equal(got.view(np.uint32), ref.view(np.uint32)), name
+
+
 def test_attn_device_error_for_inconsistent_request():
     """prefix_len above max_prefix: the request is reported and skipped."""
     announce("attn device error word")

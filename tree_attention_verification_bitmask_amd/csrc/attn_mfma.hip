@@ -23,16 +23,14 @@
 // 16-byte granule of a cached K/V row lands at an XOR-swizzled position in its
 // LDS row so the matrix-operand reads below are free of bank conflicts.
 //
-// Per-wave software pipeline.  Step i of a wave runs, in this order,
-//   S(i+1) = Q K(i+1)^T   (eight MFMAs, K(i+1) already in registers),
-//   the softmax of chunk i on S(i) (computed one step earlier),
-//   reads of K(i+2) from LDS into registers (for the next step),
-//   O += P(i) V(i)        (eight MFMAs, V(i) already in registers),
-//   reads of V(i+1) from LDS into registers.
-// Operands are read one step ahead, so LDS latency never stalls a matrix
-// product, and the vector work of the softmax has the products of the other
-// wave on the SIMD (and its own S(i+1) chain) to hide behind.  The steady
-// state is unrolled by eight so every ring offset is an immediate.
+// Ping-pong schedule.  Waves 0-3 (group A) and 4-7 (group B) share the four
+// SIMDs, one of each per SIMD.  For chunk j a wave runs a vector phase V(j)
+// (the softmax of S(j)) and a matrix phase M(j) (O += P(j) V(j), then
+// S(j+1) = Q K(j+1)^T, 16 MFMAs, with the operand registers of the next
+// phase refilled from LDS right after each product).  A barrier separates
+// the phases, and group B runs one phase behind group A, so on every SIMD one
+// wave feeds the matrix core while the other computes exponentials.  The
+// operands are read one phase ahead, so LDS latency never stalls a product.
 //
 // Transposed products.  S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = 32 keys
 // x 16 channels of K read from LDS, B = Q^T held in registers.  LDS row i of a
@@ -59,8 +57,8 @@
 //
 // Split key axis.  The host picks `splits` slices of `keys_per_split` keys so
 // that the grid fills the chip.  With one slice the kernel writes the
-// normalised output; otherwise it writes fp32 partials (unnormalised O, the
-// reference m, the sum l) and attn_combine_kernel merges them.
+// normalised output; otherwise it writes partials (O / l in bf16, with the
+// fp32 reference m and sum l) and attn_combine_kernel merges them.
 //
 // XCD-aware order.  Workgroup ids are dealt round-robin to the 8 XCDs; the
 // kernel maps id -> task so that each XCD gets a contiguous block of tasks,
@@ -99,7 +97,7 @@ constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
 // i + kAhead - kStages - 1 <= i - 1.  K(i+2) must have been issued before
 // step i, i.e. kAhead >= 3.
 static_assert(kAhead >= 3 && kAhead <= kStages, "ring depth");
-static_assert(kStages == 8, "the main loop is unrolled by the ring depth");
+static_assert(kStages * 2 * 32 * 256 + 256 * 16 * 8 <= 160 * 1024, "K/V rings and ancestor rows fit the 160 KB LDS");
 
 template <int D>
 struct Geo {
