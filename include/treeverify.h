@@ -7,6 +7,8 @@
  *         Tree Attention Accelerate LLM Serving" (llms.blog).
  *   [DT]  "DominoTree: Conditional Tree-Structured Drafting with Domino for
  *         Speculative Decoding" (arXiv 2607.08642).
+ *   [DAR] "DARTree: Speculative Diffusion Decoding with Autoregressive Draft
+ *         Trees" (gist.science), Technical Summary.
  *
  * A batch holds B requests.  Request b owns:
  *   - draft-tree nodes cu_nodes[b] .. cu_nodes[b+1]-1 of every per-node array
@@ -68,12 +70,14 @@ typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
 #define TV_MAX_NODES 1024          /* nodes per request                   */
 #define TV_MAX_DEPTH 64            /* levels per tree / accepted tokens   */
 #define TV_MAX_TOTAL_NODES 16777215 /* nodes per batch (24-bit error index) */
+#define TV_MAX_LEDGER 8192         /* ledger slots (depths x lanes) per request */
 
 /* device error codes (the top byte of the err word) */
 #define TV_DEVERR_BAD_PARENT 1  /* parent[v] not in [-1, v); index = global node v       */
 #define TV_DEVERR_TOO_DEEP 2    /* level(i) > max_depth; index = global node i           */
 #define TV_DEVERR_BAD_REQUEST 3 /* request sizes disagree with the host sizes; index = b */
 #define TV_DEVERR_BAD_PATH 4    /* accepted path entry out of range; index = b           */
+#define TV_DEVERR_BAD_LEDGER 5  /* chosen slot whose parent is unusable; index = b       */
 
 /* Human-readable name of a tv_status value (static string). */
 const char *tv_status_string(int status);
@@ -205,6 +209,40 @@ tv_status kv_compact_path(void *k_cache, void *v_cache, const int32_t *cu_nodes,
                           int32_t total_nodes, int32_t max_depth, int64_t kv_rows, int32_t hkv,
                           int32_t head_dim, tv_dtype dtype, int32_t *new_kv_len, int32_t *err,
                           void *stream);
+
+/*
+ * tree_select_topb -- the draft tree chosen in one step from a frontier ledger.
+ *
+ * Defines: [DT] section 3.3 and Appendix B: the frontier builder writes every
+ * scored candidate to a ledger [batch, D, W*k] with its cumulative
+ * log-probability and parent pointer; after the last depth the tree is the
+ * ledger's global top B, ordered so parents precede children, parent pointers
+ * remapped, short trees padded with dead leaves.  [DAR] "2. Deferred
+ * Best-First Pruning": the same global top B with a depth bonus beta added
+ * to each candidate's score; for beta <= 0 (and W = B) it equals the
+ * sequential best-first heap's tree.
+ * Readings: key = score + beta * level (level = t + 1 for ledger depth t),
+ * evaluated in double; keys rank descending, equal keys by depth then slot;
+ * the output lists the chosen candidates in that rank order; a dead leaf has
+ * parent -1 and token -1 (never accepted by tree_accept_greedy).
+ *
+ * In:  score [B, D, L] float32 (non-finite = empty slot); parent [B, D, L]
+ *      int32: -1 at depth 0, else the slot (0..L-1) of the parent candidate
+ *      at depth t-1; token [B, D, L] int32.  batch = B >= 0;
+ *      1 <= depth <= TV_MAX_DEPTH; lanes = L >= 1 with depth*L <=
+ *      TV_MAX_LEDGER; 1 <= budget <= TV_MAX_NODES; beta finite.
+ * Out: tree_parent [B, budget] int32 (request-local, parents first),
+ *      tree_token [B, budget] int32, n_real [B] int32 = min(budget, finite
+ *      slots): positions >= n_real are dead leaves.  The output is the input
+ *      of tree_mask_build with cu_nodes[b] = b * budget.
+ * err: BAD_LEDGER when a chosen candidate's parent slot is out of range, not
+ *      chosen, or ranked after it (only when keys rise along a path, e.g.
+ *      beta > 0); that candidate becomes a dead leaf.
+ */
+tv_status tree_select_topb(const float *score, const int32_t *parent, const int32_t *token,
+                           int32_t batch, int32_t depth, int32_t lanes, int32_t budget, float beta,
+                           int32_t *tree_parent, int32_t *tree_token, int32_t *n_real, int32_t *err,
+                           void *stream);
 
 #ifdef __cplusplus
 }

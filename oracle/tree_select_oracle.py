@@ -36,11 +36,12 @@ design notes):
     pop order.
   * dead leaves: parent -1 (a root child) and token -1, which the greedy
     walk never accepts.
-  * a selected candidate whose parent slot is out of range or not selected
-    (possible only when keys rise along a path, e.g. beta > 0) is reported
-    as a bad ledger and emitted as a dead leaf.
+  * a selected candidate whose parent slot is out of range, not selected, or
+    ranked after it (possible only when keys rise along a path, e.g.
+    beta > 0) is reported as a bad ledger and emitted as a dead leaf, so the
+    output always lists parents before children.
 
-Parity pins (tests/test_oracle_pins.py): selection against a brute-force
+Parity pins (tests/test_select_pins.py): selection against a brute-force
 ranking written independently, the heap equivalence on tie-free inputs at
 batch sizes 1, 2, 5 and 32 ([DT] Appendix B), ancestor closure, the dead-leaf
 padding and the bad-ledger report.
@@ -52,7 +53,7 @@ import zlib
 
 import numpy as np
 
-ERR_BAD_LEDGER = 5  # a selected candidate's parent is out of range or not selected
+ERR_BAD_LEDGER = 5  # a selected candidate's parent is out of range, unselected or ranked later
 
 
 def _enc(code: int, index: int) -> int:
@@ -98,8 +99,9 @@ def select_one(score, parent, token, budget: int, beta: float):
             ok = p == -1
             pp = -1
         else:
-            ok = 0 <= p < L and ((t - 1) * L + p) in pos
-            pp = pos.get((t - 1) * L + p, -1) if ok else -1
+            # the parent must be chosen and ranked before its child
+            ok = 0 <= p < L and pos.get((t - 1) * L + p, i) < i
+            pp = pos[(t - 1) * L + p] if ok else -1
         if not ok:
             bad = True
             continue  # dead leaf: parent -1, token -1

@@ -147,5 +147,27 @@ def test_binding_constants_match_header():
     defs = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (TV_\w+) (\d+)", text)}
     assert defs["TV_MAX_NODES"] == BND.TV_MAX_NODES
     assert defs["TV_MAX_DEPTH"] == BND.TV_MAX_DEPTH
-    for name in ("BAD_PARENT", "TOO_DEEP", "BAD_REQUEST", "BAD_PATH"):
+    assert defs["TV_MAX_LEDGER"] == BND.TV_MAX_LEDGER
+    for name in ("BAD_PARENT", "TOO_DEEP", "BAD_REQUEST", "BAD_PATH", "BAD_LEDGER"):
         assert defs["TV_DEVERR_" + name] == getattr(BND, "DEVERR_" + name)
+
+
+def select(L, score=FAKE, parent=FAKE, token=FAKE, B=1, D=4, Ln=8, budget=16, beta=0.0, tp=FAKE,
+           tt=FAKE, nr=FAKE):
+    return L.tree_select_topb(score, parent, token, B, D, Ln, budget, beta, tp, tt, nr, None, None)
+
+
+def test_select_host_checks(L):
+    assert select(L, B=-1) == SHAPE
+    assert select(L, D=0) == SHAPE
+    assert select(L, Ln=0) == SHAPE
+    assert select(L, budget=0) == SHAPE
+    assert select(L, D=65) == LIMIT
+    assert select(L, budget=1025) == LIMIT
+    assert select(L, D=64, Ln=129) == LIMIT          # 8256 slots > TV_MAX_LEDGER
+    assert select(L, beta=float("nan")) == SHAPE
+    assert select(L, beta=float("inf")) == SHAPE
+    assert select(L, tp=None) == NULL
+    assert select(L, score=None) == NULL
+    assert select(L, B=0, score=None, parent=None, token=None) == OK
+    assert select(L, B=0, D=64, Ln=128, budget=1024) == OK   # largest sizes, empty batch

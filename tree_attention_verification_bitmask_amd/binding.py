@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(PKG, "libtreeverify.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "treeverify.h")
 
 TV_F32, TV_BF16 = 0, 1
-TV_MAX_NODES, TV_MAX_DEPTH = 1024, 64
-DEVERR_BAD_PARENT, DEVERR_TOO_DEEP, DEVERR_BAD_REQUEST, DEVERR_BAD_PATH = 1, 2, 3, 4
+TV_MAX_NODES, TV_MAX_DEPTH, TV_MAX_LEDGER = 1024, 64, 8192
+DEVERR_BAD_PARENT, DEVERR_TOO_DEEP, DEVERR_BAD_REQUEST, DEVERR_BAD_PATH, DEVERR_BAD_LEDGER = 1, 2, 3, 4, 5
 
 
 class TreeVerifyError(RuntimeError):
@@ -56,6 +56,8 @@ def lib() -> C.CDLL:
     L.kv_compact_path.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, C.c_int,
                                   vp, vp, vp]
     L.kv_compact_path.restype = C.c_int
+    L.tree_select_topb.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp]
+    L.tree_select_topb.restype = C.c_int
     _lib = L
     return L
 
@@ -211,3 +213,28 @@ def kv_compact_path(k_cache, v_cache, cu_nodes, kv_start, prefix_len, accept_len
         _ptr(accept_len), _ptr(accept_idx), B, total_nodes, max_depth, rows, hkv, d, code,
         _ptr(new_kv_len), _ptr(err), _stream(stream)))
     return new_kv_len, err
+
+
+def tree_select_topb(score, parent, token, budget: int, beta: float = 0.0, tree_parent=None,
+                     tree_token=None, n_real=None, err=None, stream=None):
+    """score float32 / parent int32 / token int32 [B, D, L] -> (tree_parent int32
+    [B, budget], tree_token int32 [B, budget], n_real int32 [B], err)."""
+    import torch
+    if score.dim() != 3 or tuple(parent.shape) != tuple(score.shape) or tuple(token.shape) != tuple(score.shape):
+        raise ValueError("score, parent and token must share one [batch, depth, lanes] shape")
+    B, D, L = score.shape
+    dev = score.device
+    _need(score, "score", torch.float32)
+    _need(parent, "parent", torch.int32)
+    _need(token, "token", torch.int32)
+    tree_parent = torch.empty((B, budget), dtype=torch.int32, device=dev) if tree_parent is None else tree_parent
+    tree_token = torch.empty((B, budget), dtype=torch.int32, device=dev) if tree_token is None else tree_token
+    n_real = torch.empty(B, dtype=torch.int32, device=dev) if n_real is None else n_real
+    err = torch.zeros(1, dtype=torch.int32, device=dev) if err is None else err
+    _need(tree_parent, "tree_parent", torch.int32, B * budget)
+    _need(tree_token, "tree_token", torch.int32, B * budget)
+    _need(n_real, "n_real", torch.int32, B)
+    _check("tree_select_topb", lib().tree_select_topb(
+        _ptr(score), _ptr(parent), _ptr(token), B, D, L, budget, float(beta), _ptr(tree_parent),
+        _ptr(tree_token), _ptr(n_real), _ptr(err), _stream(stream)))
+    return tree_parent, tree_token, n_real, err

@@ -169,4 +169,19 @@ tv_status kv_compact_path(void *k_cache, void *v_cache, const int32_t *cu_nodes,
                                                (hipStream_t)stream));
 }
 
+tv_status tree_select_topb(const float *score, const int32_t *parent, const int32_t *token,
+                           int32_t batch, int32_t depth, int32_t lanes, int32_t budget, float beta,
+                           int32_t *tree_parent, int32_t *tree_token, int32_t *n_real, int32_t *err,
+                           void *stream) {
+    if (batch < 0 || depth < 1 || lanes < 1 || budget < 1) return TV_ERR_SHAPE;
+    if (batch > 65535 || depth > TV_MAX_DEPTH || budget > TV_MAX_NODES) return TV_ERR_LIMIT;
+    if ((int64_t)depth * lanes > TV_MAX_LEDGER) return TV_ERR_LIMIT;
+    if (!(beta == beta) || beta > 3.0e38f || beta < -3.0e38f) return TV_ERR_SHAPE;
+    if (!tree_parent || !tree_token || !n_real) return TV_ERR_NULL;
+    if (batch > 0 && (!score || !parent || !token)) return TV_ERR_NULL;
+    if (batch == 0) return TV_OK;
+    return launch_status(tv::launch_select_topb(score, parent, token, batch, depth, lanes, budget, beta,
+                                                tree_parent, tree_token, n_real, err, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -25,6 +25,10 @@ hipError_t launch_kv_compact(void *k, void *v, const int32_t *cu_nodes, const in
                              int64_t kv_rows, int hkv, int head_dim, tv_dtype dtype, int32_t *new_len,
                              int32_t *err, hipStream_t stream);
 
+hipError_t launch_select_topb(const float *score, const int32_t *parent, const int32_t *token, int batch,
+                              int depth, int lanes, int budget, float beta, int32_t *tree_parent,
+                              int32_t *tree_token, int32_t *n_real, int32_t *err, hipStream_t stream);
+
 // Problem description shared by the attention kernels.
 struct AttnArgs {
     const void *q, *k, *v;

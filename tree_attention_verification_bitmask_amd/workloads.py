@@ -403,3 +403,75 @@ def make_from_trees(parents: list, prefix_len: list, hq: int, hkv: int, d: int,
         target=np.concatenate(targets).astype(np.int32) if B else np.zeros(0, np.int32),
         root_target=np.array(roots, dtype=np.int32), seed=seed, meta=dict(values=values),
     )
+
+
+# ---------------------------------------------------------------------------
+# Frontier ledgers: the input of tree_select_topb ([DT] section 3.3 and
+# Appendix B: [batch, D, W*k] slots, each a cumulative log-probability, a
+# parent slot at the previous depth and a draft token).
+# ---------------------------------------------------------------------------
+
+def random_ledger(rng: np.random.Generator, batch: int, depth: int, width: int, k: int,
+                  p_empty: float = 0.0, tie_step: float = 0.0):
+    """A ledger whose scores never rise along a parent pointer: slot e of
+    depth t (lane e // k, child e % k) hangs under a random live slot of depth
+    t - 1 and scores its parent's score minus a positive step (an exponential
+    draw, or a multiple of ``tie_step`` -- zero included -- when it is set, to
+    make ties).  A fraction ``p_empty`` of slots is empty (score -inf).
+    Returns (score float32, parent int32, token int32), each [batch, depth,
+    width * k]."""
+    L = width * k
+    score = np.full((batch, depth, L), -np.inf, np.float32)
+    parent = np.full((batch, depth, L), -1, np.int32)
+    token = rng.integers(0, 151936, (batch, depth, L)).astype(np.int32)
+    for b in range(batch):
+        for t in range(depth):
+            if tie_step > 0:
+                step = (rng.integers(0, 4, L) * tie_step).astype(np.float32)
+            else:
+                step = rng.exponential(0.7, L).astype(np.float32)
+            live = rng.random(L) >= p_empty
+            if t == 0:
+                score[b, 0, live] = -step[live]
+                continue
+            prev = np.flatnonzero(np.isfinite(score[b, t - 1]))
+            if prev.size == 0:
+                continue
+            par = prev[rng.integers(0, prev.size, L)]
+            parent[b, t] = par
+            s = (score[b, t - 1, par] - step).astype(np.float32)
+            score[b, t, live] = s[live]
+    return score, parent, token
+
+
+def frontier_shaped_ledger(rng: np.random.Generator, batch: int, depth: int, width: int, k: int):
+    """A ledger with the frontier builder's shape ([DT] section 3.3): depth 1
+    holds the root's k children; at every later depth the `width` best slots
+    of the previous depth (by score; ties by slot) are the lanes, and lane l's
+    k children fill slots l*k .. l*k+k-1 with probabilities p_r ~ gamma^r
+    (gamma ~ U(0.2, 0.8) per lane, normalised) added to the lane's score in
+    float32.  Slots of lanes that do not exist stay empty.  Returns (score
+    float32, parent int32, token int32), each [batch, depth, width * k]."""
+    L = width * k
+    score = np.full((batch, depth, L), -np.inf, np.float32)
+    parent = np.full((batch, depth, L), -1, np.int32)
+    token = np.full((batch, depth, L), -1, np.int32)
+    r = np.arange(k)
+    for b in range(batch):
+        lane_slot = np.array([-1])
+        lane_score = np.zeros(1, np.float32)
+        for t in range(depth):
+            nl = lane_slot.size
+            gamma = rng.uniform(0.2, 0.8, nl)
+            w = gamma[:, None] ** r[None, :]
+            logp = np.log(w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+            slots = (np.arange(nl)[:, None] * k + r[None, :]).reshape(-1)
+            score[b, t, slots] = (lane_score[:, None] + logp).reshape(-1).astype(np.float32)
+            parent[b, t, slots] = np.repeat(lane_slot, k) if t > 0 else -1
+            for li in range(nl):
+                token[b, t, li * k:(li + 1) * k] = rng.choice(151936, size=k, replace=False)
+            live = np.flatnonzero(np.isfinite(score[b, t]))
+            order = live[np.lexsort((live, -score[b, t, live].astype(np.float64)))]
+            lane_slot = order[:width].astype(np.int32)
+            lane_score = score[b, t, lane_slot]
+    return score, parent, token
