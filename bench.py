@@ -231,6 +231,12 @@ def main(argv=None):
                     help="run one device-to-device copy of this many MiB first (counter calibration)")
     ap.add_argument("--ingest-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from two rocprofv3 --pmc output folders and exit")
+    ap.add_argument("--select", action="store_true",
+                    help="time tree_select_topb (draft tree from a frontier ledger) instead of the pass")
+    ap.add_argument("--select-batch", type=int, default=32)
+    ap.add_argument("--select-budget", type=int, default=64)
+    ap.add_argument("--select-depth", type=int, default=16)
+    ap.add_argument("--select-k", type=int, default=4)
     args = ap.parse_args(argv)
     if args.ingest_traffic:
         print(ingest_traffic(args.workload, args.ingest_traffic[0], args.ingest_traffic[1],
@@ -250,6 +256,9 @@ def main(argv=None):
     L = BND.lib()  # raises if the HIP library is missing
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+
+    if args.select:
+        return bench_select(args, torch, BND, L, dev)
 
     if args.calib_copy_mib > 0:
         n_el = args.calib_copy_mib << 18  # float32 elements
@@ -404,6 +413,82 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_select(args, torch, BND, L, dev):
+    """One step = one tree_select_topb call over a batch of frontier-shaped
+    ledgers ([batch, depth, budget * k] slots: W = B lanes of k children per
+    depth, as [DT] section 3.3 sets them), rotated over enough copies to keep
+    the Infinity Cache cold.  value = draft trees selected per second."""
+    Bt, Bn, D, k = args.select_batch, args.select_budget, args.select_depth, args.select_k
+    L_ = Bn * k
+    rng = np.random.default_rng(args.seed)
+    score, parent, token = W.frontier_shaped_ledger(rng, Bt, D, Bn, k)
+    set_bytes = score.nbytes + parent.nbytes + token.nbytes
+    R = max(1, math.ceil(COLD_BYTES / set_bytes))
+    sc0 = torch.from_numpy(score).to(dev)
+    pa0 = torch.from_numpy(parent).to(dev)
+    tk0 = torch.from_numpy(token).to(dev)
+    sets = [(sc0.clone(), pa0.clone(), tk0.clone()) for _ in range(R)]
+    tp = torch.empty((Bt, Bn), dtype=torch.int32, device=dev)
+    tt = torch.empty((Bt, Bn), dtype=torch.int32, device=dev)
+    nr = torch.empty(Bt, dtype=torch.int32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = C_void(stream.cuda_stream)
+    P_ = lambda t: C_void(t.data_ptr())  # noqa: E731
+    call_args = [(P_(a), P_(b), P_(c), Bt, D, L_, Bn, 0.0, P_(tp), P_(tt), P_(nr), P_(err), sp)
+                 for (a, b, c) in sets]
+    for i in range(args.warmup):
+        if L.tree_select_topb(*call_args[i % R]):
+            raise RuntimeError("tree_select_topb rejected its arguments")
+    torch.cuda.synchronize()
+    if int(err.item()) != 0:
+        raise RuntimeError(f"device error word {int(err.item()):#x}")
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1 << 24)
+    start.record(stream)
+    for i in range(K):
+        evs[i][0].record(stream)
+        L.tree_select_topb(*call_args[(args.warmup + i) % R])
+        evs[i][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    call_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_step = start.elapsed_time(end) / K
+    us = float(call_ms.mean() * 1e3)
+    byts = Bt * D * L_ * 12 + Bt * Bn * 8 + Bt * 4   # ledger read once, tree and counts written
+    roof = {"bound": "hbm", "achieved": byts / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "traffic": None, "traffic_detail": "not measured for this kernel",
+            "kernel": "tree_select_topb", "avg_us": us,
+            "p10_us": float(np.percentile(call_ms, 10) * 1e3), "p90_us": float(np.percentile(call_ms, 90) * 1e3),
+            "alg_bytes": byts}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    line = {
+        "metric": "draft trees selected per second (tree_select_topb)",
+        "value": Bt / (us * 1e-6),
+        "unit": "trees/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64 keys, int32",
+        "data": "synthetic",
+        "config": {"workload": f"frontier ledgers: batch {Bt}, depth {D}, W = B = {Bn} lanes x k = {k}",
+                   "seed": args.seed, "ledger_slots_per_request": D * L_, "cold_cache_sets": R},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import tree_select_oracle as S
+        t0 = time.perf_counter()
+        n = 0
+        while n < Bt and time.perf_counter() - t0 < args.cpu_budget:
+            S.select_one(score[n], parent[n], token[n], Bn, 0.0)
+            n += 1
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": n / dt, "unit": "trees/s", "cores": 1, "kind": "oracle",
+                                "sample": f"select_one on requests 0..{n - 1} of the same ledgers ({dt:.2f} s)"}
     print(json.dumps(line), flush=True)
     return 0
 
