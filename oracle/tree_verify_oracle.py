@@ -292,3 +292,21 @@ def kv_compact(k, v, kv_start, prefix_len, accept_len, accept_idx):
             v2[base + j] = v[src]
         new_len[b] = int(prefix_len[b]) + L
     return k2, v2, new_len
+
+
+# ---------------------------------------------------------------------------
+# O-argmax: the target's choice at each node ([TSD] "Verification and
+# Acceptance Algorithms", greedy tree verification: the target prediction at
+# a node is the argmax of its logits)
+# ---------------------------------------------------------------------------
+
+def target_argmax(logits) -> np.ndarray:
+    """Row-wise argmax of logits [rows, vocab] (fp32, or bf16 widened exactly
+    to fp32 by the caller).  Readings: the lowest index wins a tie (-0 and +0
+    are equal); a NaN ranks above every number, so a row holding NaN returns
+    its first NaN.  numpy's argmax implements exactly this rule and serves as
+    the step."""
+    x = np.asarray(logits, dtype=np.float64)
+    if x.shape[1] == 0:
+        raise ValueError("vocab must be at least 1")
+    return np.argmax(x, axis=1).astype(np.int32)
