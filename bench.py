@@ -237,6 +237,11 @@ def main(argv=None):
     ap.add_argument("--select-budget", type=int, default=64)
     ap.add_argument("--select-depth", type=int, default=16)
     ap.add_argument("--select-k", type=int, default=4)
+    ap.add_argument("--argmax", action="store_true",
+                    help="time tree_target_argmax (the target's choice per node) instead of the pass")
+    ap.add_argument("--argmax-rows", type=int, default=129)
+    ap.add_argument("--argmax-vocab", type=int, default=151936)
+    ap.add_argument("--argmax-dtype", default="f32", choices=["f32", "bf16"])
     args = ap.parse_args(argv)
     if args.ingest_traffic:
         print(ingest_traffic(args.workload, args.ingest_traffic[0], args.ingest_traffic[1],
@@ -259,6 +264,8 @@ def main(argv=None):
 
     if args.select:
         return bench_select(args, torch, BND, L, dev)
+    if args.argmax:
+        return bench_argmax(args, torch, BND, L, dev)
 
     if args.calib_copy_mib > 0:
         n_el = args.calib_copy_mib << 18  # float32 elements
@@ -489,6 +496,77 @@ def bench_select(args, torch, BND, L, dev):
         dt = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": n / dt, "unit": "trees/s", "cores": 1, "kind": "oracle",
                                 "sample": f"select_one on requests 0..{n - 1} of the same ledgers ({dt:.2f} s)"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_argmax(args, torch, BND, L, dev):
+    """One step = one tree_target_argmax call over [rows, vocab] logits (the
+    default 129 x 151936 fp32 is c3's 128 tree nodes plus the root row at the
+    Qwen3 vocabulary, 78 MB), rotated over enough copies to keep the
+    Infinity Cache cold.  value = node choices per second."""
+    rows, V = args.argmax_rows, args.argmax_vocab
+    bf = args.argmax_dtype == "bf16"
+    es = 2 if bf else 4
+    rng = np.random.default_rng(args.seed)
+    x = torch.from_numpy(rng.normal(0, 3, (rows, V)).astype(np.float32)).to(dev)
+    if bf:
+        x = x.to(torch.bfloat16)
+    set_bytes = rows * V * es
+    R = max(2, math.ceil(COLD_BYTES / set_bytes))
+    sets = [x.clone() for _ in range(R)]
+    del x
+    tok = torch.empty(rows, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = C_void(stream.cuda_stream)
+    code = BND.TV_BF16 if bf else BND.TV_F32
+    call_args = [(C_void(t.data_ptr()), rows, V, code, C_void(tok.data_ptr()), sp) for t in sets]
+    for i in range(args.warmup):
+        if L.tree_target_argmax(*call_args[i % R]):
+            raise RuntimeError("tree_target_argmax rejected its arguments")
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1 << 24)
+    start.record(stream)
+    for i in range(K):
+        evs[i][0].record(stream)
+        L.tree_target_argmax(*call_args[(args.warmup + i) % R])
+        evs[i][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    call_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    us = float(call_ms.mean() * 1e3)
+    byts = rows * V * es + rows * 4
+    roof = {"bound": "hbm", "achieved": byts / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "traffic": None, "traffic_detail": "not measured for this kernel",
+            "kernel": "tree_target_argmax", "avg_us": us,
+            "p10_us": float(np.percentile(call_ms, 10) * 1e3), "p90_us": float(np.percentile(call_ms, 90) * 1e3),
+            "alg_bytes": byts}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    line = {
+        "metric": "node target choices per second (tree_target_argmax)",
+        "value": rows / (us * 1e-6),
+        "unit": "nodes/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": start.elapsed_time(end) / K,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.argmax_dtype,
+        "data": "synthetic",
+        "config": {"workload": f"logits {rows} x {V} {args.argmax_dtype}", "seed": args.seed,
+                   "cold_cache_sets": R},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import tree_verify_oracle as O
+        xs = sets[0].float().cpu().numpy()
+        t0 = time.perf_counter()
+        n = 0
+        while n < rows and time.perf_counter() - t0 < args.cpu_budget:
+            O.target_argmax(xs[n:n + 16])
+            n = min(rows, n + 16)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": n / dt, "unit": "nodes/s", "cores": 1, "kind": "oracle",
+                                "sample": f"target_argmax on rows 0..{n - 1} of the same logits ({dt:.2f} s)"}
     print(json.dumps(line), flush=True)
     return 0
 

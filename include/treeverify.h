@@ -71,6 +71,7 @@ typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
 #define TV_MAX_DEPTH 64            /* levels per tree / accepted tokens   */
 #define TV_MAX_TOTAL_NODES 16777215 /* nodes per batch (24-bit error index) */
 #define TV_MAX_LEDGER 8192         /* ledger slots (depths x lanes) per request */
+#define TV_MAX_VOCAB 16777216      /* logits per row                              */
 
 /* device error codes (the top byte of the err word) */
 #define TV_DEVERR_BAD_PARENT 1  /* parent[v] not in [-1, v); index = global node v       */
@@ -243,6 +244,24 @@ tv_status tree_select_topb(const float *score, const int32_t *parent, const int3
                            int32_t batch, int32_t depth, int32_t lanes, int32_t budget, float beta,
                            int32_t *tree_parent, int32_t *tree_token, int32_t *n_real, int32_t *err,
                            void *stream);
+
+/*
+ * tree_target_argmax -- the target's greedy choice at every node.
+ *
+ * Defines: [TSD] "Verification and Acceptance Algorithms", greedy tree
+ * verification: the target prediction at a node is the argmax of the logits
+ * the verification pass produced there; these choices are the
+ * target_tokens (and root_target) of tree_accept_greedy.
+ * Readings: the lowest index wins a tie (-0 equals +0); a NaN ranks above
+ * every number, so a row holding NaN gives its first NaN.
+ *
+ * In:  logits [rows, vocab] in dtype (fp32 or bf16), row-major.
+ *      0 <= rows <= TV_MAX_TOTAL_NODES; 1 <= vocab <= TV_MAX_VOCAB.
+ * Out: token [rows] int32.
+ * No device-side errors.
+ */
+tv_status tree_target_argmax(const void *logits, int32_t rows, int32_t vocab, tv_dtype dtype,
+                             int32_t *token, void *stream);
 
 #ifdef __cplusplus
 }

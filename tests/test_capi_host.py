@@ -148,6 +148,7 @@ def test_binding_constants_match_header():
     assert defs["TV_MAX_NODES"] == BND.TV_MAX_NODES
     assert defs["TV_MAX_DEPTH"] == BND.TV_MAX_DEPTH
     assert defs["TV_MAX_LEDGER"] == BND.TV_MAX_LEDGER
+    assert defs["TV_MAX_VOCAB"] == BND.TV_MAX_VOCAB
     for name in ("BAD_PARENT", "TOO_DEEP", "BAD_REQUEST", "BAD_PATH", "BAD_LEDGER"):
         assert defs["TV_DEVERR_" + name] == getattr(BND, "DEVERR_" + name)
 
@@ -171,3 +172,16 @@ def test_select_host_checks(L):
     assert select(L, score=None) == NULL
     assert select(L, B=0, score=None, parent=None, token=None) == OK
     assert select(L, B=0, D=64, Ln=128, budget=1024) == OK   # largest sizes, empty batch
+
+
+def test_argmax_host_checks(L):
+    am = lambda logits=FAKE, rows=4, vocab=100, dt=1, tok=FAKE: L.tree_target_argmax(logits, rows, vocab, dt, tok, None)
+    assert am(rows=-1) == SHAPE
+    assert am(vocab=0) == SHAPE
+    assert am(vocab=16777217) == LIMIT
+    assert am(rows=16777216) == LIMIT
+    assert am(dt=7) == DTYPE
+    assert am(tok=None) == NULL
+    assert am(logits=None) == NULL
+    assert am(logits=FAKE_ODD) == ALIGN
+    assert am(rows=0, logits=None, tok=None) == OK

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG, "libtreeverify.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "treeverify.h")
 
 TV_F32, TV_BF16 = 0, 1
-TV_MAX_NODES, TV_MAX_DEPTH, TV_MAX_LEDGER = 1024, 64, 8192
+TV_MAX_NODES, TV_MAX_DEPTH, TV_MAX_LEDGER, TV_MAX_VOCAB = 1024, 64, 8192, 16777216
 DEVERR_BAD_PARENT, DEVERR_TOO_DEEP, DEVERR_BAD_REQUEST, DEVERR_BAD_PATH, DEVERR_BAD_LEDGER = 1, 2, 3, 4, 5
 
 
@@ -58,6 +58,8 @@ def lib() -> C.CDLL:
     L.kv_compact_path.restype = C.c_int
     L.tree_select_topb.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp]
     L.tree_select_topb.restype = C.c_int
+    L.tree_target_argmax.argtypes = [vp, i32, i32, C.c_int, vp, vp]
+    L.tree_target_argmax.restype = C.c_int
     _lib = L
     return L
 
@@ -238,3 +240,19 @@ def tree_select_topb(score, parent, token, budget: int, beta: float = 0.0, tree_
         _ptr(score), _ptr(parent), _ptr(token), B, D, L, budget, float(beta), _ptr(tree_parent),
         _ptr(tree_token), _ptr(n_real), _ptr(err), _stream(stream)))
     return tree_parent, tree_token, n_real, err
+
+
+def tree_target_argmax(logits, token=None, stream=None):
+    """logits [rows, vocab] (float32 or bfloat16) -> token int32 [rows]: the
+    lowest index of each row's maximum (NaN ranks highest)."""
+    import torch
+    if logits.dim() != 2:
+        raise ValueError("logits must be [rows, vocab]")
+    rows, vocab = logits.shape
+    code = _dtype_code(logits)
+    _need(logits, "logits")
+    token = torch.empty(rows, dtype=torch.int32, device=logits.device) if token is None else token
+    _need(token, "token", torch.int32, rows)
+    _check("tree_target_argmax", lib().tree_target_argmax(_ptr(logits), rows, vocab, code, _ptr(token),
+                                                          _stream(stream)))
+    return token

@@ -184,4 +184,15 @@ tv_status tree_select_topb(const float *score, const int32_t *parent, const int3
                                                 tree_parent, tree_token, n_real, err, (hipStream_t)stream));
 }
 
+tv_status tree_target_argmax(const void *logits, int32_t rows, int32_t vocab, tv_dtype dtype,
+                             int32_t *token, void *stream) {
+    if (rows < 0 || vocab < 1) return TV_ERR_SHAPE;
+    if (rows > TV_MAX_TOTAL_NODES || vocab > TV_MAX_VOCAB) return TV_ERR_LIMIT;
+    if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_DTYPE;
+    if (rows > 0 && (!logits || !token)) return TV_ERR_NULL;
+    if (!aligned(logits, 16)) return TV_ERR_ALIGN;
+    if (rows == 0) return TV_OK;
+    return launch_status(tv::launch_target_argmax(logits, rows, vocab, dtype, token, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -29,6 +29,9 @@ hipError_t launch_select_topb(const float *score, const int32_t *parent, const i
                               int depth, int lanes, int budget, float beta, int32_t *tree_parent,
                               int32_t *tree_token, int32_t *n_real, int32_t *err, hipStream_t stream);
 
+hipError_t launch_target_argmax(const void *logits, int rows, int vocab, tv_dtype dtype, int32_t *token,
+                                hipStream_t stream);
+
 // Problem description shared by the attention kernels.
 struct AttnArgs {
     const void *q, *k, *v;
