@@ -310,3 +310,70 @@ def target_argmax(logits) -> np.ndarray:
     if x.shape[1] == 0:
         raise ValueError("vocab must be at least 1")
     return np.argmax(x, axis=1).astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# O-rope: rotary embedding at tree position ids ([TSD] "Tree Positional
+# IDs": PosID(v) = PosID(root) + depth(v) is what RoPE sees)
+# ---------------------------------------------------------------------------
+
+def rope_rotate(x, pos, base: float) -> np.ndarray:
+    """Rotate the last axis of x [..., d] by position pos (broadcast over the
+    leading axes).  Reading (the pages name RoPE without its formula): the
+    rotate-half layout, channel i paired with channel i + d/2, angle
+    pos * base**(-2i/d) for i < d/2; float64 throughout."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    h = d // 2
+    inv = base ** (-2.0 * np.arange(h, dtype=np.float64) / d)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[..., :h], x[..., h:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def tree_rope(q, k, pos, cu_nodes, kv_start, prefix_len, base: float):
+    """q [T, Hq, d] rotated by pos[t]; the tree's K rows (cache row
+    kv_start[b] + P_b + j for node j of request b) rotated by the same
+    position; every other cache row unchanged.  Returns (q', k')."""
+    q2 = rope_rotate(q, np.asarray(pos)[:, None], base)
+    k2 = np.asarray(k, dtype=np.float64).copy()
+    cu = np.asarray(cu_nodes)
+    for b in range(cu.shape[0] - 1):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        r0 = int(kv_start[b]) + int(prefix_len[b])
+        for j in range(hi - lo):
+            k2[r0 + j] = rope_rotate(k2[r0 + j], np.full(k2.shape[1], pos[lo + j]), base)
+    return q2, k2
+
+
+# ---------------------------------------------------------------------------
+# O-rollback by token table ([TSD] "KV Cache Rollback": unaccepted nodes are
+# discarded by "page table updates" in paged caches)
+# ---------------------------------------------------------------------------
+
+def token_table_rollback(req_to_token, tree_slots, cu_nodes, prefix_len, accept_len, accept_idx):
+    """Paged cache with one token per page: req_to_token[b, p] is the slot of
+    position p of request b, and node j of request b was written to slot
+    tree_slots[lo + j].  After acceptance, positions P_b .. P_b + L_b - 1
+    point at the accepted nodes' slots in path order; no K/V moves.  Returns
+    (table', new_len [B], freed [T] (each request's unaccepted slots in node
+    order, from its own offset lo; the rest of its region is -1), n_freed [B])."""
+    tab = np.array(req_to_token, dtype=np.int32, copy=True)
+    cu = np.asarray(cu_nodes)
+    B = cu.shape[0] - 1
+    T = int(cu[-1]) if B > 0 else 0
+    new_len = np.zeros(B, np.int32)
+    freed = np.full(T, -1, np.int32)
+    n_freed = np.zeros(B, np.int32)
+    for b in range(B):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        P, L = int(prefix_len[b]), int(accept_len[b])
+        path = [int(x) for x in accept_idx[b, :L]]
+        for j, node in enumerate(path):
+            tab[b, P + j] = tree_slots[lo + node]
+        new_len[b] = P + L
+        rest = [tree_slots[lo + i] for i in range(hi - lo) if i not in set(path)]
+        freed[lo:lo + len(rest)] = rest
+        n_freed[b] = len(rest)
+    return tab, new_len, freed, n_freed
