@@ -263,6 +263,63 @@ tv_status tree_select_topb(const float *score, const int32_t *parent, const int3
 tv_status tree_target_argmax(const void *logits, int32_t rows, int32_t vocab, tv_dtype dtype,
                              int32_t *token, void *stream);
 
+/*
+ * tree_rope_apply -- rotary position embedding at the tree's position ids.
+ *
+ * Defines: [TSD] "The Tree Attention Mechanism", part 3 "Tree Positional IDs":
+ * the position a node's RoPE sees is PosID(root) + depth, i.e. pos_ids from
+ * tree_mask_build, not the node's index in the flattened tree.
+ * Reading (the pages name RoPE without its formula): the rotate-half layout,
+ * channel i paired with channel i + d/2, rotated by the angle
+ * pos * base^(-2i/d) for i < d/2 (base = the model's rope theta, 1e6 for
+ * Qwen3).  Angles, sines, cosines and the rotation are computed in double;
+ * each element is rounded once to dtype (bf16 through float: within one
+ * bf16 ulp of the exact value).
+ *
+ * In/out: q [T, hq, head_dim] (every node, every query head) and the tree's
+ *      K rows of k_cache [kv_rows, hkv, head_dim] (row kv_start[b] + P_b + j
+ *      for node j of request b), rotated in place.  Prefix rows are not
+ *      touched.  16-byte aligned.
+ * In:  pos_ids [T] int32; cu_nodes [B+1]; kv_start, prefix_len [B].
+ *      head_dim in {64, 128}; base > 0 and finite.
+ * err: BAD_REQUEST (a node outside every request, or a tree row outside the
+ *      cache); that row is not rotated.
+ */
+tv_status tree_rope_apply(void *q, void *k_cache, const int32_t *pos_ids, const int32_t *cu_nodes,
+                          const int32_t *kv_start, const int32_t *prefix_len, int32_t batch,
+                          int32_t total_nodes, int64_t kv_rows, int32_t hq, int32_t hkv, int32_t head_dim,
+                          float base, tv_dtype dtype, int32_t *err, void *stream);
+
+/*
+ * kv_rollback_token_table -- discard the unaccepted nodes of a paged cache by
+ * updating its token table; no K/V moves.
+ *
+ * Defines: [TSD] "KV Cache Rollback": unaccepted tree nodes are discarded "by
+ * page table updates in PagedAttention systems".
+ * Reading: pages of one token (a token table as in token-level KV pools):
+ * req_to_token[b * table_stride + p] is the cache slot of position p of
+ * request b, and node j of request b was written to slot tree_slots[lo + j]
+ * (lo = cu_nodes[b]).  Afterwards positions P_b .. P_b + L_b - 1 hold the
+ * accepted nodes' slots in path order; gathering K/V through the table then
+ * gives what kv_compact_path leaves in a contiguous cache.
+ *
+ * In/out: req_to_token [B, table_stride] int32 (only positions
+ *      P_b .. P_b + L_b - 1 are written).
+ * In:  tree_slots [T]; cu_nodes [B+1]; prefix_len, accept_len [B];
+ *      accept_idx [B, max_depth] from tree_accept_greedy.
+ * Out: new_len [B] = P_b + L_b; freed_slots [T]: from offset cu_nodes[b],
+ *      the slots of request b's unaccepted nodes in node order, then -1 up
+ *      to N_b; n_freed [B] = N_b - L_b.
+ * err: BAD_REQUEST (cu_nodes outside [0, T] or decreasing, L_b outside
+ *      [0, min(max_depth, N_b)], or P_b + L_b > table_stride); BAD_PATH (an
+ *      accept_idx entry outside [0, N_b)).  Such a request is untouched.
+ */
+tv_status kv_rollback_token_table(int32_t *req_to_token, int64_t table_stride, const int32_t *tree_slots,
+                                  const int32_t *cu_nodes, const int32_t *prefix_len,
+                                  const int32_t *accept_len, const int32_t *accept_idx, int32_t batch,
+                                  int32_t total_nodes, int32_t max_depth, int32_t *new_len,
+                                  int32_t *freed_slots, int32_t *n_freed, int32_t *err, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -185,3 +185,25 @@ def test_argmax_host_checks(L):
     assert am(logits=None) == NULL
     assert am(logits=FAKE_ODD) == ALIGN
     assert am(rows=0, logits=None, tok=None) == OK
+
+
+def test_rope_and_rollback_host_checks(L):
+    rope = lambda q=FAKE, k=FAKE, pos=FAKE, cu=FAKE, ks=FAKE, P=FAKE, B=1, T=16, rows=100, hq=8, hkv=2, d=128, \
+        base=1e6, dt=1: L.tree_rope_apply(q, k, pos, cu, ks, P, B, T, rows, hq, hkv, d, base, dt, None, None)
+    assert rope(hq=0) == SHAPE
+    assert rope(rows=-1) == SHAPE
+    assert rope(base=0.0) == SHAPE
+    assert rope(base=float("nan")) == SHAPE
+    assert rope(d=96) == DTYPE
+    assert rope(dt=5) == DTYPE
+    assert rope(pos=None) == NULL
+    assert rope(q=FAKE_ODD) == ALIGN
+    assert rope(B=0, T=0, q=None, k=None, pos=None) == OK
+    rb = lambda tab=FAKE, stride=64, slots=FAKE, cu=FAKE, P=FAKE, al=FAKE, ai=FAKE, B=1, T=16, D=16, nl=FAKE, \
+        fr=FAKE, nf=FAKE: L.kv_rollback_token_table(tab, stride, slots, cu, P, al, ai, B, T, D, nl, fr, nf, None, None)
+    assert rb(D=0) == SHAPE
+    assert rb(stride=0) == SHAPE
+    assert rb(D=65) == LIMIT
+    assert rb(tab=None) == NULL
+    assert rb(fr=None) == NULL
+    assert rb(B=0) == OK

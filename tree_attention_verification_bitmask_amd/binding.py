@@ -60,6 +60,10 @@ def lib() -> C.CDLL:
     L.tree_select_topb.restype = C.c_int
     L.tree_target_argmax.argtypes = [vp, i32, i32, C.c_int, vp, vp]
     L.tree_target_argmax.restype = C.c_int
+    L.tree_rope_apply.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32, C.c_int, vp, vp]
+    L.tree_rope_apply.restype = C.c_int
+    L.kv_rollback_token_table.argtypes = [vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.kv_rollback_token_table.restype = C.c_int
     _lib = L
     return L
 
@@ -256,3 +260,49 @@ def tree_target_argmax(logits, token=None, stream=None):
     _check("tree_target_argmax", lib().tree_target_argmax(_ptr(logits), rows, vocab, code, _ptr(token),
                                                           _stream(stream)))
     return token
+
+
+def tree_rope_apply(q, k_cache, pos_ids, cu_nodes, kv_start, prefix_len, base: float = 1.0e6, err=None,
+                    stream=None):
+    """Rotates q [T, hq, d] and the tree's K rows of k_cache [rows, hkv, d] in
+    place by pos_ids [T]; -> err."""
+    import torch
+    T, hq, d = q.shape
+    rows, hkv, d2 = k_cache.shape
+    if d2 != d or k_cache.dtype != q.dtype:
+        raise ValueError("q and k_cache disagree in head_dim or dtype")
+    code = _dtype_code(q)
+    B = cu_nodes.numel() - 1
+    _need(q, "q")
+    _need(k_cache, "k_cache")
+    for t, n in ((cu_nodes, "cu_nodes"), (kv_start, "kv_start"), (prefix_len, "prefix_len")):
+        _need(t, n, torch.int32)
+    _need(pos_ids, "pos_ids", torch.int32, T)
+    err = torch.zeros(1, dtype=torch.int32, device=q.device) if err is None else err
+    _check("tree_rope_apply", lib().tree_rope_apply(
+        _ptr(q), _ptr(k_cache), _ptr(pos_ids), _ptr(cu_nodes), _ptr(kv_start), _ptr(prefix_len), B, T, rows,
+        hq, hkv, d, float(base), code, _ptr(err), _stream(stream)))
+    return err
+
+
+def kv_rollback_token_table(req_to_token, tree_slots, cu_nodes, prefix_len, accept_len, accept_idx,
+                            max_depth: int, total_nodes: int, new_len=None, freed_slots=None, n_freed=None,
+                            err=None, stream=None):
+    """Updates req_to_token [B, stride] in place; -> (new_len [B],
+    freed_slots [T], n_freed [B], err)."""
+    import torch
+    B, stride = req_to_token.shape
+    dev = req_to_token.device
+    for t, n in ((req_to_token, "req_to_token"), (cu_nodes, "cu_nodes"), (prefix_len, "prefix_len"),
+                 (accept_len, "accept_len"), (accept_idx, "accept_idx"), (tree_slots, "tree_slots")):
+        _need(t, n, torch.int32)
+    new_len = torch.empty(B, dtype=torch.int32, device=dev) if new_len is None else new_len
+    freed_slots = (torch.empty(max(total_nodes, 1), dtype=torch.int32, device=dev)
+                   if freed_slots is None else freed_slots)
+    n_freed = torch.empty(B, dtype=torch.int32, device=dev) if n_freed is None else n_freed
+    err = torch.zeros(1, dtype=torch.int32, device=dev) if err is None else err
+    _check("kv_rollback_token_table", lib().kv_rollback_token_table(
+        _ptr(req_to_token), stride, _ptr(tree_slots), _ptr(cu_nodes), _ptr(prefix_len), _ptr(accept_len),
+        _ptr(accept_idx), B, total_nodes, max_depth, _ptr(new_len), _ptr(freed_slots), _ptr(n_freed), _ptr(err),
+        _stream(stream)))
+    return new_len, freed_slots, n_freed, err

@@ -195,4 +195,42 @@ tv_status tree_target_argmax(const void *logits, int32_t rows, int32_t vocab, tv
     return launch_status(tv::launch_target_argmax(logits, rows, vocab, dtype, token, (hipStream_t)stream));
 }
 
+tv_status tree_rope_apply(void *q, void *k_cache, const int32_t *pos_ids, const int32_t *cu_nodes,
+                          const int32_t *kv_start, const int32_t *prefix_len, int32_t batch,
+                          int32_t total_nodes, int64_t kv_rows, int32_t hq, int32_t hkv, int32_t head_dim,
+                          float base, tv_dtype dtype, int32_t *err, void *stream) {
+    tv_status st = check_batch(batch, total_nodes);
+    if (st != TV_OK) return st;
+    if (hq < 1 || hkv < 1 || kv_rows < 0) return TV_ERR_SHAPE;
+    if (hq > 65535 || hkv > 65535) return TV_ERR_LIMIT;
+    if (!(base > 0.f) || base > 3.0e38f) return TV_ERR_SHAPE;
+    if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_DTYPE;
+    if (head_dim != 64 && head_dim != 128) return TV_ERR_DTYPE;
+    if (!cu_nodes || !kv_start || !prefix_len) return TV_ERR_NULL;
+    if (total_nodes > 0 && (!q || !k_cache || !pos_ids)) return TV_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k_cache, 16)) return TV_ERR_ALIGN;
+    if (batch == 0 || total_nodes == 0) return TV_OK;
+    return launch_status(tv::launch_tree_rope(q, k_cache, pos_ids, cu_nodes, kv_start, prefix_len, batch,
+                                              total_nodes, kv_rows, hq, hkv, head_dim, base, dtype, err,
+                                              (hipStream_t)stream));
+}
+
+tv_status kv_rollback_token_table(int32_t *req_to_token, int64_t table_stride, const int32_t *tree_slots,
+                                  const int32_t *cu_nodes, const int32_t *prefix_len,
+                                  const int32_t *accept_len, const int32_t *accept_idx, int32_t batch,
+                                  int32_t total_nodes, int32_t max_depth, int32_t *new_len,
+                                  int32_t *freed_slots, int32_t *n_freed, int32_t *err, void *stream) {
+    tv_status st = check_batch(batch, total_nodes);
+    if (st != TV_OK) return st;
+    if (max_depth < 1 || table_stride < 1) return TV_ERR_SHAPE;
+    if (max_depth > TV_MAX_DEPTH) return TV_ERR_LIMIT;
+    if (!req_to_token || !cu_nodes || !prefix_len || !accept_len || !accept_idx || !new_len || !n_freed)
+        return TV_ERR_NULL;
+    if (total_nodes > 0 && (!tree_slots || !freed_slots)) return TV_ERR_NULL;
+    if (batch == 0) return TV_OK;
+    return launch_status(tv::launch_rollback_table(req_to_token, table_stride, tree_slots, cu_nodes, prefix_len,
+                                                   accept_len, accept_idx, batch, total_nodes, max_depth, new_len,
+                                                   freed_slots, n_freed, err, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -32,6 +32,14 @@ hipError_t launch_select_topb(const float *score, const int32_t *parent, const i
 hipError_t launch_target_argmax(const void *logits, int rows, int vocab, tv_dtype dtype, int32_t *token,
                                 hipStream_t stream);
 
+hipError_t launch_tree_rope(void *q, void *k, const int32_t *pos, const int32_t *cu_nodes, const int32_t *kv_start,
+                            const int32_t *prefix_len, int batch, int total_nodes, int64_t kv_rows, int hq, int hkv,
+                            int head_dim, float base, tv_dtype dtype, int32_t *err, hipStream_t stream);
+hipError_t launch_rollback_table(int32_t *table, int64_t stride, const int32_t *tree_slots, const int32_t *cu_nodes,
+                                 const int32_t *prefix_len, const int32_t *accept_len, const int32_t *accept_idx,
+                                 int batch, int total_nodes, int max_depth, int32_t *new_len, int32_t *freed,
+                                 int32_t *n_freed, int32_t *err, hipStream_t stream);
+
 // Problem description shared by the attention kernels.
 struct AttnArgs {
     const void *q, *k, *v;
