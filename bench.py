@@ -242,6 +242,8 @@ def main(argv=None):
     ap.add_argument("--argmax-rows", type=int, default=129)
     ap.add_argument("--argmax-vocab", type=int, default=151936)
     ap.add_argument("--argmax-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--rope", action="store_true",
+                    help="time tree_rope_apply and kv_rollback_token_table on the workload instead of the pass")
     args = ap.parse_args(argv)
     if args.ingest_traffic:
         print(ingest_traffic(args.workload, args.ingest_traffic[0], args.ingest_traffic[1],
@@ -266,6 +268,8 @@ def main(argv=None):
         return bench_select(args, torch, BND, L, dev)
     if args.argmax:
         return bench_argmax(args, torch, BND, L, dev)
+    if args.rope:
+        return bench_rope(args, torch, BND, L, dev)
 
     if args.calib_copy_mib > 0:
         n_el = args.calib_copy_mib << 18  # float32 elements
@@ -567,6 +571,73 @@ def bench_argmax(args, torch, BND, L, dev):
         dt = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": n / dt, "unit": "nodes/s", "cores": 1, "kind": "oracle",
                                 "sample": f"target_argmax on rows 0..{n - 1} of the same logits ({dt:.2f} s)"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_rope(args, torch, BND, L, dev):
+    """tree_rope_apply (Q and the tree's K rows of the workload, rotated at the
+    tree position ids) and kv_rollback_token_table (accepted path of the
+    workload, one token per page), each timed with HIP events per call.  The
+    rotation is applied repeatedly to the same buffers (timing only)."""
+    wl = W.make_workload(args.workload, seed=args.seed, force_path=True)
+    fdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    code = BND.TV_BF16 if wl.dtype == "bf16" else BND.TV_F32
+    es = 2 if wl.dtype == "bf16" else 4
+    T, B = wl.total_nodes, wl.batch
+    i32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(dev)  # noqa: E731
+    parent, cu, P, ks = i32(wl.parent), i32(wl.cu_nodes), i32(wl.prefix_len), i32(wl.kv_start)
+    q = torch.from_numpy(wl.q).to(dev).to(fdt).contiguous()
+    k = torch.from_numpy(wl.k).to(dev).to(fdt).contiguous()
+    anc, lev, pos, err = BND.tree_mask_build(parent, cu, P, wl.max_nodes, wl.max_depth)
+    alen, aidx, _, _ = BND.tree_accept_greedy(parent, i32(wl.draft), i32(wl.target), i32(wl.root_target), cu,
+                                              wl.max_depth)
+    stride = int((wl.prefix_len + np.diff(wl.cu_nodes)).max())
+    table = torch.zeros((B, stride), dtype=torch.int32, device=dev)
+    slots = torch.arange(T, dtype=torch.int32, device=dev)
+    nl = torch.empty(B, dtype=torch.int32, device=dev)
+    fr = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    nf = torch.empty(B, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = C_void(stream.cuda_stream)
+    P_ = lambda t: C_void(t.data_ptr())  # noqa: E731
+    rope_args = (P_(q), P_(k), P_(pos), P_(cu), P_(ks), P_(P), B, T, k.shape[0], wl.hq, wl.hkv, wl.d, 1.0e6, code,
+                 P_(err), sp)
+    rb_args = (P_(table), stride, P_(slots), P_(cu), P_(P), P_(alen), P_(aidx), B, T, wl.max_depth, P_(nl), P_(fr),
+               P_(nf), P_(err), sp)
+    out = {}
+    for name, fn, a in (("tree_rope_apply", L.tree_rope_apply, rope_args),
+                        ("kv_rollback_token_table", L.kv_rollback_token_table, rb_args)):
+        for _ in range(args.warmup):
+            if fn(*a):
+                raise RuntimeError(f"{name} rejected its arguments")
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda._sleep(1 << 22)
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn(*a)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = np.array([a_.elapsed_time(b_) for a_, b_ in evs])
+        out[name] = float(ms.mean() * 1e3)
+    if int(err.item()) != 0:
+        raise RuntimeError(f"device error word {int(err.item()):#x}")
+    rope_bytes = 2 * T * (wl.hq + wl.hkv) * wl.d * es + T * 4
+    us = out["tree_rope_apply"]
+    roof = {"bound": "hbm", "achieved": rope_bytes / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "traffic": None, "traffic_detail": "not measured for this kernel", "kernel": "tree_rope_apply",
+            "avg_us": us, "alg_bytes": rope_bytes, "rollback_avg_us": out["kv_rollback_token_table"]}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    line = {
+        "metric": "tree nodes rotated per second (tree_rope_apply)",
+        "value": T / (us * 1e-6), "unit": "nodes/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": us * 1e-3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {W.CONFIGS[wl.name]['desc']}", "seed": wl.seed},
+        "roofline": roof,
+    }
     print(json.dumps(line), flush=True)
     return 0
 
