@@ -475,3 +475,61 @@ def frontier_shaped_ledger(rng: np.random.Generator, batch: int, depth: int, wid
             lane_slot = order[:width].astype(np.int32)
             lane_score = score[b, t, lane_slot]
     return score, parent, token
+
+
+# ---------------------------------------------------------------------------
+# Gated-DeltaNet layer inputs for tree-aware recurrent verification.  The
+# layer shape is a stand-in (the page names a hybrid Gated-DeltaNet target but
+# prints no layer sizes): 16 query/key heads and 32 value heads of 128
+# channels, a width-4 short convolution over the 2*16*128 + 32*128 = 8192
+# mixed channels.
+# ---------------------------------------------------------------------------
+
+GDN_LAYER = dict(hk=16, hv=32, dk=128, dv=128, conv_k=4)
+
+
+@dataclass
+class GdnInputs:
+    parent: np.ndarray       # int32 [T], per-request local parents
+    cu_nodes: np.ndarray     # int32 [B+1]
+    x: np.ndarray            # float32 [T, C], bf16-representable: the layer's mixed inputs
+    conv_state: np.ndarray   # float32 [B, K-1, C], bf16-representable, oldest first
+    conv_w: np.ndarray       # float32 [C, K], bf16-representable
+    q: np.ndarray            # float32 [T, Hk, dk], bf16-representable
+    k: np.ndarray            # float32 [T, Hk, dk]
+    v: np.ndarray            # float32 [T, Hv, dv]
+    g: np.ndarray            # float32 [T, Hv], log decay (<= 0)
+    beta: np.ndarray         # float32 [T, Hv], write strength in (0, 1)
+    state: np.ndarray        # float32 [B, Hv, dv, dk], the committed recurrent state
+    max_depth: int
+
+
+def gdn_inputs(rng: np.random.Generator, parents: list, hk: int = 16, hv: int = 32, dk: int = 128,
+               dv: int = 128, conv_k: int = 4, state_std: float = 0.1) -> GdnInputs:
+    """Seeded synthetic inputs for one Gated-DeltaNet layer over a batch of
+    draft trees (one parent array per request).  x, conv_state, q, k, v ~
+    N(0, 1) and the conv weights ~ N(0, 1/4), all rounded to bf16; the log
+    decay g ~ -U(0.01, 0.5) and beta ~ U(0.05, 0.95); the committed state ~
+    N(0, state_std) in float32."""
+    B = len(parents)
+    sizes = np.array([len(p) for p in parents], dtype=np.int64)
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(sizes)
+    T = int(cu[-1])
+    C = 2 * hk * dk + hv * dv
+    depth = max([int(_depths(np.asarray(p)).max()) if len(p) else 1 for p in parents] + [1])
+    nrm = lambda *s: round_to_bf16(rng.standard_normal(size=s, dtype=np.float32))
+    return GdnInputs(
+        parent=np.concatenate([np.asarray(p, np.int32) for p in parents]) if T else np.zeros(0, np.int32),
+        cu_nodes=cu,
+        x=nrm(T, C),
+        conv_state=nrm(B, conv_k - 1, C),
+        conv_w=round_to_bf16(rng.standard_normal(size=(C, conv_k), dtype=np.float32) * np.float32(0.5)),
+        q=nrm(T, hk, dk),
+        k=nrm(T, hk, dk),
+        v=nrm(T, hv, dv),
+        g=-rng.uniform(0.01, 0.5, size=(T, hv)).astype(np.float32),
+        beta=rng.uniform(0.05, 0.95, size=(T, hv)).astype(np.float32),
+        state=(rng.standard_normal(size=(B, hv, dv, dk), dtype=np.float32) * np.float32(state_std)),
+        max_depth=depth,
+    )
