@@ -72,6 +72,9 @@ typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
 #define TV_MAX_TOTAL_NODES 16777215 /* nodes per batch (24-bit error index) */
 #define TV_MAX_LEDGER 8192         /* ledger slots (depths x lanes) per request */
 #define TV_MAX_VOCAB 16777216      /* logits per row                              */
+#define TV_GDN_HEAD_DIM 128        /* Gated-DeltaNet q/k and v channels per head   */
+#define TV_GDN_MAX_NODES 256       /* nodes per request in tree_gdn_verify         */
+#define TV_GDN_MAX_TABLE 4096      /* N_b x max_depth per request in tree_gdn_verify */
 
 /* device error codes (the top byte of the err word) */
 #define TV_DEVERR_BAD_PARENT 1  /* parent[v] not in [-1, v); index = global node v       */
@@ -79,6 +82,7 @@ typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
 #define TV_DEVERR_BAD_REQUEST 3 /* request sizes disagree with the host sizes; index = b */
 #define TV_DEVERR_BAD_PATH 4    /* accepted path entry out of range; index = b           */
 #define TV_DEVERR_BAD_LEDGER 5  /* chosen slot whose parent is unusable; index = b       */
+#define TV_DEVERR_LIMIT 6       /* a request above a per-request limit; index = b        */
 
 /* Human-readable name of a tv_status value (static string). */
 const char *tv_status_string(int status);
@@ -319,6 +323,93 @@ tv_status kv_rollback_token_table(int32_t *req_to_token, int64_t table_stride, c
                                   const int32_t *accept_len, const int32_t *accept_idx, int32_t batch,
                                   int32_t total_nodes, int32_t max_depth, int32_t *new_len,
                                   int32_t *freed_slots, int32_t *n_freed, int32_t *err, void *stream);
+
+/*
+ * Tree-aware recurrent verification for a Gated-DeltaNet layer: three calls.
+ *
+ * Defines: [DT] section 4.5.4, "Tree-aware recurrent verification": in a
+ * recurrent layer every tree node needs the state of its own root path and a
+ * dense convolution window made of its own ancestors, and only the accepted
+ * path's recurrent state is committed (a chain recurrence over the flattened
+ * tree lets rejected siblings write into the state later nodes read).
+ * Readings (the page gives no formulas): the gated delta rule with
+ * L2-normalised queries and keys,
+ *   k^ = k / sqrt(|k|^2 + 1e-6),  q^ = scale * q / sqrt(|q|^2 + 1e-6)
+ *   S_t = exp(g_t) S_p (I - beta_t k^_t k^_t^T) + beta_t v_t k^_t^T,  o_t = S_t q^_t
+ * (p = the node's parent; the request's committed state S0 for a root
+ * child; with l2norm = 0, k^ = k and q^ = scale * q), value head h reading
+ * query/key head h / (hv / hk), S of shape [dv, dk] per value head; and a
+ * depthwise causal convolution of width conv_k with SiLU whose window for a
+ * node is the committed conv state (the conv_k - 1 most recent inputs, oldest
+ * first) followed by the inputs along the node's root path.
+ * Element types: the layer's activations (x, conv state, taps, y, q, k, v) are
+ * bf16; g, beta, the state and the outputs are float32.  head_dim (dk = dv)
+ * must be TV_GDN_HEAD_DIM.
+ */
+
+/*
+ * tree_gdn_conv -- the short convolution over each node's ancestor window.
+ *
+ * In:  x [T, channels] bf16 (the layer's mixed q/k/v inputs per node);
+ *      conv_state [B, conv_k - 1, channels] bf16; weight [channels, conv_k]
+ *      bf16 (weight[c][conv_k - 1] multiplies the node's own input); parent
+ *      [T] (request-local, parent[i] < i); cu_nodes [B+1].  conv_k in
+ *      {2, 3, 4}; channels a positive multiple of 8; x, conv_state, weight, y
+ *      16-byte aligned.
+ * Out: y [T, channels] bf16 = SiLU(sum_i weight[c][i] window[i][c]), computed
+ *      in float32 and rounded once.
+ * err: BAD_REQUEST (a node outside every request); BAD_PARENT (a parent read
+ *      on a window outside [-1, i); the walk stops there as at a root).
+ */
+tv_status tree_gdn_conv(const void *x, const void *conv_state, const void *weight, const int32_t *parent,
+                        const int32_t *cu_nodes, int32_t batch, int32_t total_nodes, int32_t channels,
+                        int32_t conv_k, void *y, int32_t *err, void *stream);
+
+/*
+ * tree_gdn_verify -- every node's Gated-DeltaNet output, each node seeing the
+ * recurrence over its own root path only.
+ *
+ * In:  q [T, hk, 128], k [T, hk, 128], v [T, hv, 128] bf16 with a common row
+ *      stride of row_stride elements (q, k and v may be views into the
+ *      output of tree_gdn_conv); row_stride a multiple of 8 and q, k, v
+ *      16-byte aligned.  g [T, hv] (log decay), beta [T, hv] float32; state
+ *      [B, hv, 128, 128] float32 (S0 of each request, row i = value
+ *      channel), 16-byte aligned, not modified; parent [T]; cu_nodes [B+1].
+ *      1 <= max_depth <= TV_MAX_DEPTH (levels of the deepest node);
+ *      hv % hk == 0; scale finite; l2norm 0 or 1.
+ * Out: out [T, hv, 128] float32.
+ * Limits per request (device-checked): N_b <= TV_GDN_MAX_NODES and
+ *      N_b * max_depth <= TV_GDN_MAX_TABLE, else LIMIT.
+ * Arithmetic: dot products of bf16 rows on the matrix cores with float32
+ *      accumulation; S0 enters those products as a bf16 pair hi + lo (about
+ *      16 significant bits); the rest in float32.
+ * err: BAD_REQUEST, LIMIT, BAD_PARENT, TOO_DEEP (level > max_depth).
+ */
+tv_status tree_gdn_verify(const void *q, const void *k, const void *v, int64_t row_stride, const float *g,
+                          const float *beta, const float *state, const int32_t *parent, const int32_t *cu_nodes,
+                          int32_t batch, int32_t total_nodes, int32_t max_depth, int32_t hk, int32_t hv,
+                          int32_t head_dim, float scale, int32_t l2norm, float *out, int32_t *err, void *stream);
+
+/*
+ * tree_gdn_commit -- keep only the accepted path's recurrent state.
+ *
+ * In/out: state [B, hv, 128, 128] float32: S0 advanced by the accepted
+ *      tokens in path order, one step at a time in float32; conv_state
+ *      [B, conv_k - 1, channels] bf16: the last conv_k - 1 entries of
+ *      (old conv state, x of the accepted nodes).  A request with
+ *      accept_len 0 is untouched.
+ * In:  x [T, channels] bf16 (the inputs tree_gdn_conv read); k, v,
+ *      row_stride, g, beta, hk, hv, head_dim, l2norm as in tree_gdn_verify;
+ *      cu_nodes [B+1]; accept_len [B], accept_idx [B, max_depth] from
+ *      tree_accept_greedy; conv_k, channels as in tree_gdn_conv.
+ * err: BAD_REQUEST (L_b outside [0, min(max_depth, N_b)]), BAD_PATH (an
+ *      accept_idx entry outside [0, N_b)); such a request is untouched.
+ */
+tv_status tree_gdn_commit(float *state, void *conv_state, const void *x, const void *k, const void *v,
+                          int64_t row_stride, const float *g, const float *beta, const int32_t *cu_nodes,
+                          const int32_t *accept_len, const int32_t *accept_idx, int32_t batch, int32_t total_nodes,
+                          int32_t max_depth, int32_t hk, int32_t hv, int32_t head_dim, int32_t channels,
+                          int32_t conv_k, int32_t l2norm, int32_t *err, void *stream);
 
 #ifdef __cplusplus
 }

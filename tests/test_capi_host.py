@@ -149,8 +149,10 @@ def test_binding_constants_match_header():
     assert defs["TV_MAX_DEPTH"] == BND.TV_MAX_DEPTH
     assert defs["TV_MAX_LEDGER"] == BND.TV_MAX_LEDGER
     assert defs["TV_MAX_VOCAB"] == BND.TV_MAX_VOCAB
-    for name in ("BAD_PARENT", "TOO_DEEP", "BAD_REQUEST", "BAD_PATH", "BAD_LEDGER"):
+    for name in ("BAD_PARENT", "TOO_DEEP", "BAD_REQUEST", "BAD_PATH", "BAD_LEDGER", "LIMIT"):
         assert defs["TV_DEVERR_" + name] == getattr(BND, "DEVERR_" + name)
+    for name in ("TV_GDN_HEAD_DIM", "TV_GDN_MAX_NODES", "TV_GDN_MAX_TABLE"):
+        assert defs[name] == getattr(BND, name)
 
 
 def select(L, score=FAKE, parent=FAKE, token=FAKE, B=1, D=4, Ln=8, budget=16, beta=0.0, tp=FAKE,
@@ -207,3 +209,42 @@ def test_rope_and_rollback_host_checks(L):
     assert rb(tab=None) == NULL
     assert rb(fr=None) == NULL
     assert rb(B=0) == OK
+
+
+def test_gdn_host_checks(L):
+    conv = lambda x=FAKE, cs=FAKE, w=FAKE, par=FAKE, cu=FAKE, B=1, T=16, Cc=8192, K=4, y=FAKE: \
+        L.tree_gdn_conv(x, cs, w, par, cu, B, T, Cc, K, y, None, None)
+    assert conv(Cc=12) == SHAPE
+    assert conv(Cc=0) == SHAPE
+    assert conv(K=1) == SHAPE
+    assert conv(K=5) == SHAPE
+    assert conv(B=-1) == SHAPE
+    assert conv(y=None) == NULL
+    assert conv(w=FAKE_ODD) == ALIGN
+    assert conv(T=0, x=None, cs=None, w=None, par=None, y=None) == OK
+    ver = lambda q=FAKE, k=FAKE, v=FAKE, rs=8192, g=FAKE, be=FAKE, st=FAKE, par=FAKE, cu=FAKE, B=1, T=64, D=16, \
+        hk=16, hv=32, d=128, scale=0.088, l2=1, out=FAKE: \
+        L.tree_gdn_verify(q, k, v, rs, g, be, st, par, cu, B, T, D, hk, hv, d, scale, l2, out, None, None)
+    assert ver(hv=24) == SHAPE                     # hv % hk != 0
+    assert ver(hk=0) == SHAPE
+    assert ver(D=0) == SHAPE
+    assert ver(D=65) == LIMIT
+    assert ver(d=64) == DTYPE
+    assert ver(rs=8190) == ALIGN
+    assert ver(q=FAKE_ODD) == ALIGN
+    assert ver(st=FAKE_ODD) == ALIGN
+    assert ver(scale=float("nan")) == SHAPE
+    assert ver(l2=2) == SHAPE
+    assert ver(out=None) == NULL
+    assert ver(B=0, T=0, q=None, k=None, v=None, g=None, be=None, st=None, par=None, out=None) == OK
+    com = lambda st=FAKE, cs=FAKE, x=FAKE, k=FAKE, v=FAKE, rs=8192, g=FAKE, be=FAKE, cu=FAKE, al=FAKE, ai=FAKE, \
+        B=1, T=64, D=16, hk=16, hv=32, d=128, Cc=8192, K=4, l2=1: \
+        L.tree_gdn_commit(st, cs, x, k, v, rs, g, be, cu, al, ai, B, T, D, hk, hv, d, Cc, K, l2, None, None)
+    assert com(st=None) == NULL
+    assert com(cs=None) == NULL
+    assert com(K=5) == SHAPE
+    assert com(hv=20) == SHAPE
+    assert com(d=256) == DTYPE
+    assert com(D=65) == LIMIT
+    assert com(cs=FAKE_ODD) == ALIGN
+    assert com(B=0) == OK

@@ -19,6 +19,8 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "treeverify.h")
 TV_F32, TV_BF16 = 0, 1
 TV_MAX_NODES, TV_MAX_DEPTH, TV_MAX_LEDGER, TV_MAX_VOCAB = 1024, 64, 8192, 16777216
 DEVERR_BAD_PARENT, DEVERR_TOO_DEEP, DEVERR_BAD_REQUEST, DEVERR_BAD_PATH, DEVERR_BAD_LEDGER = 1, 2, 3, 4, 5
+DEVERR_LIMIT = 6
+TV_GDN_HEAD_DIM, TV_GDN_MAX_NODES, TV_GDN_MAX_TABLE = 128, 256, 4096
 
 
 class TreeVerifyError(RuntimeError):
@@ -64,6 +66,14 @@ def lib() -> C.CDLL:
     L.tree_rope_apply.restype = C.c_int
     L.kv_rollback_token_table.argtypes = [vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp]
     L.kv_rollback_token_table.restype = C.c_int
+    L.tree_gdn_conv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
+    L.tree_gdn_conv.restype = C.c_int
+    L.tree_gdn_verify.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
+                                  vp, vp, vp]
+    L.tree_gdn_verify.restype = C.c_int
+    L.tree_gdn_commit.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                  i32, i32, vp, vp]
+    L.tree_gdn_commit.restype = C.c_int
     _lib = L
     return L
 
@@ -306,3 +316,108 @@ def kv_rollback_token_table(req_to_token, tree_slots, cu_nodes, prefix_len, acce
         _ptr(accept_idx), B, total_nodes, max_depth, _ptr(new_len), _ptr(freed_slots), _ptr(n_freed), _ptr(err),
         _stream(stream)))
     return new_len, freed_slots, n_freed, err
+
+
+# ---------------------------------------------------------------------------
+# Tree-aware Gated-DeltaNet verification (tree_gdn_conv, tree_gdn_verify,
+# tree_gdn_commit).  q, k and v are [T, H, 128] bf16 tensors sharing one row
+# stride, e.g. the views gdn_split() takes of tree_gdn_conv's output.
+# ---------------------------------------------------------------------------
+
+def gdn_split(y, hk: int, hv: int, d: int = 128):
+    """Views (q, k, v) of a mixed [T, 2*hk*d + hv*d] row: q, then k, then v."""
+    T = y.shape[0]
+    q = y[:, :hk * d].unflatten(1, (hk, d))
+    k = y[:, hk * d:2 * hk * d].unflatten(1, (hk, d))
+    v = y[:, 2 * hk * d:].unflatten(1, (hv, d))
+    assert v.shape == (T, hv, d)
+    return q, k, v
+
+
+def _rows_stride(ts, names):
+    """Common row stride of [T, H, d] bf16 tensors with unit channel stride."""
+    import torch
+    rs = None
+    for t, n in zip(ts, names):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{n} must be a GPU tensor")
+        if t.dtype != torch.bfloat16 or t.dim() != 3:
+            raise TypeError(f"{n} must be a [T, H, d] bfloat16 tensor")
+        if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise ValueError(f"{n} must have contiguous heads")
+        s = t.stride(0) if t.shape[0] > 1 else None
+        if s is not None:
+            if rs is not None and s != rs:
+                raise ValueError("q, k and v must share one row stride")
+            rs = s
+    if rs is None:
+        rs = max(t.shape[1] * t.shape[2] for t in ts)
+    return rs
+
+
+def tree_gdn_conv(x, conv_state, weight, parent, cu_nodes, y=None, err=None, stream=None):
+    """x [T, C] bf16, conv_state [B, K-1, C] bf16, weight [C, K] bf16 ->
+    (y [T, C] bf16, err)."""
+    import torch
+    T, Cc = x.shape
+    B = cu_nodes.numel() - 1
+    K = weight.shape[1]
+    for t, n in ((x, "x"), (conv_state, "conv_state"), (weight, "weight")):
+        _need(t, n, torch.bfloat16)
+    _need(parent, "parent", torch.int32, T)
+    _need(cu_nodes, "cu_nodes", torch.int32)
+    y = torch.empty_like(x) if y is None else y
+    _need(y, "y", torch.bfloat16, T * Cc)
+    err = torch.zeros(1, dtype=torch.int32, device=x.device) if err is None else err
+    _check("tree_gdn_conv", lib().tree_gdn_conv(
+        _ptr(x), _ptr(conv_state), _ptr(weight), _ptr(parent), _ptr(cu_nodes), B, T, Cc, K, _ptr(y), _ptr(err),
+        _stream(stream)))
+    return y, err
+
+
+def tree_gdn_verify(q, k, v, g, beta, state, parent, cu_nodes, max_depth: int, scale: float | None = None,
+                    l2norm: bool = True, out=None, err=None, stream=None):
+    """q, k [T, hk, 128], v [T, hv, 128] bf16 (one row stride); g, beta [T, hv]
+    float32; state [B, hv, 128, 128] float32 -> (out [T, hv, 128] float32, err)."""
+    import torch
+    T, hk, d = q.shape
+    hv = v.shape[1]
+    B = cu_nodes.numel() - 1
+    rs = _rows_stride((q, k, v), ("q", "k", "v"))
+    for t, n in ((g, "g"), (beta, "beta"), (state, "state")):
+        _need(t, n, torch.float32)
+    _need(parent, "parent", torch.int32, T)
+    _need(cu_nodes, "cu_nodes", torch.int32)
+    scale = d ** -0.5 if scale is None else scale
+    out = torch.empty((T, hv, d), dtype=torch.float32, device=q.device) if out is None else out
+    _need(out, "out", torch.float32, T * hv * d)
+    err = torch.zeros(1, dtype=torch.int32, device=q.device) if err is None else err
+    _check("tree_gdn_verify", lib().tree_gdn_verify(
+        _ptr(q), _ptr(k), _ptr(v), rs, _ptr(g), _ptr(beta), _ptr(state), _ptr(parent), _ptr(cu_nodes), B, T,
+        max_depth, hk, hv, d, float(scale), int(bool(l2norm)), _ptr(out), _ptr(err), _stream(stream)))
+    return out, err
+
+
+def tree_gdn_commit(state, conv_state, x, k, v, g, beta, cu_nodes, accept_len, accept_idx, max_depth: int,
+                    l2norm: bool = True, err=None, stream=None):
+    """Advances state [B, hv, 128, 128] float32 and conv_state [B, K-1, C] bf16
+    in place by each request's accepted path -> err."""
+    import torch
+    T, Cc = x.shape
+    B = cu_nodes.numel() - 1
+    hk, hv, d = k.shape[1], v.shape[1], k.shape[2]
+    rs = _rows_stride((k, v), ("k", "v"))
+    _need(state, "state", torch.float32)
+    _need(conv_state, "conv_state", torch.bfloat16)
+    _need(x, "x", torch.bfloat16)
+    for t, n in ((g, "g"), (beta, "beta")):
+        _need(t, n, torch.float32)
+    for t, n in ((cu_nodes, "cu_nodes"), (accept_len, "accept_len"), (accept_idx, "accept_idx")):
+        _need(t, n, torch.int32)
+    K = conv_state.shape[1] + 1
+    err = torch.zeros(1, dtype=torch.int32, device=state.device) if err is None else err
+    _check("tree_gdn_commit", lib().tree_gdn_commit(
+        _ptr(state), _ptr(conv_state), _ptr(x), _ptr(k), _ptr(v), rs, _ptr(g), _ptr(beta), _ptr(cu_nodes),
+        _ptr(accept_len), _ptr(accept_idx), B, T, max_depth, hk, hv, d, Cc, K, int(bool(l2norm)), _ptr(err),
+        _stream(stream)))
+    return err

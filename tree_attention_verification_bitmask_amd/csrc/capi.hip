@@ -35,6 +35,22 @@ tv_status check_attn_sizes(int32_t batch, int32_t total_nodes, int32_t max_nodes
     return TV_OK;
 }
 
+tv_status check_gdn_heads(int32_t hk, int32_t hv, int32_t head_dim, int32_t max_depth, int64_t row_stride) {
+    if (hk < 1 || hv < 1 || hv % hk != 0 || max_depth < 1 || row_stride < 1) return TV_ERR_SHAPE;
+    if (hv > 65535 || max_depth > TV_MAX_DEPTH) return TV_ERR_LIMIT;
+    if (head_dim != TV_GDN_HEAD_DIM) return TV_ERR_DTYPE;
+    if (row_stride % 8 != 0) return TV_ERR_ALIGN;
+    return TV_OK;
+}
+
+tv_status check_gdn_conv(int32_t total_or_batch, int32_t channels, int32_t conv_k) {
+    if (channels < 8 || channels % 8 != 0) return TV_ERR_SHAPE;
+    if (conv_k < 2 || conv_k > 4) return TV_ERR_SHAPE;
+    const int64_t groups = (channels / 8 + 255) / 256;
+    if ((int64_t)total_or_batch * groups > (1ll << 31) - 1) return TV_ERR_LIMIT;
+    return TV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -231,6 +247,60 @@ tv_status kv_rollback_token_table(int32_t *req_to_token, int64_t table_stride, c
     return launch_status(tv::launch_rollback_table(req_to_token, table_stride, tree_slots, cu_nodes, prefix_len,
                                                    accept_len, accept_idx, batch, total_nodes, max_depth, new_len,
                                                    freed_slots, n_freed, err, (hipStream_t)stream));
+}
+
+tv_status tree_gdn_conv(const void *x, const void *conv_state, const void *weight, const int32_t *parent,
+                        const int32_t *cu_nodes, int32_t batch, int32_t total_nodes, int32_t channels,
+                        int32_t conv_k, void *y, int32_t *err, void *stream) {
+    tv_status st = check_batch(batch, total_nodes);
+    if (st != TV_OK) return st;
+    if ((st = check_gdn_conv(total_nodes, channels, conv_k)) != TV_OK) return st;
+    if (!cu_nodes) return TV_ERR_NULL;
+    if (total_nodes > 0 && (!x || !conv_state || !weight || !parent || !y)) return TV_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(conv_state, 16) || !aligned(weight, 16) || !aligned(y, 16))
+        return TV_ERR_ALIGN;
+    if (batch == 0 || total_nodes == 0) return TV_OK;
+    return launch_status(tv::launch_gdn_conv(x, conv_state, weight, parent, cu_nodes, batch, total_nodes, channels,
+                                             conv_k, y, err, (hipStream_t)stream));
+}
+
+tv_status tree_gdn_verify(const void *q, const void *k, const void *v, int64_t row_stride, const float *g,
+                          const float *beta, const float *state, const int32_t *parent, const int32_t *cu_nodes,
+                          int32_t batch, int32_t total_nodes, int32_t max_depth, int32_t hk, int32_t hv,
+                          int32_t head_dim, float scale, int32_t l2norm, float *out, int32_t *err, void *stream) {
+    tv_status st = check_batch(batch, total_nodes);
+    if (st != TV_OK) return st;
+    if ((st = check_gdn_heads(hk, hv, head_dim, max_depth, row_stride)) != TV_OK) return st;
+    if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return TV_ERR_SHAPE;
+    if (l2norm != 0 && l2norm != 1) return TV_ERR_SHAPE;
+    if (!cu_nodes) return TV_ERR_NULL;
+    if (total_nodes > 0 && (!q || !k || !v || !g || !beta || !state || !parent || !out)) return TV_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(state, 16)) return TV_ERR_ALIGN;
+    if ((int64_t)batch * hv * (TV_GDN_HEAD_DIM / 32) > (1ll << 31) - 1) return TV_ERR_LIMIT;
+    if (batch == 0 || total_nodes == 0) return TV_OK;
+    return launch_status(tv::launch_gdn_verify(q, k, v, row_stride, g, beta, state, parent, cu_nodes, batch,
+                                               total_nodes, max_depth, hk, hv, scale, l2norm, out, err,
+                                               (hipStream_t)stream));
+}
+
+tv_status tree_gdn_commit(float *state, void *conv_state, const void *x, const void *k, const void *v,
+                          int64_t row_stride, const float *g, const float *beta, const int32_t *cu_nodes,
+                          const int32_t *accept_len, const int32_t *accept_idx, int32_t batch, int32_t total_nodes,
+                          int32_t max_depth, int32_t hk, int32_t hv, int32_t head_dim, int32_t channels,
+                          int32_t conv_k, int32_t l2norm, int32_t *err, void *stream) {
+    tv_status st = check_batch(batch, total_nodes);
+    if (st != TV_OK) return st;
+    if ((st = check_gdn_heads(hk, hv, head_dim, max_depth, row_stride)) != TV_OK) return st;
+    if ((st = check_gdn_conv(batch, channels, conv_k)) != TV_OK) return st;
+    if (l2norm != 0 && l2norm != 1) return TV_ERR_SHAPE;
+    if ((int64_t)batch * hv > (1ll << 31) - 1) return TV_ERR_LIMIT;
+    if (!state || !conv_state || !cu_nodes || !accept_len || !accept_idx) return TV_ERR_NULL;
+    if (total_nodes > 0 && (!x || !k || !v || !g || !beta)) return TV_ERR_NULL;
+    if (!aligned(state, 16) || !aligned(conv_state, 16) || !aligned(x, 16)) return TV_ERR_ALIGN;
+    if (batch == 0) return TV_OK;
+    return launch_status(tv::launch_gdn_commit(state, conv_state, x, k, v, row_stride, g, beta, cu_nodes,
+                                               accept_len, accept_idx, batch, total_nodes, max_depth, hk, hv,
+                                               channels, conv_k, l2norm, err, (hipStream_t)stream));
 }
 
 }  // extern "C"

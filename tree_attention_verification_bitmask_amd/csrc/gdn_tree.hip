@@ -1,0 +1,570 @@
+// Tree-aware recurrent verification for a Gated-DeltaNet layer.
+//
+// [DT] = "DominoTree: Conditional Tree-Structured Drafting with Domino for
+// Speculative Decoding" (arXiv 2607.08642), section 4.5.4, "Tree-aware
+// recurrent verification": an ancestor mask is not enough for a recurrent
+// layer.  Every node needs the recurrent state of its own root path and a
+// dense short-convolution window made of its own ancestors, and only the
+// accepted path's state is committed.  A chain recurrence over the flattened
+// tree would let a rejected sibling write into the state its cousins read.
+//
+// The page gives no formulas; the layer is the gated delta rule with L2-normalised
+// queries and keys:
+//   S_t = e^{g_t} S_p (I - beta_t k^_t k^_t^T) + beta_t v_t k^_t^T,  o_t = S_t q^_t
+// where p = parent(t), the request's committed state S0 stands in for the
+// parent of a root child, S is [dv, dk] per value head, and value head h reads
+// query/key head h / (Hv / Hk).
+//
+// gdn_conv_kernel: the depthwise causal convolution (width K) with SiLU.  A
+// node's window is the committed conv state followed by the inputs along its
+// root path, i.e. its K nearest ancestors-or-self, topped up from the conv
+// state.  Streaming work: one thread per (node, 8 channels).
+//
+// gdn_verify_kernel: all nodes' outputs in one pass per (request, value head,
+// 32-channel slice of v).  The recurrence is unrolled with the
+// ancestor-restricted WY form: writing S_t = e^{G_t} S0 + sum_{s in path(t)}
+// e^{G_t - G_s} u_s k^_s^T (G = log decay summed along the root path), the
+// write vectors satisfy
+//   u_t + sum_{s in anc(t)} A[t,s] u_s = r_t,
+//   A[t,s] = beta_t e^{G_t - G_s} (k^_t . k^_s),  r_t = beta_t (v_t - e^{G_t} S0 k^_t)
+// and o_t = e^{G_t} S0 q^_t + sum_{s in path(t)} c[t,s] u_s with
+// c[t,s] = e^{G_t - G_s} (q^_t . k^_s).  Both sums run over one root path only,
+// so each node eliminates u on its own path: z^T (I + A_path) = c^T by back
+// substitution, and o_t = e^{G_t} S0 q^_t + sum_a z_a r_{s_a}.  The dense
+// products (K K^T, Q K^T, S0 K^T, S0 Q^T) run on v_mfma_f32_32x32x16_bf16; the
+// fp32 state enters them as a bf16 hi + lo pair (about 16 significant bits,
+// two products).  Only the entries on ancestor pairs are kept, in per-node
+// tables indexed by the ancestor's level.
+//
+// gdn_commit_state_kernel / gdn_commit_conv_kernel: the accepted path's tokens
+// replayed in order into the committed state (fp32, one step at a time), and
+// the conv state advanced by the accepted inputs.
+#include "tv_device.h"
+#include "tv_launch.h"
+
+namespace tv {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHd = TV_GDN_HEAD_DIM;      // dk = dv
+constexpr int kSlice = 32;                // value channels per verify workgroup
+constexpr int kSlices = kHd / kSlice;
+constexpr int kVThreads = 256;
+constexpr int kMaxN = TV_GDN_MAX_NODES;   // nodes per request
+constexpr int kTab = TV_GDN_MAX_TABLE;    // nodes x max_depth per request
+constexpr int kKRow = kHd + 8;            // LDS row of K in bf16 (272 B: rows 4 banks apart)
+constexpr float kEps = 1e-6f;
+constexpr int kConvThreads = 256;
+
+static_assert(kHd == 128, "fragments assume 128 channels per head");
+static_assert(kMaxN * kKRow * 2 + kMaxN * kSlice * 4 + 2 * kTab * 4 + kTab * 2 + 5 * kMaxN * 4 <= 160 * 1024,
+              "verify tables fit the 160 KB LDS");
+
+__device__ __forceinline__ float bf(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// ---------------------------------------------------------------------------
+// Convolution over each node's ancestor window.
+// ---------------------------------------------------------------------------
+template <int K>
+__global__ void __launch_bounds__(kConvThreads) gdn_conv_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ cstate, const uint16_t *__restrict__ w,
+    const int32_t *__restrict__ parent, const int32_t *__restrict__ cu_nodes, int batch, int C, int groups,
+    uint16_t *__restrict__ y, int32_t *__restrict__ err) {
+    const int t = blockIdx.x / groups;
+    const int gi = blockIdx.x - t * groups;
+    const bool reporter = gi == 0 && threadIdx.x == 0;
+    const int b = request_of(cu_nodes, batch, t);
+    if (b < 0) {
+        if (reporter) report(err, TV_DEVERR_BAD_REQUEST, 0);
+        return;
+    }
+    const int lo = cu_nodes[b];
+    // a[j] = the node's j-th ancestor-or-self (local index), -1 past the root
+    int a[K];
+    int din = 0;
+    int cur = t - lo;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        a[j] = cur;
+        if (cur >= 0) {
+            ++din;
+            const int p = parent[lo + cur];
+            const bool ok = p >= -1 && p < cur;
+            if (!ok && reporter) report(err, TV_DEVERR_BAD_PARENT, lo + cur);
+            cur = ok ? p : -1;
+        }
+    }
+    const int c8 = (gi * kConvThreads + threadIdx.x) * 8;
+    if (c8 >= C) return;
+    // taps of the 8 channels: w[(c8 + e) * K + i], 8K contiguous bf16
+    float wf[8][K];
+    {
+        const u32x4 *wp = reinterpret_cast<const u32x4 *>(w + (int64_t)c8 * K);
+        uint32_t wv[4 * K];
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+            const u32x4 q = wp[i];
+            wv[4 * i] = q[0];
+            wv[4 * i + 1] = q[1];
+            wv[4 * i + 2] = q[2];
+            wv[4 * i + 3] = q[3];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int i = 0; i < K; ++i) {
+                const int f = e * K + i;
+                wf[e][i] = (f & 1) ? bf16_hi(wv[f >> 1]) : bf16_lo(wv[f >> 1]);
+            }
+    }
+    float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        // window slot K-1-j: the j-th ancestor-or-self, else conv state row
+        // K-2-(j-din) (the most recent committed input is row K-2)
+        const uint16_t *src = a[j] >= 0 ? x + (int64_t)(lo + a[j]) * C + c8
+                                        : cstate + ((int64_t)b * (K - 1) + (K - 2 - (j - din))) * C + c8;
+        const u32x4 q = *reinterpret_cast<const u32x4 *>(src);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float xv = (e & 1) ? bf16_hi(q[e >> 1]) : bf16_lo(q[e >> 1]);
+            z[e] = fmaf(wf[e][K - 1 - j], xv, z[e]);
+        }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float y0 = z[2 * e] / (1.f + expf(-z[2 * e]));
+        const float y1 = z[2 * e + 1] / (1.f + expf(-z[2 * e + 1]));
+        o[e] = pack_bf16x2(y0, y1);
+    }
+    *reinterpret_cast<u32x4 *>(y + (int64_t)t * C + c8) = o;
+}
+
+// ---------------------------------------------------------------------------
+// Verification: one workgroup per (request, value head, 32-channel slice).
+// ---------------------------------------------------------------------------
+struct VerifyArgs {
+    const uint16_t *q, *k, *v;
+    int64_t rs;  // row stride of q, k, v in elements
+    const float *g, *beta, *state;
+    const int32_t *parent, *cu_nodes;
+    int batch, total_nodes, D, hk, hv;
+    float scale;
+    int l2norm;
+    float *out;
+    int32_t *err;
+};
+
+__device__ __forceinline__ bf16x8_t lds_frag(const uint16_t *p) { return *reinterpret_cast<const bf16x8_t *>(p); }
+
+__global__ void __launch_bounds__(kVThreads) gdn_verify_kernel(VerifyArgs p) {
+    __shared__ __align__(16) uint16_t kS[kMaxN * kKRow];  // K rows of the request, bf16
+    __shared__ float rS[kMaxN * kSlice];                   // r_t for the slice
+    __shared__ float Atab[kTab];                           // [t][level-1]: k.k, then A[t, anc]
+    __shared__ float Ctab[kTab];                           // [t][level-1]: q.k, then c, then z
+    __shared__ int16_t anc[kTab];                          // [t][level-1]: the ancestor at that level
+    __shared__ float Gs[kMaxN], nk[kMaxN], mq[kMaxN], bt[kMaxN];
+    __shared__ int lev[kMaxN];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // XCD-aware order: the 8 workgroups dealt to one XCD in a row are
+    // consecutive tasks, so the tasks that read one key head share an L2.
+    int id = blockIdx.x;
+    const int nwg = gridDim.x;
+    if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
+    const int slice = id % kSlices;
+    const int h = (id / kSlices) % p.hv;
+    const int b = id / (kSlices * p.hv);
+    const int D = p.D;
+    int lo;
+    const int n = request_nodes(p.cu_nodes, b, p.total_nodes, p.total_nodes, &lo);
+    if (n < 0) {
+        if (tid == 0) report(p.err, TV_DEVERR_BAD_REQUEST, b);
+        return;
+    }
+    if (n > kMaxN || n * D > kTab) {
+        if (tid == 0) report(p.err, TV_DEVERR_LIMIT, b);
+        return;
+    }
+    if (n == 0) return;
+    const int hkk = h / (p.hv / p.hk);
+    const int i0 = slice * kSlice;
+    const int nb = (n + 31) >> 5;
+    const bool reporter = h == 0 && slice == 0;
+
+    // ---- (0) levels, ancestor rows, cumulative log decay --------------------
+    if (tid < n) {
+        const int t = tid;
+        int L = 0, u = t;
+        while (u >= 0) {
+            if (L == D) {
+                if (reporter) report(p.err, TV_DEVERR_TOO_DEEP, lo + t);
+                break;
+            }
+            ++L;
+            const int pp = p.parent[lo + u];
+            if (pp < -1 || pp >= u) {
+                if (reporter) report(p.err, TV_DEVERR_BAD_PARENT, lo + u);
+                break;
+            }
+            u = pp;
+        }
+        // L >= 1 steps were validated: write them root first
+        u = t;
+        for (int j = L - 1; j >= 0; --j) {
+            anc[t * D + j] = (int16_t)u;
+            if (j > 0) u = p.parent[lo + u];
+        }
+        float G = 0.f;
+        for (int j = 0; j < L; ++j) G += p.g[(int64_t)(lo + anc[t * D + j]) * p.hv + h];
+        lev[t] = L;
+        Gs[t] = G;
+        bt[t] = p.beta[(int64_t)(lo + t) * p.hv + h];
+    }
+    // K rows (zero rows pad the last 32-row block)
+    for (int e = tid; e < nb * 32 * 16; e += kVThreads) {
+        const int row = e >> 4, g16 = e & 15;
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (row < n)
+            val = *reinterpret_cast<const u32x4 *>(p.k + (int64_t)(lo + row) * p.rs + hkk * kHd + 8 * g16);
+        *reinterpret_cast<u32x4 *>(&kS[row * kKRow + 8 * g16]) = val;
+    }
+    __syncthreads();
+    if (tid < n) {
+        const int t = tid;
+        float sk = 0.f, sq = 0.f;
+        const uint16_t *qrow = p.q + (int64_t)(lo + t) * p.rs + hkk * kHd;
+#pragma unroll 4
+        for (int g16 = 0; g16 < 16; ++g16) {
+            const u32x4 kv = *reinterpret_cast<const u32x4 *>(&kS[t * kKRow + 8 * g16]);
+            const u32x4 qv = *reinterpret_cast<const u32x4 *>(qrow + 8 * g16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float k0 = bf16_lo(kv[e]), k1 = bf16_hi(kv[e]);
+                const float q0 = bf16_lo(qv[e]), q1 = bf16_hi(qv[e]);
+                sk = fmaf(k0, k0, fmaf(k1, k1, sk));
+                sq = fmaf(q0, q0, fmaf(q1, q1, sq));
+            }
+        }
+        nk[t] = p.l2norm ? 1.f / sqrtf(sk + kEps) : 1.f;
+        mq[t] = p.scale * (p.l2norm ? 1.f / sqrtf(sq + kEps) : 1.f);
+    }
+    __syncthreads();
+
+    // ---- (1) dense products on the matrix cores ------------------------------
+    // Wave w owns row blocks w and 7 - w (the triangle's work balanced).
+    // Fragment of lane l: row l % 32, channels 16 ks + 8 (l / 32) .. + 8.
+    const int col = lane & 31, half = lane >> 5;
+    const f32x16_t zero16 = {};
+    f32x16_t qs_acc[2] = {zero16, zero16};
+#pragma unroll
+    for (int slot = 0; slot < 2; ++slot) {
+        const int tb = slot == 0 ? wave : 7 - wave;
+        if (tb >= nb) continue;
+        bf16x8_t ka[8], qa[8];
+        const int r = tb * 32 + col;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) ka[ks] = lds_frag(&kS[r * kKRow + 16 * ks + 8 * half]);
+        {
+            const uint16_t *qrow = p.q + (int64_t)(lo + min(r, n - 1)) * p.rs + hkk * kHd + 8 * half;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                qa[ks] = *reinterpret_cast<const bf16x8_t *>(qrow + 16 * ks);
+                if (r >= n) qa[ks] = bf16x8_t{};
+            }
+        }
+        // S0 k and S0 q for the slice: B[kk][j] = S0[i0 + j][kk], as hi + lo
+        f32x16_t ks_acc = zero16, qsa = zero16;
+        {
+            const float *srow = p.state + (((int64_t)b * p.hv + h) * kHd + (i0 + col)) * kHd + 8 * half;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const f32x4 s0 = *reinterpret_cast<const f32x4 *>(srow + 16 * ks);
+                const f32x4 s1 = *reinterpret_cast<const f32x4 *>(srow + 16 * ks + 4);
+                bf16x8_t hi, lo8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float xv = e < 4 ? s0[e] : s1[e - 4];
+                    const __bf16 hb = (__bf16)xv;
+                    hi[e] = hb;
+                    lo8[e] = (__bf16)(xv - (float)hb);
+                }
+                ks_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], hi, ks_acc, 0, 0, 0);
+                ks_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], lo8, ks_acc, 0, 0, 0);
+                qsa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], hi, qsa, 0, 0, 0);
+                qsa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], lo8, qsa, 0, 0, 0);
+            }
+        }
+        qs_acc[slot] = qsa;
+        // accumulator element e of lane l: row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32
+        int levt[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int t = tb * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+            levt[e] = t < n ? lev[t] : 0;
+            if (t < n) {
+                const float vv = bf(p.v[(int64_t)(lo + t) * p.rs + h * kHd + i0 + col]);
+                rS[t * kSlice + col] = bt[t] * (vv - expf(Gs[t]) * nk[t] * ks_acc[e]);
+            }
+        }
+        // k.k and q.k against every earlier row block; keep ancestor pairs
+        for (int sb = 0; sb <= tb; ++sb) {
+            bf16x8_t kb[8];
+            const int sr = sb * 32 + col;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) kb[ks] = lds_frag(&kS[sr * kKRow + 16 * ks + 8 * half]);
+            f32x16_t kk = zero16, qk = zero16;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                kk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], kb[ks], kk, 0, 0, 0);
+                qk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kb[ks], qk, 0, 0, 0);
+            }
+            // lane's column is node s = sr; element e's row is node t
+            const int ls = sr < n ? lev[sr] : kMaxN;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int t = tb * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+                if (ls <= levt[e] && anc[t * D + ls - 1] == sr) {
+                    Atab[t * D + ls - 1] = kk[e];
+                    Ctab[t * D + ls - 1] = qk[e];
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- (2) per node: scale the tables, then eliminate along the path ------
+    if (tid < n) {
+        const int t = tid;
+        const int L = lev[t];
+        const float Gt = Gs[t], ntt = nk[t], bn = bt[t] * ntt, mt = mq[t];
+        for (int a = 0; a < L; ++a) {
+            const int s = anc[t * D + a];
+            const float f = expf(Gt - Gs[s]) * nk[s];
+            if (a < L - 1) Atab[t * D + a] *= bn * f;
+            Ctab[t * D + a] *= mt * f;
+        }
+    }
+    __syncthreads();
+    if (tid < n) {
+        const int t = tid;
+        const int L = lev[t];
+        float *crow = &Ctab[t * D];
+        // z^T (I + A_path) = c^T: z_a is final once every deeper a' is done
+        for (int a = L - 1; a >= 1; --a) {
+            const float za = crow[a];
+            const float *arow = &Atab[anc[t * D + a] * D];
+            for (int j = 0; j < a; ++j) crow[j] = fmaf(-za, arow[j], crow[j]);
+        }
+    }
+    __syncthreads();
+
+    // ---- (3) outputs in the accumulator layout --------------------------------
+#pragma unroll
+    for (int slot = 0; slot < 2; ++slot) {
+        const int tb = slot == 0 ? wave : 7 - wave;
+        if (tb >= nb) continue;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int t = tb * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+            if (t >= n) continue;
+            const int L = lev[t];
+            float o = mq[t] * expf(Gs[t]) * qs_acc[slot][e];
+            for (int a = 0; a < L; ++a) o = fmaf(Ctab[t * D + a], rS[anc[t * D + a] * kSlice + col], o);
+            p.out[((int64_t)(lo + t) * p.hv + h) * kHd + i0 + col] = o;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Commit: the accepted tokens replayed into the state, and the conv state.
+// ---------------------------------------------------------------------------
+constexpr int kCThreads = 256;
+
+// Checks request b's accepted path; returns L (>= 0) or -1 after reporting.
+__device__ __forceinline__ int commit_path(const int32_t *cu_nodes, const int32_t *accept_len,
+                                           const int32_t *accept_idx, int b, int total_nodes, int D,
+                                           bool reporter, int32_t *err, int *lo_out, int32_t *s_idx) {
+    int lo;
+    const int n = request_nodes(cu_nodes, b, total_nodes, total_nodes, &lo);
+    *lo_out = lo;
+    const int L = n < 0 ? -1 : accept_len[b];
+    if (n < 0 || L < 0 || L > D || L > n) {
+        if (reporter && threadIdx.x == 0) report(err, TV_DEVERR_BAD_REQUEST, b);
+        return -1;
+    }
+    bool bad = false;
+    if ((int)threadIdx.x < L) {
+        const int my = accept_idx[(int64_t)b * D + threadIdx.x];
+        bad = my < 0 || my >= n;
+        s_idx[threadIdx.x] = my;
+    }
+    if (__syncthreads_or(bad)) {
+        if (reporter && threadIdx.x == 0) report(err, TV_DEVERR_BAD_PATH, b);
+        return -1;
+    }
+    return L;
+}
+
+__global__ void __launch_bounds__(kCThreads) gdn_commit_state_kernel(
+    float *__restrict__ state, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, int64_t rs,
+    const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu_nodes,
+    const int32_t *__restrict__ accept_len, const int32_t *__restrict__ accept_idx, int total_nodes, int D, int hk,
+    int hv, int l2norm, int32_t *__restrict__ err) {
+    __shared__ float khat[TV_MAX_DEPTH][kHd];
+    __shared__ float al[TV_MAX_DEPTH], be[TV_MAX_DEPTH];
+    __shared__ int32_t s_idx[TV_MAX_DEPTH];
+    const int b = blockIdx.x / hv, h = blockIdx.x - (blockIdx.x / hv) * hv;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int lo;
+    const int L = commit_path(cu_nodes, accept_len, accept_idx, b, total_nodes, D, h == 0, err, &lo, s_idx);
+    if (L <= 0) return;
+    const int hkk = h / (hv / hk);
+    // normalised keys, decays and write strengths of the accepted tokens
+    for (int j = wave; j < L; j += kCThreads / 64) {
+        const int64_t t = lo + s_idx[j];
+        const uint32_t pr = *reinterpret_cast<const uint32_t *>(k + t * rs + hkk * kHd + 2 * lane);
+        const float k0 = bf16_lo(pr), k1 = bf16_hi(pr);
+        const float ss = wave_sum(fmaf(k0, k0, k1 * k1));
+        const float nf = l2norm ? 1.f / sqrtf(ss + kEps) : 1.f;
+        khat[j][2 * lane] = k0 * nf;
+        khat[j][2 * lane + 1] = k1 * nf;
+        if (lane == 0) {
+            al[j] = expf(g[t * hv + h]);
+            be[j] = beta[t * hv + h];
+        }
+    }
+    __syncthreads();
+    // thread: state row i, columns c0 .. c0 + 63
+    const int i = tid >> 1, c0 = (tid & 1) * 64;
+    float *srow = state + (((int64_t)b * hv + h) * kHd + i) * kHd + c0;
+    float s[64];
+#pragma unroll
+    for (int c = 0; c < 64; c += 4) {
+        const f32x4 x4 = *reinterpret_cast<const f32x4 *>(srow + c);
+        s[c] = x4[0];
+        s[c + 1] = x4[1];
+        s[c + 2] = x4[2];
+        s[c + 3] = x4[3];
+    }
+    for (int j = 0; j < L; ++j) {
+        const float vi = bf(v[(int64_t)(lo + s_idx[j]) * rs + h * kHd + i]);
+        const float *kh = &khat[j][c0];
+        float y = 0.f;
+#pragma unroll
+        for (int c = 0; c < 64; ++c) y = fmaf(s[c], kh[c], y);
+        y += __shfl_xor(y, 1, 64);
+        const float a = al[j];
+        const float wgt = be[j] * (vi - a * y);
+#pragma unroll
+        for (int c = 0; c < 64; ++c) s[c] = fmaf(wgt, kh[c], a * s[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < 64; c += 4) *reinterpret_cast<f32x4 *>(srow + c) = f32x4{s[c], s[c + 1], s[c + 2], s[c + 3]};
+}
+
+template <int K>
+__global__ void __launch_bounds__(kCThreads) gdn_commit_conv_kernel(
+    uint16_t *__restrict__ cstate, const uint16_t *__restrict__ x, const int32_t *__restrict__ cu_nodes,
+    const int32_t *__restrict__ accept_len, const int32_t *__restrict__ accept_idx, int total_nodes, int D, int C,
+    int groups, int32_t *__restrict__ err) {
+    __shared__ int32_t s_idx[TV_MAX_DEPTH];
+    const int b = blockIdx.x / groups;
+    const int gi = blockIdx.x - b * groups;
+    int lo;
+    const int L = commit_path(cu_nodes, accept_len, accept_idx, b, total_nodes, D, gi == 0, err, &lo, s_idx);
+    if (L <= 0) return;
+    const int c8 = (gi * kCThreads + threadIdx.x) * 8;
+    if (c8 >= C) return;
+    // sequence = old rows 0 .. K-2, then the accepted inputs; keep the last K-1
+    uint16_t *base = cstate + (int64_t)b * (K - 1) * C + c8;
+    u32x4 nv[K - 1];
+#pragma unroll
+    for (int r = 0; r < K - 1; ++r) {
+        const int q = L + r;
+        const uint16_t *src = q < K - 1 ? base + (int64_t)q * C : x + (int64_t)(lo + s_idx[q - (K - 1)]) * C + c8;
+        nv[r] = *reinterpret_cast<const u32x4 *>(src);
+    }
+#pragma unroll
+    for (int r = 0; r < K - 1; ++r) *reinterpret_cast<u32x4 *>(base + (int64_t)r * C) = nv[r];
+}
+
+}  // namespace
+
+hipError_t launch_gdn_conv(const void *x, const void *conv_state, const void *weight, const int32_t *parent,
+                           const int32_t *cu_nodes, int batch, int total_nodes, int channels, int conv_k, void *y,
+                           int32_t *err, hipStream_t stream) {
+    if (batch == 0 || total_nodes == 0) return hipSuccess;
+    const int groups = (channels / 8 + kConvThreads - 1) / kConvThreads;
+    const dim3 grid((unsigned)((int64_t)total_nodes * groups));
+    const auto *xp = (const uint16_t *)x;
+    const auto *cp = (const uint16_t *)conv_state;
+    const auto *wp = (const uint16_t *)weight;
+    auto *yp = (uint16_t *)y;
+    switch (conv_k) {
+        case 2:
+            hipLaunchKernelGGL(gdn_conv_kernel<2>, grid, dim3(kConvThreads), 0, stream, xp, cp, wp, parent, cu_nodes,
+                               batch, channels, groups, yp, err);
+            break;
+        case 3:
+            hipLaunchKernelGGL(gdn_conv_kernel<3>, grid, dim3(kConvThreads), 0, stream, xp, cp, wp, parent, cu_nodes,
+                               batch, channels, groups, yp, err);
+            break;
+        default:
+            hipLaunchKernelGGL(gdn_conv_kernel<4>, grid, dim3(kConvThreads), 0, stream, xp, cp, wp, parent, cu_nodes,
+                               batch, channels, groups, yp, err);
+            break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gdn_verify(const void *q, const void *k, const void *v, int64_t row_stride, const float *g,
+                             const float *beta, const float *state, const int32_t *parent, const int32_t *cu_nodes,
+                             int batch, int total_nodes, int max_depth, int hk, int hv, float scale, int l2norm,
+                             float *out, int32_t *err, hipStream_t stream) {
+    if (batch == 0 || total_nodes == 0) return hipSuccess;
+    VerifyArgs a{(const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, row_stride, g, beta, state,
+                 parent, cu_nodes, batch, total_nodes, max_depth, hk, hv, scale, l2norm, out, err};
+    const int64_t grid = (int64_t)batch * hv * kSlices;
+    hipLaunchKernelGGL(gdn_verify_kernel, dim3((unsigned)grid), dim3(kVThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gdn_commit(float *state, void *conv_state, const void *x, const void *k, const void *v,
+                             int64_t row_stride, const float *g, const float *beta, const int32_t *cu_nodes,
+                             const int32_t *accept_len, const int32_t *accept_idx, int batch, int total_nodes,
+                             int max_depth, int hk, int hv, int channels, int conv_k, int l2norm, int32_t *err,
+                             hipStream_t stream) {
+    if (batch == 0) return hipSuccess;
+    hipLaunchKernelGGL(gdn_commit_state_kernel, dim3((unsigned)((int64_t)batch * hv)), dim3(kCThreads), 0, stream,
+                       state, (const uint16_t *)k, (const uint16_t *)v, row_stride, g, beta, cu_nodes, accept_len,
+                       accept_idx, total_nodes, max_depth, hk, hv, l2norm, err);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int groups = (channels / 8 + kCThreads - 1) / kCThreads;
+    const dim3 grid((unsigned)((int64_t)batch * groups));
+    auto *cp = (uint16_t *)conv_state;
+    const auto *xp = (const uint16_t *)x;
+    switch (conv_k) {
+        case 2:
+            hipLaunchKernelGGL(gdn_commit_conv_kernel<2>, grid, dim3(kCThreads), 0, stream, cp, xp, cu_nodes,
+                               accept_len, accept_idx, total_nodes, max_depth, channels, groups, err);
+            break;
+        case 3:
+            hipLaunchKernelGGL(gdn_commit_conv_kernel<3>, grid, dim3(kCThreads), 0, stream, cp, xp, cu_nodes,
+                               accept_len, accept_idx, total_nodes, max_depth, channels, groups, err);
+            break;
+        default:
+            hipLaunchKernelGGL(gdn_commit_conv_kernel<4>, grid, dim3(kCThreads), 0, stream, cp, xp, cu_nodes,
+                               accept_len, accept_idx, total_nodes, max_depth, channels, groups, err);
+            break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace tv

@@ -44,18 +44,6 @@ __device__ __forceinline__ void store_el<uint16_t>(uint16_t *p, double v) {
     *p = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// Request of node t: the b with cu_nodes[b] <= t < cu_nodes[b+1] (binary
-// search), or -1 when the offsets do not place t in any request.
-__device__ __forceinline__ int request_of(const int32_t *cu, int batch, int t) {
-    int lo = 0, hi = batch;  // invariant: cu[lo] <= t < cu[hi] when t is inside
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (cu[mid] <= t) lo = mid;
-        else hi = mid;
-    }
-    return (cu[lo] <= t && t < cu[lo + 1]) ? lo : -1;
-}
-
 // Work item w covers (row, pair): rows 0 .. T*hq-1 are query rows (node t =
 // row / hq), the next T*hkv rows are tree K rows (node t = row / hkv).
 template <typename T>

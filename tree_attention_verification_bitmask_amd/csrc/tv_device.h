@@ -24,6 +24,18 @@ __device__ __forceinline__ int request_nodes(const int32_t *cu_nodes, int b, int
     return hi - lo;
 }
 
+// Request of node t: the b with cu_nodes[b] <= t < cu_nodes[b+1] (binary
+// search), or -1 when the offsets do not place t in any request.
+__device__ __forceinline__ int request_of(const int32_t *cu, int batch, int t) {
+    int lo = 0, hi = batch;  // invariant: cu[lo] <= t < cu[hi] when t is inside
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cu[mid] <= t) lo = mid;
+        else hi = mid;
+    }
+    return (cu[lo] <= t && t < cu[lo + 1]) ? lo : -1;
+}
+
 // bf16 <-> fp32.  bf16 is stored as the upper half of an fp32 bit pattern.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

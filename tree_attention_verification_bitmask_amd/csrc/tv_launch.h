@@ -40,6 +40,19 @@ hipError_t launch_rollback_table(int32_t *table, int64_t stride, const int32_t *
                                  int batch, int total_nodes, int max_depth, int32_t *new_len, int32_t *freed,
                                  int32_t *n_freed, int32_t *err, hipStream_t stream);
 
+hipError_t launch_gdn_conv(const void *x, const void *conv_state, const void *weight, const int32_t *parent,
+                           const int32_t *cu_nodes, int batch, int total_nodes, int channels, int conv_k, void *y,
+                           int32_t *err, hipStream_t stream);
+hipError_t launch_gdn_verify(const void *q, const void *k, const void *v, int64_t row_stride, const float *g,
+                             const float *beta, const float *state, const int32_t *parent, const int32_t *cu_nodes,
+                             int batch, int total_nodes, int max_depth, int hk, int hv, float scale, int l2norm,
+                             float *out, int32_t *err, hipStream_t stream);
+hipError_t launch_gdn_commit(float *state, void *conv_state, const void *x, const void *k, const void *v,
+                             int64_t row_stride, const float *g, const float *beta, const int32_t *cu_nodes,
+                             const int32_t *accept_len, const int32_t *accept_idx, int batch, int total_nodes,
+                             int max_depth, int hk, int hv, int channels, int conv_k, int l2norm, int32_t *err,
+                             hipStream_t stream);
+
 // Problem description shared by the attention kernels.
 struct AttnArgs {
     const void *q, *k, *v;
