@@ -186,17 +186,22 @@ def algorithmic_work(wl):
     return byts, flops
 
 
+def blas_threads() -> int:
+    """Threads numpy's BLAS may use (the oracle's matrix routines)."""
+    try:
+        import threadpoolctl
+        blas = [p for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+        return int(max([p["num_threads"] for p in blas] or [1]))
+    except Exception:  # pragma: no cover
+        return 1
+
+
 def cpu_baseline(wl, budget_s: float = 15.0):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     mask, acceptance and compaction for the whole batch, and attention for as
     many whole nodes (all heads) as fit in about budget_s seconds."""
     from oracle import tree_verify_oracle as O
-    try:
-        import threadpoolctl
-        blas = [p for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
-        threads = max([p["num_threads"] for p in blas] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    threads = blas_threads()
     t0 = time.perf_counter()
     O.mask_build(wl.parent, wl.cu_nodes, wl.prefix_len, wl.max_nodes, wl.max_depth)
     alen, aidx, _ = O.accept_greedy(wl.parent, wl.draft, wl.target, wl.root_target, wl.cu_nodes, wl.max_depth)
@@ -244,6 +249,9 @@ def main(argv=None):
     ap.add_argument("--argmax-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--rope", action="store_true",
                     help="time tree_rope_apply and kv_rollback_token_table on the workload instead of the pass")
+    ap.add_argument("--gdn", action="store_true",
+                    help="time one Gated-DeltaNet layer's tree verification (conv, verify, commit) on the "
+                         "workload's trees instead of the pass")
     args = ap.parse_args(argv)
     if args.ingest_traffic:
         print(ingest_traffic(args.workload, args.ingest_traffic[0], args.ingest_traffic[1],
@@ -270,6 +278,8 @@ def main(argv=None):
         return bench_argmax(args, torch, BND, L, dev)
     if args.rope:
         return bench_rope(args, torch, BND, L, dev)
+    if args.gdn:
+        return bench_gdn(args, torch, BND, L, dev)
 
     if args.calib_copy_mib > 0:
         n_el = args.calib_copy_mib << 18  # float32 elements
@@ -638,6 +648,116 @@ def bench_rope(args, torch, BND, L, dev):
         "config": {"workload": f"{wl.name}: {W.CONFIGS[wl.name]['desc']}", "seed": wl.seed},
         "roofline": roof,
     }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def gdn_alg_bytes(T, B, hk, hv, d, C, K, D, n_acc):
+    """Algorithmic HBM bytes of the three calls: every input read once, every
+    output written once (bf16 activations, fp32 g/beta/state/outputs)."""
+    conv = T * C * 2 + B * (K - 1) * C * 2 + C * K * 2 + T * C * 2 + T * 4
+    verify = T * (2 * hk + hv) * d * 2 + 2 * T * hv * 4 + B * hv * d * d * 4 + T * hv * d * 4 + T * 4
+    commit = 2 * B * hv * d * d * 4 + n_acc * (hk + hv) * d * 2 + 2 * n_acc * hv * 4 \
+        + B * (K - 1) * C * 2 * 2 + n_acc * C * 2 + B * (1 + D) * 4
+    return conv, verify, commit
+
+
+def bench_gdn(args, torch, BND, L, dev):
+    """One step = one Gated-DeltaNet layer verifying the workload's draft
+    trees: tree_gdn_conv, tree_gdn_verify and tree_gdn_commit of the greedy
+    accepted path, for a 16 q/k-head, 32 v-head, 128-channel layer with a
+    width-4 convolution (8192 mixed channels).  Each call is timed with HIP
+    events.  The commit advances the state in place on every step (timing
+    only; its cost does not depend on the values)."""
+    import ctypes
+    from tree_attention_verification_bitmask_amd import workloads as Wm
+    wl = W.make_workload(args.workload, seed=args.seed, force_path=True)
+    lay = Wm.GDN_LAYER
+    hk, hv, d, K = lay["hk"], lay["hv"], lay["dk"], lay["conv_k"]
+    parents = [wl.parent[wl.cu_nodes[b]:wl.cu_nodes[b + 1]] for b in range(wl.batch)]
+    gi = Wm.gdn_inputs(np.random.default_rng(args.seed), parents, hk=hk, hv=hv, dk=d, dv=d, conv_k=K)
+    T, B, C = wl.total_nodes, wl.batch, gi.x.shape[1]
+    D = wl.max_depth
+    i32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(dev)  # noqa: E731
+    f32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)  # noqa: E731
+    bf = lambda x: f32(x).to(torch.bfloat16).contiguous()  # noqa: E731
+    parent, cu = i32(wl.parent), i32(wl.cu_nodes)
+    x, cs, w = bf(gi.x), bf(gi.conv_state), bf(gi.conv_w)
+    g, beta, state = f32(gi.g), f32(gi.beta), f32(gi.state)
+    y = torch.empty_like(x)
+    out = torch.empty((T, hv, d), dtype=torch.float32, device=dev)
+    alen, aidx, _, err = BND.tree_accept_greedy(parent, i32(wl.draft), i32(wl.target), i32(wl.root_target), cu, D)
+    torch.cuda.synchronize()
+    n_acc = int(alen.sum().item())
+    stream = torch.cuda.current_stream()
+    sp = C_void(stream.cuda_stream)
+    P_ = lambda t: C_void(t.data_ptr())  # noqa: E731
+    qv, kv, vv = BND.gdn_split(y, hk, hv)
+    rs = y.stride(0)
+    scale = d ** -0.5
+    conv_args = (P_(x), P_(cs), P_(w), P_(parent), P_(cu), B, T, C, K, P_(y), P_(err), sp)
+    ver_args = (P_(qv), P_(kv), P_(vv), rs, P_(g), P_(beta), P_(state), P_(parent), P_(cu), B, T, D, hk, hv, d,
+                ctypes.c_float(scale), 1, P_(out), P_(err), sp)
+    com_args = (P_(state), P_(cs), P_(x), P_(kv), P_(vv), rs, P_(g), P_(beta), P_(cu), P_(alen), P_(aidx), B, T, D,
+                hk, hv, d, C, K, 1, P_(err), sp)
+    calls = (("tree_gdn_conv", L.tree_gdn_conv, conv_args), ("tree_gdn_verify", L.tree_gdn_verify, ver_args),
+             ("tree_gdn_commit", L.tree_gdn_commit, com_args))
+    for _ in range(args.warmup):
+        for name, fn, a in calls:
+            if fn(*a):
+                raise RuntimeError(f"{name} rejected its arguments")
+    torch.cuda.synchronize()
+    if int(err.item()) != 0:
+        raise RuntimeError(f"device error word {int(err.item()):#x}")
+    K_ = args.steps
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    evs = [[ev() for _ in range(4)] for _ in range(K_)]
+    start, end = ev(), ev()
+    torch.cuda._sleep(1 << 22)
+    start.record(stream)
+    for i in range(K_):
+        evs[i][0].record(stream)
+        for j, (_, fn, a) in enumerate(calls):
+            fn(*a)
+            evs[i][j + 1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    per = {name: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K_)]) * 1e3)
+           for j, (name, _, _) in enumerate(calls)}
+    step_us = float(np.mean([evs[i][0].elapsed_time(evs[i][3]) for i in range(K_)]) * 1e3)
+    conv_b, ver_b, com_b = gdn_alg_bytes(T, B, hk, hv, d, C, K, D, n_acc)
+    us = per["tree_gdn_verify"]
+    roof = {"bound": "hbm", "achieved": ver_b / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "traffic": None, "traffic_detail": "not measured for this kernel", "kernel": "tree_gdn_verify",
+            "avg_us": us, "alg_bytes": ver_b,
+            "others": {n: {"avg_us": per[n], "alg_bytes": b_, "frac": b_ / (per[n] * 1e-6) / 1e9 / HBM_PEAK_GBS}
+                       for n, b_ in (("tree_gdn_conv", conv_b), ("tree_gdn_commit", com_b))}}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    line = {
+        "metric": "tree nodes verified per second through one Gated-DeltaNet layer (conv + verify + commit)",
+        "value": T / (step_us * 1e-6), "unit": "nodes/s", "n_gpus": 1, "steps": K_, "warmup": args.warmup,
+        "ms_per_step": start.elapsed_time(end) / K_, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{wl.name} trees ({W.CONFIGS[wl.name]['desc']}); Gated-DeltaNet layer "
+                               f"{hk} q/k heads, {hv} v heads, d {d}, conv {K}, {C} channels", "seed": wl.seed,
+                   "accepted_tokens": n_acc},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import tree_gdn_oracle as G
+        # the first n nodes of request 0 (a prefix of a tree is a tree)
+        n = int(wl.cu_nodes[1])
+        sub = np.array([0, n])
+        t0 = time.perf_counter()
+        yo = G.gdn_conv_tree(gi.x[:n], gi.conv_state[:1], gi.conv_w, wl.parent[:n], sub)
+        G.gdn_tree_verify(gi.q[:n], gi.k[:n], gi.v[:n], gi.g[:n], gi.beta[:n], gi.state[:1], wl.parent[:n], sub,
+                          scale, True)
+        dt = time.perf_counter() - t0
+        del yo
+        line["cpu_baseline"] = {"value": n / dt, "unit": "nodes/s", "cores": blas_threads(),
+                                "kind": "oracle",
+                                "sample": f"conv + verify of the first {n} nodes of request 0, all {hv} heads "
+                                          f"({dt:.2f} s)"}
     print(json.dumps(line), flush=True)
     return 0
 

@@ -3,18 +3,21 @@ against the oracle, through the C ABI: the per-node conv window, the
 per-node recurrent output, and the commit of the accepted path's state.
 
 Tolerances (derived from the arithmetic; the oracle is float64):
-  * conv output y is bf16, computed in float32 and rounded once: within one
-    bf16 ulp of the exact value, |err| <= 2^-7 |y| + 1e-6.
-  * verify output o is float32.  The dominant error is the committed state
-    entering the matrix products as a bf16 pair hi + lo (relative 2^-17 per
-    element): |S0 x| errs by <= 2^-17 sum_j |S0_ij| |x_j| ~ 1e-5 for unit x
-    and the state scale used here, carried along the node's path (<= 16
-    levels) with weights of magnitude <= 1, plus float32 rounding (~1e-6).
-    The check allows 2e-4 (1 + |o|), about 10x the worst case; a wrong
-    ancestor moves o by 1e-2 .. 1 (the negative control checks that).
-  * commit: float32 state, one fp32 step per accepted token; the oracle's
-    float64 replay differs by a few float32 ulps of the state entries:
-    |err| <= 1e-5 (1 + |S|).  The conv state is moved bit-exactly.
+  * conv output y is bf16, computed in float32 and rounded once to nearest:
+    within half a bf16 ulp of the exact value, |err| <= 2^-8 |y| (1 + 2^-10)
+    + 1e-7 (the float32 sum and SiLU add a few 2^-24).
+  * verify output o is float32.  The dominant term is the committed state
+    entering the bf16 matrix products as hi + lo: |S0 - hi - lo| <= 2^-18 |S0|
+    per element, so S0 x errs by <= 2^-18 |S0_i|_2 |x|_2, about 4.4e-6 for
+    unit x and the state scale used here (N(0, 0.1), 128 columns).  It enters
+    o through e^G S0 q^ and through each r_s weighted by z (|e^G| <= 1, the
+    weights summing to at most ~2 on these inputs): <= 1e-5.  Float32
+    rounding adds ~1e-6.  The check is |err| <= 1e-5 (1 + |o|); the observed
+    worst case is 7e-7, and a wrong ancestor moves o by 1e-2 .. 1 (the
+    negative control checks that).
+  * commit: the state stays float32, one step per accepted token with at most
+    three roundings per updated entry, over <= 16 steps here: |err| <=
+    3e-6 (1 + |S|) (observed 1e-7).  The conv state is moved bit-exactly.
 """
 import numpy as np
 import pytest
@@ -27,8 +30,8 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-O_REL = 2e-4
-S_REL = 1e-5
+O_REL = 1e-5
+S_REL = 3e-6
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -75,6 +78,8 @@ def run_verify(gi, scale, l2norm=True, parent=None, max_depth=None):
 
 
 def check_o(got, ref, what=""):
+    ratio = float((np.abs(got - ref) / (1.0 + np.abs(ref))).max()) if got.size else 0.0
+    print(f"[err] {what}: max |err| / (1 + |o|) = {ratio:.3e}", flush=True)
     bad = np.abs(got - ref) > O_REL * (1.0 + np.abs(ref))
     assert not bad.any(), (what, int(bad.sum()), float(np.abs(got - ref).max()))
 
@@ -111,8 +116,10 @@ def test_conv_parity(kind, K, hk, hv):
     torch.cuda.synchronize()
     got = y.float().cpu().numpy()
     ref = G.gdn_conv_tree(gi.x, gi.conv_state, gi.conv_w, gi.parent, gi.cu_nodes)
+    print(f"[err] conv: max |err| / (2^-8 |y| + 1e-7) = "
+          f"{float((np.abs(got - ref) / (2.0 ** -8 * np.abs(ref) + 1e-7)).max()):.3f}", flush=True)
     assert int(err.item()) == 0
-    bad = np.abs(got - ref) > 2.0 ** -7 * np.abs(ref) + 1e-6
+    bad = np.abs(got - ref) > 2.0 ** -8 * (1 + 2.0 ** -10) * np.abs(ref) + 1e-7
     assert not bad.any(), (int(bad.sum()), float(np.abs(got - ref).max()))
 
 
@@ -138,7 +145,11 @@ def test_verify_parity(kind, hk, hv, l2norm):
     announce(f"gdn verify {kind} hk={hk} hv={hv} l2norm={l2norm}")
     rng = np.random.default_rng(len(kind) * 7 + hk * 3 + hv)
     gi = W.gdn_inputs(rng, trees(kind, rng), hk=hk, hv=hv)
-    scale = 128 ** -0.5 if l2norm else 0.01
+    if not l2norm:
+        # the rule assumes |k| <= 1 (else I - beta k k^T amplifies): unit rows
+        gi.k = W.round_to_bf16(gi.k / np.linalg.norm(gi.k, axis=-1, keepdims=True))
+        gi.q = W.round_to_bf16(gi.q / np.linalg.norm(gi.q, axis=-1, keepdims=True))
+    scale = 128 ** -0.5
     got, err = run_verify(gi, scale, l2norm)
     assert err == 0
     ref = G.gdn_tree_verify(gi.q, gi.k, gi.v, gi.g, gi.beta, gi.state, gi.parent, gi.cu_nodes, scale, l2norm)
@@ -260,6 +271,7 @@ def test_commit_parity(kind, K):
     S_ref, cs_ref = G.gdn_commit(gi.state, gi.conv_state, gi.x, gi.k, gi.v, gi.g, gi.beta, gi.cu_nodes,
                                  alen, aidx)
     S = st.cpu().numpy()
+    print(f"[err] commit state: {float((np.abs(S - S_ref) / (1 + np.abs(S_ref))).max()):.3e}", flush=True)
     assert (np.abs(S - S_ref) <= S_REL * (1 + np.abs(S_ref))).all(), float(np.abs(S - S_ref).max())
     assert np.array_equal(cs.float().cpu().numpy(), cs_ref.astype(np.float32))
     for b in range(len(pars)):
@@ -329,7 +341,7 @@ def test_layer_step_pipeline():
     assert int(err.item()) == 0
     # the conv output of the new token: its window is the same either way
     y1h = y1.float().cpu().numpy()
-    assert (np.abs(y1h[0] - ye[48]) <= 2.0 ** -7 * np.abs(ye[48]) + 1e-6).all()
+    assert (np.abs(y1h[0] - ye[48]) <= 2.0 ** -8 * (1 + 2.0 ** -10) * np.abs(ye[48]) + 1e-7).all()
     # the layer output: the oracle on the extended tree, fed the device's own
     # bf16 conv outputs (so only the state path is compared)
     yall = np.concatenate([y.float().cpu().numpy(), y1h])

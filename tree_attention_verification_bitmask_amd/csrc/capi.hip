@@ -293,7 +293,10 @@ tv_status tree_gdn_commit(float *state, void *conv_state, const void *x, const v
     if ((st = check_gdn_heads(hk, hv, head_dim, max_depth, row_stride)) != TV_OK) return st;
     if ((st = check_gdn_conv(batch, channels, conv_k)) != TV_OK) return st;
     if (l2norm != 0 && l2norm != 1) return TV_ERR_SHAPE;
-    if ((int64_t)batch * hv > (1ll << 31) - 1) return TV_ERR_LIMIT;
+    // one launch: batch * hv * (128 / 32) state workgroups + batch * ceil(channels / 2048) conv workgroups
+    if ((int64_t)batch * hv * (TV_GDN_HEAD_DIM / 32) + (int64_t)batch * ((channels / 8 + 255) / 256) >
+        (1ll << 31) - 1)
+        return TV_ERR_LIMIT;
     if (!state || !conv_state || !cu_nodes || !accept_len || !accept_idx) return TV_ERR_NULL;
     if (total_nodes > 0 && (!x || !k || !v || !g || !beta)) return TV_ERR_NULL;
     if (!aligned(state, 16) || !aligned(conv_state, 16) || !aligned(x, 16)) return TV_ERR_ALIGN;
