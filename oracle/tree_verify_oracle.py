@@ -312,6 +312,43 @@ def target_argmax(logits) -> np.ndarray:
     return np.argmax(x, axis=1).astype(np.int32)
 
 
+def target_sample(logits, temperature: float, u) -> np.ndarray:
+    """The target's sampled choice at every node, for verification at
+    temperature T > 0 with a deterministic draft ([DT] section 4.1: the target
+    is sampled while the draft stays deterministic; with a point-mass draft
+    distribution, [TSD]'s min(1, p/q) rule accepts a child exactly when the
+    target's sample equals its token).  Row r's token is drawn from
+    softmax(logits[r] / T) by inverse transform with the caller's uniform
+    u[r] in [0, 1): with y = x * (1/T), M = max y and w = exp(y - M) (float64),
+    the token is the smallest index whose cumulative weight exceeds u * sum(w);
+    if rounding leaves none, the last index with w > 0.  Readings for
+    non-finite rows: a NaN gives the first NaN, else +inf the first +inf, and a
+    row of -inf gives index 0."""
+    x = np.asarray(logits, dtype=np.float64)
+    if x.shape[1] == 0:
+        raise ValueError("vocab must be at least 1")
+    inv_t = 1.0 / float(temperature)
+    out = np.zeros(x.shape[0], dtype=np.int32)
+    for r in range(x.shape[0]):
+        row = x[r]
+        if np.isnan(row).any():
+            out[r] = int(np.flatnonzero(np.isnan(row))[0])
+            continue
+        if np.isposinf(row).any():
+            out[r] = int(np.flatnonzero(np.isposinf(row))[0])
+            continue
+        y = row * inv_t
+        m = y.max()
+        if m == -np.inf:
+            out[r] = 0
+            continue
+        w = np.exp(y - m)
+        c = np.cumsum(w)
+        i = int(np.searchsorted(c, float(u[r]) * c[-1], side="right"))
+        out[r] = i if i < row.shape[0] else int(np.flatnonzero(w > 0)[-1])
+    return out
+
+
 # ---------------------------------------------------------------------------
 # O-rope: rotary embedding at tree position ids ([TSD] "Tree Positional
 # IDs": PosID(v) = PosID(root) + depth(v) is what RoPE sees)
