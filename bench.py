@@ -247,6 +247,10 @@ def main(argv=None):
     ap.add_argument("--argmax-rows", type=int, default=129)
     ap.add_argument("--argmax-vocab", type=int, default=151936)
     ap.add_argument("--argmax-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--sample", action="store_true",
+                    help="time tree_target_sample (the target's sampled choice per node, T > 0) on the "
+                         "--argmax-rows x --argmax-vocab logits instead of the pass")
+    ap.add_argument("--sample-temperature", type=float, default=1.0)
     ap.add_argument("--rope", action="store_true",
                     help="time tree_rope_apply and kv_rollback_token_table on the workload instead of the pass")
     ap.add_argument("--gdn", action="store_true",
@@ -276,6 +280,8 @@ def main(argv=None):
         return bench_select(args, torch, BND, L, dev)
     if args.argmax:
         return bench_argmax(args, torch, BND, L, dev)
+    if args.sample:
+        return bench_sample(args, torch, BND, L, dev)
     if args.rope:
         return bench_rope(args, torch, BND, L, dev)
     if args.gdn:
@@ -581,6 +587,83 @@ def bench_argmax(args, torch, BND, L, dev):
         dt = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": n / dt, "unit": "nodes/s", "cores": 1, "kind": "oracle",
                                 "sample": f"target_argmax on rows 0..{n - 1} of the same logits ({dt:.2f} s)"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_sample(args, torch, BND, L, dev):
+    """One step = one tree_target_sample call (chunk pass + pick pass) over
+    [rows, vocab] logits with one float64 uniform per row, rotated over enough
+    copies to keep the Infinity Cache cold.  value = node choices per second.
+    The roofline counts the logits read once plus the uniforms and tokens."""
+    rows, V = args.argmax_rows, args.argmax_vocab
+    bf = args.argmax_dtype == "bf16"
+    es = 2 if bf else 4
+    rng = np.random.default_rng(args.seed)
+    x = torch.from_numpy(rng.normal(0, 3, (rows, V)).astype(np.float32)).to(dev)
+    if bf:
+        x = x.to(torch.bfloat16)
+    set_bytes = rows * V * es
+    R = max(2, math.ceil(COLD_BYTES / set_bytes))
+    sets = [x.clone() for _ in range(R)]
+    del x
+    u = torch.from_numpy(rng.random(rows)).to(dev)
+    tok = torch.empty(rows, dtype=torch.int32, device=dev)
+    ws_bytes = int(L.tree_target_sample_workspace_size(rows, V))
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = C_void(stream.cuda_stream)
+    code = BND.TV_BF16 if bf else BND.TV_F32
+    temp = float(np.float32(args.sample_temperature))
+    call_args = [(C_void(t.data_ptr()), rows, V, code, temp, C_void(u.data_ptr()), C_void(tok.data_ptr()),
+                  C_void(ws.data_ptr()), ws_bytes, sp) for t in sets]
+    for i in range(args.warmup):
+        if L.tree_target_sample(*call_args[i % R]):
+            raise RuntimeError("tree_target_sample rejected its arguments")
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1 << 24)
+    start.record(stream)
+    for i in range(K):
+        evs[i][0].record(stream)
+        L.tree_target_sample(*call_args[(args.warmup + i) % R])
+        evs[i][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    call_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    us = float(call_ms.mean() * 1e3)
+    byts = rows * V * es + rows * (8 + 4)
+    roof = {"bound": "hbm", "achieved": byts / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "traffic": None, "traffic_detail": "not measured for this kernel",
+            "kernel": "tree_target_sample", "avg_us": us,
+            "p10_us": float(np.percentile(call_ms, 10) * 1e3), "p90_us": float(np.percentile(call_ms, 90) * 1e3),
+            "alg_bytes": byts, "fp64_exp_per_s": rows * V / (us * 1e-6)}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    line = {
+        "metric": "node sampled target choices per second (tree_target_sample)",
+        "value": rows / (us * 1e-6),
+        "unit": "nodes/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": start.elapsed_time(end) / K,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.argmax_dtype + "->f64",
+        "data": "synthetic",
+        "config": {"workload": f"logits {rows} x {V} {args.argmax_dtype}, T {temp}", "seed": args.seed,
+                   "cold_cache_sets": R},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import tree_verify_oracle as O
+        xs = sets[0].float().cpu().numpy()
+        uh = u.cpu().numpy()
+        t0 = time.perf_counter()
+        n = 0
+        while n < rows and time.perf_counter() - t0 < args.cpu_budget:
+            O.target_sample(xs[n:n + 16], temp, uh[n:n + 16])
+            n = min(rows, n + 16)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": n / dt, "unit": "nodes/s", "cores": 1, "kind": "oracle",
+                                "sample": f"target_sample on rows 0..{n - 1} of the same logits ({dt:.2f} s)"}
     print(json.dumps(line), flush=True)
     return 0
 

@@ -60,7 +60,7 @@ typedef enum {
     TV_ERR_SHAPE = 2,     /* inconsistent or negative sizes (e.g. hq % hkv != 0)      */
     TV_ERR_DTYPE = 3,     /* unsupported dtype / head_dim                             */
     TV_ERR_LIMIT = 4,     /* a size above a library limit (TV_MAX_*)                  */
-    TV_ERR_WORKSPACE = 5, /* workspace smaller than tree_attn_verify_workspace_size() */
+    TV_ERR_WORKSPACE = 5, /* workspace smaller than the call's *_workspace_size()      */
     TV_ERR_LAUNCH = 6,    /* the HIP runtime refused a launch                         */
     TV_ERR_ALIGN = 7      /* a pointer breaks the stated alignment                    */
 } tv_status;
@@ -266,6 +266,41 @@ tv_status tree_select_topb(const float *score, const int32_t *parent, const int3
  */
 tv_status tree_target_argmax(const void *logits, int32_t rows, int32_t vocab, tv_dtype dtype,
                              int32_t *token, void *stream);
+
+/*
+ * tree_target_sample -- the target's sampled choice at every node (T > 0).
+ *
+ * Defines: [DT] section 4.1: at temperature T > 0 the target token at each
+ * node is sampled from the target's distribution while the draft stays
+ * deterministic; [TSD] "Verification and Acceptance Algorithms", stochastic
+ * verification: with such a (point-mass) draft the min(1, p/q) test accepts a
+ * child exactly when the target's sample equals its token, so these tokens are
+ * the target_tokens (and root_target) of tree_accept_greedy at T > 0.
+ * Row r's token is drawn from softmax(logits[r] / temperature) by inverse
+ * transform with the caller's uniform u[r]: with y = x / T, M = max y and
+ * w_i = exp(y_i - M), the token is the smallest i with
+ * w_0 + ... + w_i > u[r] * (w_0 + ... + w_{vocab-1}), all in float64.
+ * Readings: if rounding leaves no such i (or u[r] is not in [0, 1)), the last
+ * index with w_i > 0; a row holding NaN gives its first NaN, else a row
+ * holding +inf its first +inf; a row of -inf gives 0.  The uniforms are an
+ * input, so the call is deterministic; the summation order differs from a
+ * sequential sum only by rounding.
+ *
+ * In:  logits [rows, vocab] in dtype (fp32 or bf16), row-major, 16-byte
+ *      aligned; u [rows] float64 (8-byte aligned), the caller's uniforms.
+ *      0 < temperature < inf.  0 <= rows <= TV_MAX_TOTAL_NODES,
+ *      1 <= vocab <= TV_MAX_VOCAB, rows * ceil(vocab / 2048) < 2^31.
+ * Out: token [rows] int32.
+ * Workspace: caller-owned device memory of at least
+ *      tree_target_sample_workspace_size(rows, vocab) bytes (24 bytes per
+ *      2048 logits), 8-byte aligned; overwritten, no contents required.
+ * Errors (host, before any launch): SHAPE (negative sizes, temperature not in
+ *      (0, inf)), LIMIT, DTYPE, NULL, ALIGN, WORKSPACE.  No device-side errors.
+ */
+size_t tree_target_sample_workspace_size(int32_t rows, int32_t vocab);
+tv_status tree_target_sample(const void *logits, int32_t rows, int32_t vocab, tv_dtype dtype,
+                             float temperature, const double *u, int32_t *token, void *workspace,
+                             size_t workspace_bytes, void *stream);
 
 /*
  * tree_rope_apply -- rotary position embedding at the tree's position ids.

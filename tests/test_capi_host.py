@@ -189,6 +189,34 @@ def test_argmax_host_checks(L):
     assert am(rows=0, logits=None, tok=None) == OK
 
 
+def test_sample_host_checks(L):
+    ws_need = L.tree_target_sample_workspace_size(4, 100)
+    assert ws_need == 4 * 1 * 24                                   # 24 bytes per 2048-logit chunk
+    assert L.tree_target_sample_workspace_size(3, 2049) == 3 * 2 * 24
+    assert L.tree_target_sample_workspace_size(-1, 5) == 0
+
+    def sm(logits=FAKE, rows=4, vocab=100, dt=1, T=1.0, u=FAKE, tok=FAKE, ws=FAKE, wsb=ws_need):
+        return L.tree_target_sample(logits, rows, vocab, dt, T, u, tok, ws, wsb, None)
+    assert sm(rows=-1) == SHAPE
+    assert sm(vocab=0) == SHAPE
+    assert sm(T=0.0) == SHAPE
+    assert sm(T=-1.0) == SHAPE
+    assert sm(T=float("inf")) == SHAPE
+    assert sm(T=float("nan")) == SHAPE
+    assert sm(vocab=16777217) == LIMIT
+    assert sm(rows=16777216) == LIMIT
+    assert sm(rows=262144, vocab=16777216, wsb=1 << 44) == LIMIT  # 2^31 chunk workgroups
+    assert sm(dt=7) == DTYPE
+    assert sm(tok=None) == NULL
+    assert sm(u=None) == NULL
+    assert sm(ws=None) == NULL
+    assert sm(logits=None) == NULL
+    assert sm(logits=FAKE_ODD) == ALIGN
+    assert sm(u=FAKE_ODD) == ALIGN
+    assert sm(wsb=ws_need - 1) == WS
+    assert sm(rows=0, logits=None, u=None, tok=None, ws=None, wsb=0) == OK
+
+
 def test_rope_and_rollback_host_checks(L):
     rope = lambda q=FAKE, k=FAKE, pos=FAKE, cu=FAKE, ks=FAKE, P=FAKE, B=1, T=16, rows=100, hq=8, hkv=2, d=128, \
         base=1e6, dt=1: L.tree_rope_apply(q, k, pos, cu, ks, P, B, T, rows, hq, hkv, d, base, dt, None, None)

@@ -62,6 +62,10 @@ def lib() -> C.CDLL:
     L.tree_select_topb.restype = C.c_int
     L.tree_target_argmax.argtypes = [vp, i32, i32, C.c_int, vp, vp]
     L.tree_target_argmax.restype = C.c_int
+    L.tree_target_sample_workspace_size.argtypes = [i32, i32]
+    L.tree_target_sample_workspace_size.restype = sz
+    L.tree_target_sample.argtypes = [vp, i32, i32, C.c_int, f32, vp, vp, vp, sz, vp]
+    L.tree_target_sample.restype = C.c_int
     L.tree_rope_apply.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32, C.c_int, vp, vp]
     L.tree_rope_apply.restype = C.c_int
     L.kv_rollback_token_table.argtypes = [vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp]
@@ -269,6 +273,32 @@ def tree_target_argmax(logits, token=None, stream=None):
     _need(token, "token", torch.int32, rows)
     _check("tree_target_argmax", lib().tree_target_argmax(_ptr(logits), rows, vocab, code, _ptr(token),
                                                           _stream(stream)))
+    return token
+
+
+def tree_target_sample_workspace_size(rows: int, vocab: int) -> int:
+    return int(lib().tree_target_sample_workspace_size(rows, vocab))
+
+
+def tree_target_sample(logits, temperature: float, u, token=None, workspace=None, stream=None):
+    """logits [rows, vocab] (float32 or bfloat16), u [rows] float64 uniforms
+    -> token int32 [rows]: the inverse-transform sample of
+    softmax(logits / temperature) at u."""
+    import torch
+    if logits.dim() != 2:
+        raise ValueError("logits must be [rows, vocab]")
+    rows, vocab = logits.shape
+    code = _dtype_code(logits)
+    _need(logits, "logits")
+    _need(u, "u", torch.float64, rows)
+    token = torch.empty(rows, dtype=torch.int32, device=logits.device) if token is None else token
+    _need(token, "token", torch.int32, rows)
+    ws_bytes = tree_target_sample_workspace_size(rows, vocab)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=logits.device)
+    _check("tree_target_sample", lib().tree_target_sample(
+        _ptr(logits), rows, vocab, code, float(temperature), _ptr(u), _ptr(token), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
     return token
 
 

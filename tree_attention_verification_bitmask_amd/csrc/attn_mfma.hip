@@ -646,7 +646,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
         // Partial of this slice: O / l rounded to bf16 (a convex combination of
         // V rows, so bf16 keeps its range) plus the fp32 (m, l).  Lane-native
         // layout [tile][split][wave][DB*4 x 4 bf16][64 lanes].  A row that sees
-        // no key of the slice has l = 0 and stores zeros.
+        // no key of the slice has l = 0 and stores zeros.  The stores are
+        // relaxed atomics at agent scope, which write through this XCD's L2:
+        // the merge kernel reads them from another XCD anyway, and the end of
+        // this kernel then has no dirty partials left to write back
+        // (measured: 1.5 us less per call at 240 workgroups).
         const int tile = (b * p.hkv + g) * p.row_tiles + rt;
         const int64_t unit = ((int64_t)tile * p.splits + s) * kWaves + wave;
         uint2 *po = p.ws_o + unit * (DB * 4 * 64) + lane;
@@ -654,10 +658,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4)
-                po[(db * 4 + i4) * 64] = make_uint2(pack_bf16x2(oacc[db][4 * i4 + 0] * inv, oacc[db][4 * i4 + 1] * inv),
-                                                    pack_bf16x2(oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv));
-        if (half == 0) p.ws_ml[unit * 32 + col] = make_float2(m_run, l_run);
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const uint64_t w =
+                    (uint64_t)pack_bf16x2(oacc[db][4 * i4 + 0] * inv, oacc[db][4 * i4 + 1] * inv) |
+                    ((uint64_t)pack_bf16x2(oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv) << 32);
+                __hip_atomic_store(reinterpret_cast<uint64_t *>(po + (db * 4 + i4) * 64), w, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+        if (half == 0) {
+            const uint64_t w = (uint64_t)__float_as_uint(m_run) | ((uint64_t)__float_as_uint(l_run) << 32);
+            __hip_atomic_store(reinterpret_cast<uint64_t *>(p.ws_ml + unit * 32 + col), w, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 

@@ -2,6 +2,7 @@
 // kernels.  Every check runs before any HIP runtime call, so a rejected call
 // enqueues nothing (and the checks can be exercised on a machine without a
 // GPU).  The definitions each call implements are cited in treeverify.h.
+#include <math.h>
 #include <stdint.h>
 
 #include "treeverify.h"
@@ -209,6 +210,28 @@ tv_status tree_target_argmax(const void *logits, int32_t rows, int32_t vocab, tv
     if (!aligned(logits, 16)) return TV_ERR_ALIGN;
     if (rows == 0) return TV_OK;
     return launch_status(tv::launch_target_argmax(logits, rows, vocab, dtype, token, (hipStream_t)stream));
+}
+
+size_t tree_target_sample_workspace_size(int32_t rows, int32_t vocab) {
+    if (rows < 0 || vocab < 1) return 0;
+    return tv::target_sample_workspace(rows, vocab);
+}
+
+tv_status tree_target_sample(const void *logits, int32_t rows, int32_t vocab, tv_dtype dtype, float temperature,
+                             const double *u, int32_t *token, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    if (rows < 0 || vocab < 1) return TV_ERR_SHAPE;
+    if (!(temperature > 0.f) || !(temperature < INFINITY)) return TV_ERR_SHAPE;
+    if (rows > TV_MAX_TOTAL_NODES || vocab > TV_MAX_VOCAB) return TV_ERR_LIMIT;
+    if (tv::target_sample_blocks(rows, vocab) > INT32_MAX) return TV_ERR_LIMIT;
+    if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_DTYPE;
+    if (rows > 0 && (!logits || !u || !token || !workspace)) return TV_ERR_NULL;
+    if (!aligned(logits, 16) || !aligned(u, 8) || !aligned(workspace, 8)) return TV_ERR_ALIGN;
+    if (workspace_bytes < tv::target_sample_workspace(rows, vocab)) return TV_ERR_WORKSPACE;
+    if (rows == 0) return TV_OK;
+    const double inv_t = 1.0 / (double)temperature;
+    return launch_status(tv::launch_target_sample(logits, rows, vocab, dtype, inv_t, u, token, workspace,
+                                                  (hipStream_t)stream));
 }
 
 tv_status tree_rope_apply(void *q, void *k_cache, const int32_t *pos_ids, const int32_t *cu_nodes,

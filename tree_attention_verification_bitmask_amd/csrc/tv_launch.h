@@ -31,6 +31,10 @@ hipError_t launch_select_topb(const float *score, const int32_t *parent, const i
 
 hipError_t launch_target_argmax(const void *logits, int rows, int vocab, tv_dtype dtype, int32_t *token,
                                 hipStream_t stream);
+size_t target_sample_workspace(int rows, int vocab);
+int64_t target_sample_blocks(int rows, int vocab);
+hipError_t launch_target_sample(const void *logits, int rows, int vocab, tv_dtype dtype, double inv_t,
+                                const double *u, int32_t *token, void *workspace, hipStream_t stream);
 
 hipError_t launch_tree_rope(void *q, void *k, const int32_t *pos, const int32_t *cu_nodes, const int32_t *kv_start,
                             const int32_t *prefix_len, int batch, int total_nodes, int64_t kv_rows, int hq, int hkv,
