@@ -678,8 +678,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
 // M = max_s m_s.  One wavefront per (tile, row group, 32-channel block, float4
 // slot i4), four per workgroup; lane layout as the partials (lane half h holds
 // channels 32 db + 8 i4 + 4 h .. +3 of row col).  The slices are taken in
-// batches of kCombineBatch whose loads are all issued before any is used, so a
-// batch costs one memory round trip.
+// batches of up to kCombineBatch whose loads are all issued before any is
+// used, so a batch costs one memory round trip; a batch loads only the slices
+// that exist.
 constexpr int kCombineWaves = 4;
 constexpr int kCombineBatch = 16;
 template <int D>
@@ -718,18 +719,19 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
     float M = -INFINITY, L = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s0 = 0; s0 < nsplit; s0 += kCombineBatch) {
+        const int nb = min(kCombineBatch, nsplit - s0);  // wave-uniform
         float2 m_l[kCombineBatch];
         uint2 o[kCombineBatch];
 #pragma unroll
         for (int u = 0; u < kCombineBatch; ++u) {
-            const int sidx = min(s0 + u, nsplit - 1);  // (clamped: past the end repeats a valid slice)
-            m_l[u] = ml[sidx * kMlStride];
-            o[u] = po[sidx * kOStride];
+            // slices past the end issue no load (a uniform branch)
+            m_l[u] = u < nb ? ml[(s0 + u) * kMlStride] : make_float2(-INFINITY, 0.f);
+            o[u] = u < nb ? po[(s0 + u) * kOStride] : make_uint2(0u, 0u);
         }
         float mb = M;
 #pragma unroll
         for (int u = 0; u < kCombineBatch; ++u)
-            if (s0 + u < nsplit) mb = fmaxf(mb, m_l[u].x);
+            if (u < nb) mb = fmaxf(mb, m_l[u].x);
         const float mref = (mb == -INFINITY) ? 0.f : mb;
         const float a = __builtin_amdgcn_exp2f((M - mref) * p.c);  // 0 when M = -inf
         L *= a;
@@ -740,7 +742,7 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
 #pragma unroll
         for (int u = 0; u < kCombineBatch; ++u) {
             // slice weight times its sum: the partial holds O / l
-            const float wl = (s0 + u < nsplit) ? __builtin_amdgcn_exp2f((m_l[u].x - mref) * p.c) * m_l[u].y : 0.f;
+            const float wl = (u < nb) ? __builtin_amdgcn_exp2f((m_l[u].x - mref) * p.c) * m_l[u].y : 0.f;
             L += wl;
             acc.x = fmaf(wl, bf16_lo(o[u].x), acc.x);
             acc.y = fmaf(wl, bf16_hi(o[u].x), acc.y);
