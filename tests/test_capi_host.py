@@ -78,6 +78,8 @@ def test_attn_host_checks(L):
     assert attn(L, d=96) == DTYPE
     assert attn(L, dtype=7) == DTYPE
     assert attn(L, max_nodes=2048) == LIMIT
+    # MFMA grid or merge waves past int range (65535 requests x 1024 KV heads)
+    assert attn(L, B=65535, T=65535 * 8, max_nodes=8, hq=4096, hkv=1024) == LIMIT
     assert attn(L, q=FAKE_ODD) == ALIGN
     assert attn(L, out=FAKE_ODD) == ALIGN
     need = L.tree_attn_verify_workspace_size(1, 128, 128, 4096, 32, 8, 128, 1)

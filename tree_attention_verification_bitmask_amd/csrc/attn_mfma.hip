@@ -61,9 +61,10 @@
 // fp32 reference m and sum l) and attn_combine_kernel merges them.
 //
 // XCD-aware order.  Workgroup ids are dealt round-robin to the 8 XCDs; the
-// kernel maps id -> task so that each XCD gets a contiguous block of tasks,
-// ordered with the row tiles of one (request, KV head, slice) adjacent, so the
-// tiles that read the same K/V run on one XCD and share its L2.
+// kernel maps id -> task so that the row tiles of one (slice, request, KV
+// head), which read the same K/V, run on one XCD and share its L2, while the
+// groups themselves are dealt round-robin over the XCDs, KV head fastest, so
+// that ragged requests load every XCD alike (see decode_task).
 #include "tv_device.h"
 #include "tv_launch.h"
 
@@ -229,20 +230,28 @@ __device__ __forceinline__ uint32_t visible16(lds_u64_t *arow, int words, int ke
 }
 
 // Task of workgroup `wid`: (request, KV head, key slice, row tile), XCD-aware.
+// A group is the row tiles of one (slice, request, KV head); they read the
+// same K/V, so a group stays on one XCD and its tiles take adjacent slots
+// there.  Groups are numbered q = (s * batch + b) * hkv + g and dealt
+// round-robin to the XCDs (XCD = q mod 8, the hardware's order of workgroup
+// ids), so every XCD holds every request's slices in nearly equal shares:
+// with 8 KV heads each XCD gets one head of every (slice, request), the same
+// work on all eight.  Within an XCD the groups come slice by slice, the full
+// first slices before the shorter last ones.
 struct Task {
     int b, g, s, rt;
 };
 __device__ __forceinline__ bool decode_task(const KParams &p, int wid, Task *t) {
-    const int ntasks = p.batch * p.hkv * p.splits * p.row_tiles;
-    const int per_xcd = (ntasks + kXcds - 1) / kXcds;
-    const int task = (wid % kXcds) * per_xcd + wid / kXcds;
-    if (task >= ntasks) return false;
-    t->rt = task % p.row_tiles;
-    int rest = task / p.row_tiles;
-    t->s = rest % p.splits;
-    rest /= p.splits;
-    t->g = rest % p.hkv;
-    t->b = rest / p.hkv;
+    const int ngroups = p.batch * p.hkv * p.splits;
+    const int x = wid % kXcds;       // XCD
+    const int k = wid / kXcds;       // slot on that XCD
+    const int q = x + kXcds * (k / p.row_tiles);
+    if (q >= ngroups) return false;
+    t->rt = k % p.row_tiles;
+    t->g = q % p.hkv;
+    const int rest = q / p.hkv;
+    t->b = rest % p.batch;
+    t->s = rest / p.batch;
     return true;
 }
 
@@ -835,8 +844,8 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *works
         p.ws_o = (uint2 *)workspace;
         p.ws_ml = (float2 *)((char *)workspace + off);
     }
-    const long ntasks = (long)a.batch * a.hkv * plan.splits * plan.row_tiles;
-    const long grid = ((ntasks + kXcds - 1) / kXcds) * kXcds;
+    const long ngroups = (long)a.batch * a.hkv * plan.splits;
+    const long grid = ((ngroups + kXcds - 1) / kXcds) * plan.row_tiles * kXcds;
     const long tiles = (long)a.batch * a.hkv * plan.row_tiles;
     const long cwaves = tiles * kWaves * (a.head_dim / 32) * 4;
     const long cblocks = (cwaves + kCombineWaves - 1) / kCombineWaves;

@@ -117,6 +117,13 @@ tv_status tree_attn_verify(const void *q, const void *k_cache, const void *v_cac
         return TV_ERR_ALIGN;
     const tv::MfmaPlan plan =
         tv::plan_attn_mfma(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype);
+    if (plan.use) {
+        // workgroup and merge-wave indices are int on the device
+        const int64_t groups = (int64_t)batch * hkv * plan.splits;
+        const int64_t grid = (groups + 7) / 8 * plan.row_tiles * 8;
+        const int64_t merge_waves = (int64_t)batch * hkv * plan.row_tiles * 8 * (head_dim / 32) * 4;
+        if (grid > INT32_MAX || merge_waves > INT32_MAX) return TV_ERR_LIMIT;
+    }
     if (plan.use && plan.ws_bytes > 0) {
         if (!workspace || workspace_bytes < plan.ws_bytes) return TV_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return TV_ERR_ALIGN;
