@@ -247,7 +247,15 @@ __device__ __forceinline__ bool decode_task(const KParams &p, int wid, Task *t) 
     const int k = wid / kXcds;       // slot on that XCD
     const int q = x + kXcds * (k / p.row_tiles);
     if (q >= ngroups) return false;
-    t->rt = k % p.row_tiles;
+    // Within an XCD the slots go round-robin to its 4 shader engines (8 CUs
+    // each) and are dispatched in order, so with 2 or 4 tiles per group the
+    // slot number alone would fix the tile each engine gets: the engines given
+    // the always-busy first tiles would queue while the others idle on the
+    // often-empty last tiles of short requests.  For batches the tile order
+    // is rotated by the slot's row of 4, so every engine sees every tile
+    // position (one request has no empty tiles and keeps the plain order).
+    const int i = k % p.row_tiles;
+    t->rt = (p.batch > 1 && 4 % p.row_tiles == 0) ? (i + k / 4) % p.row_tiles : i;
     t->g = q % p.hkv;
     const int rest = q / p.hkv;
     t->b = rest % p.batch;
@@ -792,10 +800,11 @@ MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefi
     const int span = max_prefix + max_nodes;  // longest key axis
     const int chunks = (span + kChunk - 1) / kChunk;
     const long base_tasks = (long)batch * hkv * plan.row_tiles;
-    // Fill the chip: one workgroup per CU (256 CUs) for a single request; two
-    // rounds for several (ragged) requests, so short ones leave room to
-    // balance.  A tuning override (TV_MFMA_SPLITS) may fix the count instead.
-    const long target = batch == 1 ? 256 : 512;
+    // Fill the chip: one workgroup per CU (256 CUs) for a single request;
+    // about two and a half rounds for several (ragged) requests, so short
+    // ones leave room to balance.  A tuning override (TV_MFMA_SPLITS) may fix
+    // the count instead.
+    const long target = batch == 1 ? 256 : 640;
     int splits = (int)((target + base_tasks - 1) / base_tasks);
     splits = env_int("TV_MFMA_SPLITS", splits);
     if (splits < 1) splits = 1;
