@@ -201,6 +201,28 @@ struct KParams {
     int32_t *err;
 };
 
+// Sizes of request b, with all four reads issued before any test: a chain of
+// tests would make each read wait for the one before (one memory round trip
+// each).  ok is false when they disagree with the host's sizes.
+struct Req {
+    int lo, n, P;
+    int64_t ks;
+    bool ok;
+};
+__device__ __forceinline__ Req load_request(const KParams &p, int b) {
+    Req r;
+    const int c0 = p.cu_nodes[b];
+    const int c1 = p.cu_nodes[b + 1];
+    r.P = p.prefix_len[b];
+    r.ks = p.kv_start[b];
+    r.lo = c0;
+    r.n = c1 - c0;
+    const bool bad = (c0 < 0) | (c1 < c0) | (c1 > p.total_nodes) | (r.n > p.max_nodes) | (r.P < 0) |
+                     (r.P > p.max_prefix) | (r.ks < 0) | (r.ks + r.P + r.n > p.kv_rows);
+    r.ok = !bad;
+    return r;
+}
+
 // Bits e = 0..15 set iff key (key0 + e) is visible to the node whose packed
 // ancestor row (in LDS) is `arow`: prefix keys (< P) always, tree key P + j iff
 // bit j, nothing at or past `key_hi`.
@@ -274,11 +296,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
     if (!decode_task(p, blockIdx.x, &tk)) return;
     const int b = tk.b, g = tk.g, s = tk.s, rt = tk.rt;
 
-    int lo;
-    const int n_nodes = request_nodes(p.cu_nodes, b, p.total_nodes, p.max_nodes, &lo);
-    const int P = p.prefix_len[b];
-    const int64_t ks = p.kv_start[b];
-    if (n_nodes < 0 || P < 0 || P > p.max_prefix || ks < 0 || ks + P + n_nodes > p.kv_rows) {
+    const Req rq = load_request(p, b);
+    const int lo = rq.lo, n_nodes = rq.n, P = rq.P;
+    const int64_t ks = rq.ks;
+    if (!rq.ok) {
         if (g == 0 && rt == 0 && s == 0 && threadIdx.x == 0) report(p.err, TV_DEVERR_BAD_REQUEST, b);
         return;
     }
@@ -703,7 +724,9 @@ constexpr int kCombineBatch = 16;
 template <int D>
 __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParams p) {
     constexpr int DB = Geo<D>::kDB;
-    const int gw = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
+    // (wave-uniform: the request's sizes then come by scalar loads, which
+    // complete independently of the partials' vector loads)
+    const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * kCombineWaves + (threadIdx.x >> 6));
     const int i4 = gw & 3;
     const int db = (gw >> 2) % DB;
     const int rg = (gw / (4 * DB)) % kWaves;
@@ -714,11 +737,29 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
     const int rt = tile % p.row_tiles;
     const int g = (tile / p.row_tiles) % p.hkv;
     const int b = tile / (p.row_tiles * p.hkv);
-    int lo;
-    const int n = request_nodes(p.cu_nodes, b, p.total_nodes, p.max_nodes, &lo);
-    const int P = p.prefix_len[b];
-    const int64_t ks = p.kv_start[b];
-    if (n < 0 || P < 0 || P > p.max_prefix || ks < 0 || ks + P + n > p.kv_rows) return;
+
+    // The partials' addresses depend only on (tile, slice, lane), so the first
+    // batch is loaded before the request's sizes arrive: the two memory round
+    // trips overlap.  Slices the request does not have were never written and
+    // hold arbitrary bits; they are skipped by branches below, never scaled by
+    // zero (0 * NaN would poison the sum).
+    const int64_t base = (int64_t)tile * p.splits;
+    const float2 *ml = p.ws_ml + (base * kWaves + rg) * 32 + col;
+    const uint2 *po = p.ws_o + (base * kWaves + rg) * (DB * 4 * 64) + (db * 4 + i4) * 64 + lane;
+    constexpr int64_t kMlStride = kWaves * 32;                    // per slice
+    constexpr int64_t kOStride = (int64_t)kWaves * DB * 4 * 64;   // per slice
+    float2 m_l[kCombineBatch];
+    uint2 o[kCombineBatch];
+    const int nb0 = min(kCombineBatch, p.splits);  // wave-uniform
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+        m_l[u] = u < nb0 ? ml[u * kMlStride] : make_float2(-INFINITY, 0.f);
+        o[u] = u < nb0 ? po[u * kOStride] : make_uint2(0u, 0u);
+    }
+
+    const Req rq = load_request(p, b);
+    if (!rq.ok) return;
+    const int lo = rq.lo, n = rq.n, P = rq.P;
     const int G = p.hq / p.hkv;
     const int rows_b = n * G;
     const int row0 = rt * kTileRows;
@@ -728,22 +769,19 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
     const int nsplit = min(p.splits, (key_end + p.keys_per_split - 1) / p.keys_per_split);
     const int r = row0 + rg * 32 + col;
 
-    const int64_t base = (int64_t)tile * p.splits;
-    const float2 *ml = p.ws_ml + (base * kWaves + rg) * 32 + col;
-    const uint2 *po = p.ws_o + (base * kWaves + rg) * (DB * 4 * 64) + (db * 4 + i4) * 64 + lane;
-    constexpr int64_t kMlStride = kWaves * 32;                    // per slice
-    constexpr int64_t kOStride = (int64_t)kWaves * DB * 4 * 64;   // per slice
     float M = -INFINITY, L = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s0 = 0; s0 < nsplit; s0 += kCombineBatch) {
         const int nb = min(kCombineBatch, nsplit - s0);  // wave-uniform
-        float2 m_l[kCombineBatch];
-        uint2 o[kCombineBatch];
+        if (s0 > 0) {
 #pragma unroll
-        for (int u = 0; u < kCombineBatch; ++u) {
-            // slices past the end issue no load (a uniform branch)
-            m_l[u] = u < nb ? ml[(s0 + u) * kMlStride] : make_float2(-INFINITY, 0.f);
-            o[u] = u < nb ? po[(s0 + u) * kOStride] : make_uint2(0u, 0u);
+            for (int u = 0; u < kCombineBatch; ++u) {
+                // slices past the end issue no load (a uniform branch)
+                if (u < nb) {
+                    m_l[u] = ml[(s0 + u) * kMlStride];
+                    o[u] = po[(s0 + u) * kOStride];
+                }
+            }
         }
         float mb = M;
 #pragma unroll
@@ -758,13 +796,15 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
         acc.w *= a;
 #pragma unroll
         for (int u = 0; u < kCombineBatch; ++u) {
-            // slice weight times its sum: the partial holds O / l
-            const float wl = (u < nb) ? __builtin_amdgcn_exp2f((m_l[u].x - mref) * p.c) * m_l[u].y : 0.f;
-            L += wl;
-            acc.x = fmaf(wl, bf16_lo(o[u].x), acc.x);
-            acc.y = fmaf(wl, bf16_hi(o[u].x), acc.y);
-            acc.z = fmaf(wl, bf16_lo(o[u].y), acc.z);
-            acc.w = fmaf(wl, bf16_hi(o[u].y), acc.w);
+            if (u < nb) {
+                // slice weight times its sum: the partial holds O / l
+                const float wl = __builtin_amdgcn_exp2f((m_l[u].x - mref) * p.c) * m_l[u].y;
+                L += wl;
+                acc.x = fmaf(wl, bf16_lo(o[u].x), acc.x);
+                acc.y = fmaf(wl, bf16_hi(o[u].x), acc.y);
+                acc.z = fmaf(wl, bf16_lo(o[u].y), acc.z);
+                acc.w = fmaf(wl, bf16_hi(o[u].y), acc.w);
+            }
         }
         M = mb;
     }
