@@ -71,6 +71,7 @@ __global__ void __launch_bounds__(64) accept_greedy_kernel(
     int lo;
     // the walk needs no per-request node cap: pass total_nodes as the cap
     const int n = request_nodes(cu_nodes, b, total_nodes, total_nodes, &lo);
+    const int root_want = root_target[b];  // (read alongside the offsets)
     int32_t *idx = accept_idx + (int64_t)b * max_depth;
     if (n < 0) {
         if (lane == 0) report(err, TV_DEVERR_BAD_REQUEST, b);
@@ -79,7 +80,6 @@ __global__ void __launch_bounds__(64) accept_greedy_kernel(
     const int32_t *par = parent + lo;
     const int32_t *dr = draft + lo;
     const int32_t *tg = target + lo;
-    const int root_want = root_target[b];
     if (n > TV_MAX_NODES) {
         // too many nodes to hold: test the children straight from memory
         walk_global(par, dr, tg, n, root_want, max_depth, idx, accept_len + b, next_token + b);

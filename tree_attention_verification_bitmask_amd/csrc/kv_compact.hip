@@ -38,12 +38,15 @@ __global__ void __launch_bounds__(kCompactThreads) kv_compact_kernel(
     const int P = prefix_len[b];
     const int64_t ks = kv_start[b];
     const int L = accept_len[b];
-    if (n < 0 || P < 0 || ks < 0 || ks + P + n > kv_rows || L < 0 || L > max_depth) {
+    // The path row is read before the sizes are checked (it lies in bounds
+    // whatever they are), and the checks use no short-circuit, so all these
+    // reads are in flight together instead of one round trip each.
+    const int s_raw = tid < max_depth ? accept_idx[(int64_t)b * max_depth + tid] : 0;
+    if ((n < 0) | (P < 0) | (ks < 0) | (ks + P + n > kv_rows) | (L < 0) | (L > max_depth)) {
         if (g == 0 && tid == 0) report(err, TV_DEVERR_BAD_REQUEST, b);
         return;
     }
-    int s = 0;
-    if (tid < L) s = accept_idx[(int64_t)b * max_depth + tid];
+    const int s = tid < L ? s_raw : 0;
     const bool bad = tid < L && (s < 0 || s >= n);
     if (tid < L) sidx[tid] = s;
     if (__syncthreads_or(bad)) {  // uniform: every thread sees the same OR

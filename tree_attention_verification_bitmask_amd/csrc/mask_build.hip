@@ -34,7 +34,7 @@ __global__ void __launch_bounds__(kMaskThreads) mask_build_kernel(
     int lo;
     const int n = request_nodes(cu_nodes, b, total_nodes, max_nodes, &lo);
     const int P = prefix_len[b];
-    if (n < 0 || P < 0) {
+    if ((n < 0) | (P < 0)) {  // (no short-circuit: both reads in flight together)
         if (threadIdx.x == 0) report(err, TV_DEVERR_BAD_REQUEST, b);
         return;
     }
