@@ -552,8 +552,8 @@ __device__ __forceinline__ int commit_path(const int32_t *cu_nodes, const int32_
     int lo;
     const int n = request_nodes(cu_nodes, b, total_nodes, total_nodes, &lo);
     *lo_out = lo;
-    const int L = n < 0 ? -1 : accept_len[b];
-    if (n < 0 || L < 0 || L > D || L > n) {
+    const int L = accept_len[b];  // (read with the offsets; b < batch)
+    if ((n < 0) | (L < 0) | (L > D) | (L > n)) {
         if (reporter && threadIdx.x == 0) report(err, TV_DEVERR_BAD_REQUEST, b);
         return -1;
     }

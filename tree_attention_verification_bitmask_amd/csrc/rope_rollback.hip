@@ -100,12 +100,15 @@ __global__ void __launch_bounds__(64) rollback_kernel(
     const int n = request_nodes(cu_nodes, b, total_nodes, total_nodes, &lo);
     const int P = prefix_len[b];
     const int L = accept_len[b];
-    if (n < 0 || P < 0 || L < 0 || L > max_depth || L > n || (int64_t)P + L > stride) {
+    // the path row is read with the sizes (in bounds whatever they are), and
+    // the checks use no short-circuit: one memory round trip, not four
+    const int32_t *idx = accept_idx + (int64_t)b * max_depth;
+    const int my_raw = lane < max_depth ? idx[lane] : -1;  // TV_MAX_DEPTH == 64 == lanes
+    if ((n < 0) | (P < 0) | (L < 0) | (L > max_depth) | (L > n) | ((int64_t)P + L > stride)) {
         if (lane == 0) report(err, TV_DEVERR_BAD_REQUEST, b);
         return;
     }
-    const int32_t *idx = accept_idx + (int64_t)b * max_depth;
-    const int my = lane < L ? idx[lane] : -1;  // TV_MAX_DEPTH == 64 == lanes
+    const int my = lane < L ? my_raw : -1;
     if (__ballot(lane < L && (my < 0 || my >= n)) != 0) {
         if (lane == 0) report(err, TV_DEVERR_BAD_PATH, b);
         return;
