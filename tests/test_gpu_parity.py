@@ -199,6 +199,13 @@ EDGE = {
     "chain_64_deep": ([W.chain_tree(64)], [250], 32, 8, 128, "bf16"),
     "many_requests": ([W.random_tree(np.random.default_rng(10 + i), 1 + 7 * i, 16) for i in range(12)],
                       [17 * i for i in range(12)], 32, 8, 128, "bf16"),
+    # batches whose largest tree needs 4 row tiles per KV head (tile order rotated across the
+    # shader engines) and 3 (plain order), with short requests leaving tiles empty
+    "batch_4_tiles": ([W.random_tree(np.random.default_rng(30), 250, 16),
+                       W.random_tree(np.random.default_rng(31), 17, 16),
+                       W.random_tree(np.random.default_rng(32), 200, 16)], [300, 0, 1000], 32, 8, 128, "bf16"),
+    "batch_3_tiles": ([W.random_tree(np.random.default_rng(33), 170, 16),
+                       W.random_tree(np.random.default_rng(34), 60, 16)], [500, 64], 32, 8, 128, "bf16"),
 }
 
 
