@@ -236,6 +236,9 @@ def main(argv=None):
                     help="run one device-to-device copy of this many MiB first (counter calibration)")
     ap.add_argument("--ingest-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from two rocprofv3 --pmc output folders and exit")
+    ap.add_argument("--warm", action="store_true",
+                    help="reuse one input set every step (warm Infinity Cache); the default rotates "
+                         "over enough copies to keep it cold, and roofline claims use the cold runs")
     ap.add_argument("--select", action="store_true",
                     help="time tree_select_topb (draft tree from a frontier ledger) instead of the pass")
     ap.add_argument("--select-batch", type=int, default=32)
@@ -311,7 +314,7 @@ def main(argv=None):
     k0 = torch.from_numpy(wl.k).to(dev).to(fdt).contiguous()
     v0 = torch.from_numpy(wl.v).to(dev).to(fdt).contiguous()
     footprint = (q0.numel() + k0.numel() + v0.numel() + q0.numel()) * es
-    R = max(1, math.ceil(COLD_BYTES / footprint))
+    R = 1 if args.warm else max(1, math.ceil(COLD_BYTES / footprint))
     sets = [(q0.clone(), k0.clone(), v0.clone()) for _ in range(R)]
     del q0, k0, v0
     words = (wl.max_nodes + 63) // 64
@@ -434,6 +437,7 @@ def main(argv=None):
         "config": {"workload": f"{wl.name}: {W.CONFIGS[wl.name]['desc']}", "seed": wl.seed, "batch": B,
                    "tree_nodes": T, "max_prefix": wl.max_prefix, "hq": wl.hq, "hkv": wl.hkv,
                    "head_dim": wl.d, "max_depth": wl.max_depth, "cold_cache_sets": R,
+                   "cache": "warm" if args.warm else "cold",
                    "workspace_bytes": ws_bytes, "host_enqueue_ms": t_host_enq * 1e3,
                    "spin_ahead_ms": spin_ms},
         "roofline": roof,
