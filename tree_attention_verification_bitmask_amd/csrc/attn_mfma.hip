@@ -614,6 +614,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
         const uint32_t kbase = kb + (uint32_t)((j + 2) % kStages) * kHalf;
         uint32_t vtt = vt, ktt = kt;
         asm volatile("" : "+v"(vtt), "+v"(ktt));
+        // The wave feeding the matrix core outranks its SIMD partner (in its
+        // softmax phase) for issue, so the products and their operand reads go
+        // out back to back; the partner's vector work fills the gaps.
+        // Measured: c4 53.4 -> 51.8 us, c5 105.8 -> 101.7 us.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -634,6 +639,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         // Results of the phase are pinned here: register-only work must not
         // drift across the barriers into the other phase.
         asm volatile("" : "+v"(sv));
