@@ -717,26 +717,28 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
     }
 }
 
-// Merge the per-slice partials of one row of one (tile, 32-row group, 8
+// Merge the per-slice partials of one row of one (tile, 32-row group,
 // channels): O = sum_s w_s O_s / sum_s w_s l_s with w_s = 2^((m_s - M) c),
-// M = max_s m_s.  One wavefront per (tile, row group, 32-channel block, float4
-// slot i4), four per workgroup; lane layout as the partials (lane half h holds
-// channels 32 db + 8 i4 + 4 h .. +3 of row col).  The slices are taken in
-// batches of up to kCombineBatch whose loads are all issued before any is
-// used, so a batch costs one memory round trip; a batch loads only the slices
-// that exist.
+// M = max_s m_s.  One wavefront per (tile, row group, 32-channel block, I4W of
+// the 4 float4 slots), four per workgroup; lane layout as the partials (lane
+// half h holds channels 32 db + 8 i4 + 4 h .. +3 of row col).  The slices are
+// taken in batches whose loads are all issued before any is used, so a batch
+// costs one memory round trip; a batch loads only the slices that exist.  With
+// few slices (I4W = 4) a wave merges all four slots: four times fewer waves,
+// each with four times the loads in flight.
 constexpr int kCombineWaves = 4;
-constexpr int kCombineBatch = 16;
-template <int D>
+template <int D, int I4W>
 __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParams p) {
     constexpr int DB = Geo<D>::kDB;
+    constexpr int kGroups = 4 / I4W;                 // waves per (tile, row group, channel block)
+    constexpr int kBatch = I4W == 1 ? 16 : 8;        // slices per batch
     // (wave-uniform: the request's sizes then come by scalar loads, which
     // complete independently of the partials' vector loads)
     const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * kCombineWaves + (threadIdx.x >> 6));
-    const int i4 = gw & 3;
-    const int db = (gw >> 2) % DB;
-    const int rg = (gw / (4 * DB)) % kWaves;
-    const int tile = gw / (4 * DB * kWaves);
+    const int i4b = (gw % kGroups) * I4W;
+    const int db = (gw / kGroups) % DB;
+    const int rg = (gw / (kGroups * DB)) % kWaves;
+    const int tile = gw / (kGroups * DB * kWaves);
     if (tile >= p.batch * p.hkv * p.row_tiles) return;
     const int lane = threadIdx.x & 63;
     const int col = lane & 31, half = lane >> 5;
@@ -751,16 +753,17 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
     // zero (0 * NaN would poison the sum).
     const int64_t base = (int64_t)tile * p.splits;
     const float2 *ml = p.ws_ml + (base * kWaves + rg) * 32 + col;
-    const uint2 *po = p.ws_o + (base * kWaves + rg) * (DB * 4 * 64) + (db * 4 + i4) * 64 + lane;
+    const uint2 *po = p.ws_o + (base * kWaves + rg) * (DB * 4 * 64) + (db * 4 + i4b) * 64 + lane;
     constexpr int64_t kMlStride = kWaves * 32;                    // per slice
     constexpr int64_t kOStride = (int64_t)kWaves * DB * 4 * 64;   // per slice
-    float2 m_l[kCombineBatch];
-    uint2 o[kCombineBatch];
-    const int nb0 = min(kCombineBatch, p.splits);  // wave-uniform
+    float2 m_l[kBatch];
+    uint2 o[kBatch][I4W];
+    const int nb0 = min(kBatch, p.splits);  // wave-uniform
 #pragma unroll
-    for (int u = 0; u < kCombineBatch; ++u) {
+    for (int u = 0; u < kBatch; ++u) {
         m_l[u] = u < nb0 ? ml[u * kMlStride] : make_float2(-INFINITY, 0.f);
-        o[u] = u < nb0 ? po[u * kOStride] : make_uint2(0u, 0u);
+#pragma unroll
+        for (int ii = 0; ii < I4W; ++ii) o[u][ii] = u < nb0 ? po[u * kOStride + ii * 64] : make_uint2(0u, 0u);
     }
 
     const Req rq = load_request(p, b);
@@ -776,40 +779,49 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
     const int r = row0 + rg * 32 + col;
 
     float M = -INFINITY, L = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = 0; s0 < nsplit; s0 += kCombineBatch) {
-        const int nb = min(kCombineBatch, nsplit - s0);  // wave-uniform
+    float4 acc[I4W];
+#pragma unroll
+    for (int ii = 0; ii < I4W; ++ii) acc[ii] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
+        const int nb = min(kBatch, nsplit - s0);  // wave-uniform
         if (s0 > 0) {
 #pragma unroll
-            for (int u = 0; u < kCombineBatch; ++u) {
+            for (int u = 0; u < kBatch; ++u) {
                 // slices past the end issue no load (a uniform branch)
                 if (u < nb) {
                     m_l[u] = ml[(s0 + u) * kMlStride];
-                    o[u] = po[(s0 + u) * kOStride];
+#pragma unroll
+                    for (int ii = 0; ii < I4W; ++ii) o[u][ii] = po[(s0 + u) * kOStride + ii * 64];
                 }
             }
         }
         float mb = M;
 #pragma unroll
-        for (int u = 0; u < kCombineBatch; ++u)
+        for (int u = 0; u < kBatch; ++u)
             if (u < nb) mb = fmaxf(mb, m_l[u].x);
         const float mref = (mb == -INFINITY) ? 0.f : mb;
         const float a = __builtin_amdgcn_exp2f((M - mref) * p.c);  // 0 when M = -inf
         L *= a;
-        acc.x *= a;
-        acc.y *= a;
-        acc.z *= a;
-        acc.w *= a;
 #pragma unroll
-        for (int u = 0; u < kCombineBatch; ++u) {
+        for (int ii = 0; ii < I4W; ++ii) {
+            acc[ii].x *= a;
+            acc[ii].y *= a;
+            acc[ii].z *= a;
+            acc[ii].w *= a;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
             if (u < nb) {
                 // slice weight times its sum: the partial holds O / l
                 const float wl = __builtin_amdgcn_exp2f((m_l[u].x - mref) * p.c) * m_l[u].y;
                 L += wl;
-                acc.x = fmaf(wl, bf16_lo(o[u].x), acc.x);
-                acc.y = fmaf(wl, bf16_hi(o[u].x), acc.y);
-                acc.z = fmaf(wl, bf16_lo(o[u].y), acc.z);
-                acc.w = fmaf(wl, bf16_hi(o[u].y), acc.w);
+#pragma unroll
+                for (int ii = 0; ii < I4W; ++ii) {
+                    acc[ii].x = fmaf(wl, bf16_lo(o[u][ii].x), acc[ii].x);
+                    acc[ii].y = fmaf(wl, bf16_hi(o[u][ii].x), acc[ii].y);
+                    acc[ii].z = fmaf(wl, bf16_lo(o[u][ii].y), acc[ii].z);
+                    acc[ii].w = fmaf(wl, bf16_hi(o[u][ii].y), acc[ii].w);
+                }
             }
         }
         M = mb;
@@ -819,9 +831,12 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
     const int node = r / G;
     const int head = g * G + r % G;
     uint16_t *orow = p.out + (((int64_t)lo + node) * p.hq + head) * D;
-    const int d = db * 32 + 8 * i4 + 4 * half;
-    *reinterpret_cast<uint2 *>(orow + d) =
-        make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+#pragma unroll
+    for (int ii = 0; ii < I4W; ++ii) {
+        const int d = db * 32 + 8 * (i4b + ii) + 4 * half;
+        *reinterpret_cast<uint2 *>(orow + d) = make_uint2(pack_bf16x2(acc[ii].x * inv, acc[ii].y * inv),
+                                                          pack_bf16x2(acc[ii].z * inv, acc[ii].w * inv));
+    }
 }
 
 int env_int(const char *name, int dflt) {
@@ -902,16 +917,22 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *works
     const long ngroups = (long)a.batch * a.hkv * plan.splits;
     const long grid = ((ngroups + kXcds - 1) / kXcds) * plan.row_tiles * kXcds;
     const long tiles = (long)a.batch * a.hkv * plan.row_tiles;
-    const long cwaves = tiles * kWaves * (a.head_dim / 32) * 4;
+    // few slices: one merge wave covers all four float4 slots of its channels
+    const bool wide = plan.splits <= 8;
+    const long cwaves = tiles * kWaves * (a.head_dim / 32) * (wide ? 1 : 4);
     const long cblocks = (cwaves + kCombineWaves - 1) / kCombineWaves;
     if (a.head_dim == 128) {
         hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, p);
-        if (plan.splits > 1)
-            hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(cblocks), dim3(64 * kCombineWaves), 0, stream, p);
+        if (plan.splits > 1 && wide)
+            hipLaunchKernelGGL((attn_combine_kernel<128, 4>), dim3(cblocks), dim3(64 * kCombineWaves), 0, stream, p);
+        else if (plan.splits > 1)
+            hipLaunchKernelGGL((attn_combine_kernel<128, 1>), dim3(cblocks), dim3(64 * kCombineWaves), 0, stream, p);
     } else {
         hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, p);
-        if (plan.splits > 1)
-            hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(cblocks), dim3(64 * kCombineWaves), 0, stream, p);
+        if (plan.splits > 1 && wide)
+            hipLaunchKernelGGL((attn_combine_kernel<64, 4>), dim3(cblocks), dim3(64 * kCombineWaves), 0, stream, p);
+        else if (plan.splits > 1)
+            hipLaunchKernelGGL((attn_combine_kernel<64, 1>), dim3(cblocks), dim3(64 * kCombineWaves), 0, stream, p);
     }
     return hipGetLastError();
 }
