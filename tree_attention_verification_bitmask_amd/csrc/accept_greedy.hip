@@ -89,16 +89,25 @@ __global__ void __launch_bounds__(64) accept_greedy_kernel(
 
     int pk[kPerLane];
     int dk[kPerLane];
+    int tk[kPerLane];
+    // every load first, then the LDS stores: a store right after its load
+    // would wait for it, one memory round trip per 64 nodes
 #pragma unroll
     for (int k = 0; k < kPerLane; ++k) {
         const int j = 64 * k + lane;
         pk[k] = -2;
         dk[k] = -1;
+        tk[k] = 0;
         if (k < nk && j < n) {
             pk[k] = par[j];
             dk[k] = dr[j];
-            stg[j] = tg[j];
+            tk[k] = tg[j];
         }
+    }
+#pragma unroll
+    for (int k = 0; k < kPerLane; ++k) {
+        const int j = 64 * k + lane;
+        if (k < nk && j < n) stg[j] = tk[k];
     }
     __syncthreads();
     // acceptable[j]: draft[j] == the target's choice at parent[j]

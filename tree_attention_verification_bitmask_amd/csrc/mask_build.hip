@@ -39,7 +39,20 @@ __global__ void __launch_bounds__(kMaskThreads) mask_build_kernel(
         return;
     }
     const int32_t *par = parent + lo;
-    for (int i = threadIdx.x; i < n; i += kMaskThreads) spar[i] = par[i];
+    // every load first, then the LDS stores (a store right after its load
+    // would wait for it: one memory round trip per 256 nodes)
+    constexpr int kPer = (TV_MAX_NODES + kMaskThreads - 1) / kMaskThreads;
+    int pv[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const int i = threadIdx.x + r * kMaskThreads;
+        pv[r] = i < n ? par[i] : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const int i = threadIdx.x + r * kMaskThreads;
+        if (i < n) spar[i] = pv[r];
+    }
     __syncthreads();
 
     for (int i = threadIdx.x; i < n; i += kMaskThreads) {
