@@ -420,6 +420,11 @@ def main(argv=None):
                  "alg_bytes": byts, "alg_flops": flops, "arith_intensity": ai,
                  "achieved_gbs": byts / (attn_us * 1e-6) / 1e9,
                  "achieved_tflops": flops / (attn_us * 1e-6) / 1e12})
+    # Secondary denominator: the HBM rate a plain device-to-device copy reaches
+    # on this GPU (read + write bytes over time), measured after the timed region.
+    copy_gbs = hbm_copy_probe(torch, dev)
+    roof["hbm_copy_probe_gbs"] = copy_gbs
+    roof["frac_of_copy_probe"] = roof["achieved_gbs"] / copy_gbs
 
     line = {
         "metric": METRIC,
@@ -593,6 +598,26 @@ def bench_argmax(args, torch, BND, L, dev):
                                 "sample": f"target_argmax on rows 0..{n - 1} of the same logits ({dt:.2f} s)"}
     print(json.dumps(line), flush=True)
     return 0
+
+
+def hbm_copy_probe(torch, dev, mib: int = 512, reps: int = 10) -> float:
+    """GB/s of a device-to-device copy of `mib` MiB (bytes read + written),
+    averaged over `reps` copies timed with HIP events."""
+    n = mib << 18  # float32 elements
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
 
 
 def bench_sample(args, torch, BND, L, dev):
