@@ -416,6 +416,7 @@ def main(argv=None):
     roof["traffic_detail"] = tdetail
     roof.update({"kernel": "tree_attn_verify", "avg_us": attn_us,
                  "p10_us": float(np.percentile(attn_ms, 10) * 1e3),
+                 "p50_us": float(np.percentile(attn_ms, 50) * 1e3),
                  "p90_us": float(np.percentile(attn_ms, 90) * 1e3),
                  "alg_bytes": byts, "alg_flops": flops, "arith_intensity": ai,
                  "achieved_gbs": byts / (attn_us * 1e-6) / 1e9,
