@@ -281,6 +281,27 @@ def test_attn_device_error_for_inconsistent_request():
     assert int(err.item()) == (O.ERR_BAD_REQUEST << 24) | 0
 
 
+def test_attn_device_error_in_batch():
+    """A batch (planned task order) where one request's prefix_len exceeds
+    max_prefix: that request is reported and skipped, the others are computed."""
+    announce("attn device error word in a batch")
+    wl = W.make_workload("c5", seed=0)
+    bad = int(np.argmax(wl.prefix_len))
+    maxp = int(np.sort(wl.prefix_len)[-2])
+    assert int(wl.prefix_len[bad]) > maxp
+    d = dev_workload(wl)
+    anc, _, _, _ = B().tree_mask_build(d["parent"], d["cu"], d["P"], wl.max_nodes, wl.max_depth)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = B().tree_attn_verify(d["q"], d["k"], d["v"], d["cu"], d["ks"], d["P"], anc, wl.max_nodes, maxp, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == (O.ERR_BAD_REQUEST << 24) | bad
+    lo, hi = int(wl.cu_nodes[bad]), int(wl.cu_nodes[bad + 1])
+    rows = [(t, h) for t, h in sample_rows(wl, 200, 3) if not lo <= t < hi]
+    got = to_np(out.float())
+    assert_attn_close(np.stack([got[t, h] for t, h in rows]), *oracle_attn(wl, rows=rows), "bf16",
+                      stated=True, what="batch with a bad request")
+
+
 # ---------------------------------------------------------------------------
 # tree_accept_greedy and kv_compact_path
 # ---------------------------------------------------------------------------

@@ -198,6 +198,7 @@ struct KParams {
     uint16_t *out;
     uint2 *ws_o;    // partial O / l as bf16, lane-native layout (see attn_fwd_kernel)
     float2 *ws_ml;  // partial (m, l) per row
+    const int32_t *task_table;  // batches: task of each workgroup, longest first (or null)
     int32_t *err;
 };
 
@@ -264,6 +265,19 @@ struct Task {
     int b, g, s, rt;
 };
 __device__ __forceinline__ bool decode_task(const KParams &p, int wid, Task *t) {
+    if (p.task_table) {
+        // planned order (attn_plan_kernel): task index ((b * hkv + g) * splits
+        // + s) * row_tiles + rt, or -1 past the real tasks
+        const int task = p.task_table[wid];
+        if (task < 0) return false;
+        t->rt = task % p.row_tiles;
+        int rest = task / p.row_tiles;
+        t->s = rest % p.splits;
+        rest /= p.splits;
+        t->g = rest % p.hkv;
+        t->b = rest / p.hkv;
+        return true;
+    }
     const int ngroups = p.batch * p.hkv * p.splits;
     const int x = wid % kXcds;       // XCD
     const int k = wid / kXcds;       // slot on that XCD
@@ -839,6 +853,91 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
     }
 }
 
+// Task plan for batches.  The static order cannot know the requests' sizes,
+// and within an XCD the slots are dispatched in order to its shader engines,
+// so a long slice behind a queue of short ones finishes late.  One workgroup
+// reads every request's sizes, gives each task (request, KV head, slice, row
+// tile) its chunk count by the attention kernel's own rules (0 = the kernel
+// would exit at once), and counting-sorts the non-empty tasks longest first
+// into the table, padded with -1.  Tasks of equal length land in any order:
+// each writes its own partial slot, so the results do not depend on it.
+// Invalid requests are reported here, since no workgroup is planned for them.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBins = 4096;     // chunk counts 1 .. kPlanBins - 1
+constexpr int kPlanMaxTasks = 65536;
+
+__device__ __forceinline__ int task_chunks(const KParams &p, int task) {
+    const int rt = task % p.row_tiles;
+    int rest = task / p.row_tiles;
+    const int s = rest % p.splits;
+    rest /= p.splits;
+    const int b = rest / p.hkv;
+    const Req rq = load_request(p, b);
+    if (!rq.ok) return 0;
+    const int G = p.hq / p.hkv;
+    const int rows_b = rq.n * G;
+    const int row0 = rt * kTileRows;
+    if (row0 >= rows_b) return 0;
+    const int row_end = min(rows_b, row0 + kTileRows);
+    const int key_end = rq.P + (row_end - 1) / G + 1;
+    const int k_lo = s * p.keys_per_split;
+    if (k_lo >= key_end) return 0;
+    const int k_hi = min(k_lo + p.keys_per_split, key_end);
+    return (k_hi - k_lo + kChunk - 1) / kChunk;
+}
+
+__global__ void __launch_bounds__(kPlanThreads) attn_plan_kernel(KParams p, int ntasks, int nslots,
+                                                                  int32_t *__restrict__ table) {
+    __shared__ int cnt[kPlanBins];
+    __shared__ int wsum[kPlanThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    for (int i = tid; i < kPlanBins; i += kPlanThreads) cnt[i] = 0;
+    for (int b = tid; b < p.batch; b += kPlanThreads)
+        if (!load_request(p, b).ok) report(p.err, TV_DEVERR_BAD_REQUEST, b);
+    __syncthreads();
+    for (int t = tid; t < ntasks; t += kPlanThreads) {
+        const int len = task_chunks(p, t);
+        if (len > 0) atomicAdd(&cnt[len], 1);
+    }
+    __syncthreads();
+    // start of each length's run, longest first: thread tid owns the bins of
+    // lengths kPlanBins - 1 - (4 tid .. 4 tid + 3)
+    constexpr int kPer = kPlanBins / kPlanThreads;
+    int v[kPer];
+    int own = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        v[e] = cnt[kPlanBins - 1 - (kPer * tid + e)];
+        own += v[e];
+    }
+    int incl = own;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kPlanThreads / 64; ++w) {
+        before += w < wv ? wsum[w] : 0;
+        total += wsum[w];
+    }
+    int run = before + incl - own;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        cnt[kPlanBins - 1 - (kPer * tid + e)] = run;
+        run += v[e];
+    }
+    __syncthreads();
+    for (int t = tid; t < ntasks; t += kPlanThreads) {
+        const int len = task_chunks(p, t);
+        if (len > 0) table[atomicAdd(&cnt[len], 1)] = t;
+    }
+    for (int i = total + tid; i < nslots; i += kPlanThreads) table[i] = -1;
+}
+
 int env_int(const char *name, int dflt) {
     const char *s = getenv(name);
     if (!s || !*s) return dflt;
@@ -865,7 +964,11 @@ MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefi
     // about two and a half rounds for several (ragged) requests, so short
     // ones leave room to balance.  A tuning override (TV_MFMA_SPLITS) may fix
     // the count instead.
-    const long target = batch == 1 ? 256 : 640;
+    // Batches that the planner can order take about four rounds of short
+    // slices (8 at c5); otherwise about two and a half in the static order.
+    const long planned = (long)batch * hkv * plan.row_tiles;  // tasks per slice
+    const bool can_plan = batch > 1;
+    const long target = batch == 1 ? 256 : (can_plan ? 1024 : 640);
     int splits = (int)((target + base_tasks - 1) / base_tasks);
     splits = env_int("TV_MFMA_SPLITS", splits);
     if (splits < 1) splits = 1;
@@ -878,6 +981,13 @@ MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefi
         plan.ws_bytes = rows * head_dim * sizeof(uint16_t);
         plan.ws_bytes = (plan.ws_bytes + 255) & ~(size_t)255;
         plan.ws_bytes += rows * sizeof(float2);
+        const long ntasks = planned * plan.splits;
+        if (can_plan && ntasks <= kPlanMaxTasks && cps < kPlanBins) {
+            plan.table = true;
+            plan.table_slots = (int)((ntasks + kXcds - 1) / kXcds * kXcds);
+            plan.table_off = (plan.ws_bytes + 255) & ~(size_t)255;
+            plan.ws_bytes = plan.table_off + (size_t)plan.table_slots * sizeof(int32_t);
+        }
     }
     return plan;
 }
@@ -907,6 +1017,7 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *works
     p.err = a.err;
     p.ws_o = nullptr;
     p.ws_ml = nullptr;
+    p.task_table = nullptr;
     if (plan.splits > 1) {
         const size_t rows = (size_t)a.batch * a.hkv * plan.row_tiles * plan.splits * kTileRows;
         size_t off = rows * a.head_dim * sizeof(uint16_t);
@@ -915,7 +1026,15 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *works
         p.ws_ml = (float2 *)((char *)workspace + off);
     }
     const long ngroups = (long)a.batch * a.hkv * plan.splits;
-    const long grid = ((ngroups + kXcds - 1) / kXcds) * plan.row_tiles * kXcds;
+    long grid = ((ngroups + kXcds - 1) / kXcds) * plan.row_tiles * kXcds;
+    if (plan.table) {
+        int32_t *table = (int32_t *)((char *)workspace + plan.table_off);
+        const int ntasks = a.batch * a.hkv * plan.row_tiles * plan.splits;
+        hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p, ntasks, plan.table_slots,
+                           table);
+        p.task_table = table;
+        grid = plan.table_slots;
+    }
     const long tiles = (long)a.batch * a.hkv * plan.row_tiles;
     // few slices: one merge wave covers all four float4 slots of its channels
     const bool wide = plan.splits <= 8;

@@ -81,6 +81,9 @@ struct MfmaPlan {
     int row_tiles = 0;     // per (request, KV head), sized for max_nodes
     int splits = 0;        // key-axis splits per row tile (1 = no combine)
     int keys_per_split = 0;
+    bool table = false;     // batches: workgroups take their task from a planned table
+    int table_slots = 0;    // workgroups launched on the table path
+    size_t table_off = 0;   // byte offset of the table in the workspace
     size_t ws_bytes = 0;
 };
 MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefix, int hq, int hkv,
