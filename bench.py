@@ -61,7 +61,7 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3
 METRIC = "verified tree-tokens/sec per GPU; % of HBM-BW / bf16-MFMA roofline"
 COLD_BYTES = 512 << 20
 ATTN_SOURCES = ("tree_attention_verification_bitmask_amd/csrc/attn_mfma.hip",)
-ATTN_KERNELS = ("attn_fwd_kernel", "attn_combine_kernel")
+ATTN_KERNELS = ("attn_fwd_kernel", "attn_combine_kernel", "attn_plan_kernel")
 
 
 def attn_source_hash() -> str:
@@ -131,7 +131,8 @@ def ingest_traffic(workload: str, fetch_dir: str, write_dir: str, calib_mib: int
         f"--workload {workload} --steps 5 --warmup 2 --no-cpu-baseline --calib-copy-mib {calib_mib}\n"
         f"python3 $REPO/bench.py --workload {workload} --ingest-traffic OUT/fetch OUT/write\n"
         "```\n\n"
-        "A call of tree_attn_verify is attn_fwd_kernel plus attn_combine_kernel; the\n"
+        "A call of tree_attn_verify is attn_fwd_kernel plus attn_combine_kernel (and,\n"
+        "for batches, the attn_plan_kernel that orders the tasks before them); the\n"
         "figures are their per-call sums averaged over the calls in the trace.  Each\n"
         f"counter is scaled by {calib_mib} MiB over what it read for the calibration copy.\n\n"
         "| counter | KiB per call (raw) | calibration copy (KiB raw) | scale | bytes per call |\n"
@@ -423,9 +424,11 @@ def main(argv=None):
                  "achieved_tflops": flops / (attn_us * 1e-6) / 1e12})
     # Secondary denominator: the HBM rate a plain device-to-device copy reaches
     # on this GPU (read + write bytes over time), measured after the timed region.
-    copy_gbs = hbm_copy_probe(torch, dev)
+    # (Skipped in counter runs: the traffic calibration takes the largest copy
+    # in the trace as its reference.)
+    copy_gbs = hbm_copy_probe(torch, dev) if args.calib_copy_mib == 0 else None
     roof["hbm_copy_probe_gbs"] = copy_gbs
-    roof["frac_of_copy_probe"] = roof["achieved_gbs"] / copy_gbs
+    roof["frac_of_copy_probe"] = roof["achieved_gbs"] / copy_gbs if copy_gbs else None
 
     line = {
         "metric": METRIC,

@@ -856,23 +856,21 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
 // Task plan for batches.  The static order cannot know the requests' sizes,
 // and within an XCD the slots are dispatched in order to its shader engines,
 // so a long slice behind a queue of short ones finishes late.  One workgroup
-// reads every request's sizes, gives each task (request, KV head, slice, row
-// tile) its chunk count by the attention kernel's own rules (0 = the kernel
-// would exit at once), and counting-sorts the non-empty tasks longest first
-// into the table, padded with -1.  Tasks of equal length land in any order:
-// each writes its own partial slot, so the results do not depend on it.
-// Invalid requests are reported here, since no workgroup is planned for them.
+// reads every request's sizes, gives each group (request, KV head, slice) the
+// chunk count of its longest row tile by the attention kernel's own rules
+// (0 = every tile would exit at once), and counting-sorts the non-empty groups
+// longest first.  Group k of that order takes workgroup ids
+// (k / 8) * 8 * row_tiles + 8 i + k % 8 for its tiles i: consecutive groups on
+// consecutive XCDs, and the tiles of one group, which read the same K/V, on
+// one XCD in adjacent slots (sharing its L2).  Empty tiles and the padding
+// hold -1.  Groups of equal length land in any order: each task writes its
+// own partial slot, so the results do not depend on it.  Invalid requests are
+// reported here, since no workgroup is planned for them.
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanBins = 4096;     // chunk counts 1 .. kPlanBins - 1
 constexpr int kPlanMaxTasks = 65536;
 
-__device__ __forceinline__ int task_chunks(const KParams &p, int task) {
-    const int rt = task % p.row_tiles;
-    int rest = task / p.row_tiles;
-    const int s = rest % p.splits;
-    rest /= p.splits;
-    const int b = rest / p.hkv;
-    const Req rq = load_request(p, b);
+__device__ __forceinline__ int tile_chunks(const KParams &p, const Req &rq, int s, int rt) {
     if (!rq.ok) return 0;
     const int G = p.hq / p.hkv;
     const int rows_b = rq.n * G;
@@ -886,17 +884,29 @@ __device__ __forceinline__ int task_chunks(const KParams &p, int task) {
     return (k_hi - k_lo + kChunk - 1) / kChunk;
 }
 
-__global__ void __launch_bounds__(kPlanThreads) attn_plan_kernel(KParams p, int ntasks, int nslots,
+// Group q = (b * hkv + g) * splits + s: its longest tile's chunk count.
+__device__ __forceinline__ int group_chunks(const KParams &p, int q) {
+    const int s = q % p.splits;
+    const int b = q / p.splits / p.hkv;
+    const Req rq = load_request(p, b);
+    int len = 0;
+    for (int rt = 0; rt < p.row_tiles; ++rt) len = max(len, tile_chunks(p, rq, s, rt));
+    return len;
+}
+
+__global__ void __launch_bounds__(kPlanThreads) attn_plan_kernel(KParams p, int ngroups, int nslots,
                                                                   int32_t *__restrict__ table) {
     __shared__ int cnt[kPlanBins];
     __shared__ int wsum[kPlanThreads / 64];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int R = p.row_tiles;
     for (int i = tid; i < kPlanBins; i += kPlanThreads) cnt[i] = 0;
     for (int b = tid; b < p.batch; b += kPlanThreads)
         if (!load_request(p, b).ok) report(p.err, TV_DEVERR_BAD_REQUEST, b);
+    for (int i = tid; i < nslots; i += kPlanThreads) table[i] = -1;
     __syncthreads();
-    for (int t = tid; t < ntasks; t += kPlanThreads) {
-        const int len = task_chunks(p, t);
+    for (int q = tid; q < ngroups; q += kPlanThreads) {
+        const int len = group_chunks(p, q);
         if (len > 0) atomicAdd(&cnt[len], 1);
     }
     __syncthreads();
@@ -918,12 +928,9 @@ __global__ void __launch_bounds__(kPlanThreads) attn_plan_kernel(KParams p, int 
     }
     if (lane == 63) wsum[wv] = incl;
     __syncthreads();
-    int before = 0, total = 0;
+    int before = 0;
 #pragma unroll
-    for (int w = 0; w < kPlanThreads / 64; ++w) {
-        before += w < wv ? wsum[w] : 0;
-        total += wsum[w];
-    }
+    for (int w = 0; w < kPlanThreads / 64; ++w) before += w < wv ? wsum[w] : 0;
     int run = before + incl - own;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
@@ -931,11 +938,24 @@ __global__ void __launch_bounds__(kPlanThreads) attn_plan_kernel(KParams p, int 
         run += v[e];
     }
     __syncthreads();
-    for (int t = tid; t < ntasks; t += kPlanThreads) {
-        const int len = task_chunks(p, t);
-        if (len > 0) table[atomicAdd(&cnt[len], 1)] = t;
+    for (int q = tid; q < ngroups; q += kPlanThreads) {
+        const int len = group_chunks(p, q);
+        if (len <= 0) continue;
+        const int k = atomicAdd(&cnt[len], 1);  // rank of the group, longest first
+        const int s = q % p.splits;
+        const int b = q / p.splits / p.hkv;
+        const Req rq = load_request(p, b);
+        const int m = k / kXcds;  // the group's rank on its XCD
+        const int base = m * kXcds * R + k % kXcds;
+        // tile rt goes to slot i of the group, rotated by the slot's row of 4
+        // as in the static order, so that every shader engine gets first and
+        // last tiles alike
+        const int rot = (4 % R == 0) ? (m * R) / 4 : 0;
+        for (int rt = 0; rt < R; ++rt) {
+            const int i = ((rt - rot) % R + R) % R;
+            if (tile_chunks(p, rq, s, rt) > 0) table[base + kXcds * i] = q * R + rt;
+        }
     }
-    for (int i = total + tid; i < nslots; i += kPlanThreads) table[i] = -1;
 }
 
 int env_int(const char *name, int dflt) {
@@ -983,8 +1003,9 @@ MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefi
         plan.ws_bytes += rows * sizeof(float2);
         const long ntasks = planned * plan.splits;
         if (can_plan && ntasks <= kPlanMaxTasks && cps < kPlanBins) {
+            const long ngroups = (long)batch * hkv * plan.splits;
             plan.table = true;
-            plan.table_slots = (int)((ntasks + kXcds - 1) / kXcds * kXcds);
+            plan.table_slots = (int)((ngroups + kXcds - 1) / kXcds * kXcds * plan.row_tiles);
             plan.table_off = (plan.ws_bytes + 255) & ~(size_t)255;
             plan.ws_bytes = plan.table_off + (size_t)plan.table_slots * sizeof(int32_t);
         }
@@ -1029,9 +1050,9 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *works
     long grid = ((ngroups + kXcds - 1) / kXcds) * plan.row_tiles * kXcds;
     if (plan.table) {
         int32_t *table = (int32_t *)((char *)workspace + plan.table_off);
-        const int ntasks = a.batch * a.hkv * plan.row_tiles * plan.splits;
-        hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p, ntasks, plan.table_slots,
-                           table);
+        const int ngroups_i = a.batch * a.hkv * plan.splits;
+        hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p, ngroups_i,
+                           plan.table_slots, table);
         p.task_table = table;
         grid = plan.table_slots;
     }
