@@ -206,6 +206,12 @@ EDGE = {
                        W.random_tree(np.random.default_rng(32), 200, 16)], [300, 0, 1000], 32, 8, 128, "bf16"),
     "batch_3_tiles": ([W.random_tree(np.random.default_rng(33), 170, 16),
                        W.random_tree(np.random.default_rng(34), 60, 16)], [500, 64], 32, 8, 128, "bf16"),
+    # planned batches with other head layouts: head_dim 64, and 2 KV heads (G = 8), so the
+    # groups do not divide evenly over the 8 XCDs
+    "batch_head_dim_64": ([W.random_tree(np.random.default_rng(35 + i), n, 16) for i, n in enumerate((90, 12, 64))],
+                          [700, 33, 0], 16, 4, 64, "bf16"),
+    "batch_2_kv_heads": ([W.random_tree(np.random.default_rng(38 + i), n, 16) for i, n in enumerate((40, 100, 7, 77))],
+                         [1500, 260, 900, 2], 16, 2, 128, "bf16"),
 }
 
 
