@@ -88,6 +88,8 @@ constexpr int kTileRows = 32 * kWaves;  // query rows per workgroup
 constexpr int kChunk = 32;              // keys per LDS stage
 constexpr int kStages = 8;              // stages per ring (K ring, V ring)
 constexpr int kAhead = 6;               // the DMA of chunk c is issued at step c - kAhead
+constexpr int kAheadShort = 4;          // the same for slices of at most kShortSlice chunks
+constexpr int kShortSlice = 12;
 constexpr int kXcds = 8;
 constexpr int kMaxWords = (TV_MAX_NODES + 63) / 64;
 constexpr int kAncBytes = kTileRows * kMaxWords * 8;  // packed rows of the tile's nodes
@@ -299,8 +301,10 @@ __device__ __forceinline__ bool decode_task(const KParams &p, int wid, Task *t) 
     return true;
 }
 
-template <int D>
+// AH = copy look-ahead in chunks (AH for long slices, fewer for short ones).
+template <int D, int AH>
 __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
+    static_assert(AH >= 3 && AH <= kStages && AH - 2 <= 4, "ring depth and counted waits");
     using Gm = Geo<D>;
     constexpr int KS = Gm::kKS, DB = Gm::kDB, PW = Gm::kDmaPerWave;
     constexpr uint32_t kHalf = Gm::kHalf;
@@ -419,12 +423,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
                          : "v"(qrow), "n"(32 * k16)
                          : "memory");
     }
-    // (3) the first kAhead chunks.  After the wait everything but chunks
-    // 2 .. kAhead-1 has landed.
+    // (3) the first AH chunks.  After the wait everything but chunks
+    // 2 .. AH-1 has landed.
 #pragma unroll
-    for (int c = 0; c < kAhead; ++c)
+    for (int c = 0; c < AH; ++c)
         if (c < n) issue(c, c);
-    wait_chunks<PW, kAhead - 2>(min(n, kAhead) - 2);
+    wait_chunks<PW, AH - 2>(min(n, AH) - 2);
 #pragma unroll
     for (int k16 = 0; k16 < KS; ++k16) asm volatile("" : "+v"(qb[k16]));
     lds_barrier();
@@ -493,28 +497,28 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
     //   M(j): O += P(j) V(j) and S(j+1) = Q K(j+1)^T (16 products), plus the
     //         reads of V(j+1) and K(j+2) from LDS into registers.
     // V(j) starts with the wave's copies (K for A, V for B) of chunk
-    // j + kAhead: the vector phase has issue slots to spare.
+    // j + AH: the vector phase has issue slots to spare.
     // Every wave runs V(0) M(0) V(1) M(1) ... with a barrier after each item;
     // group B first passes one barrier alone, so it runs one item behind and
     // on each SIMD one wave feeds the matrix core while the other runs the
     // exponentials.  Barrier 2j+1 starts A's M(j): before it A waits for its
     // part of K(j+2) and B (at the end of its M(j-1)) for its part of V(j+1).
-    // A copy issued in V(j) overwrites the stage of chunk j + kAhead - 8,
-    // whose last reads (B's M of chunk j + kAhead - 9) were consumed at least
+    // A copy issued in V(j) overwrites the stage of chunk j + AH - 8,
+    // whose last reads (B's M of chunk j + AH - 9) were consumed at least
     // two items earlier.
     auto copy_ahead = [&](int j) {
-        if (j + kAhead < n) issue(j + kAhead, (uint32_t)((j + kAhead) % kStages));
+        if (j + AH < n) issue(j + AH, (uint32_t)((j + AH) % kStages));
     };
     auto copy_ahead1 = [&](int j, int jj) {
-        if (j + kAhead < n) issue1(j + kAhead, (uint32_t)((j + kAhead) % kStages), jj);
+        if (j + AH < n) issue1(j + AH, (uint32_t)((j + AH) % kStages), jj);
     };
     // Waits ahead of the barrier that opens A's M(j) (A: K(j+2)) and the one
     // that opens A's M(j+1) (B, after its M(j): V(j+2)).
     auto wait_before_m = [&](int j) {
-        if (!grp_b) wait_chunks<PW, kAhead - 2>(n - (j + 3));
+        if (!grp_b) wait_chunks<PW, AH - 2>(n - (j + 3));
     };
     auto wait_after_m = [&](int j) {
-        if (grp_b) wait_chunks<PW, kAhead - 2>(n - (j + 3));
+        if (grp_b) wait_chunks<PW, AH - 2>(n - (j + 3));
     };
     if (!active) {
         // A wave without rows only keeps the copy schedule and the barriers.
@@ -1059,16 +1063,25 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *works
     const long tiles = (long)a.batch * a.hkv * plan.row_tiles;
     // few slices: one merge wave covers all four float4 slots of its channels
     const bool wide = plan.splits <= 8;
+    // short slices: the prologue outweighs the loop, so fewer chunks are
+    // copied ahead of the first barrier
+    const bool short_slices = plan.keys_per_split / kChunk <= kShortSlice;
     const long cwaves = tiles * kWaves * (a.head_dim / 32) * (wide ? 1 : 4);
     const long cblocks = (cwaves + kCombineWaves - 1) / kCombineWaves;
     if (a.head_dim == 128) {
-        hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, p);
+        if (short_slices)
+            hipLaunchKernelGGL((attn_fwd_kernel<128, kAheadShort>), dim3(grid), dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((attn_fwd_kernel<128, kAhead>), dim3(grid), dim3(kThreads), 0, stream, p);
         if (plan.splits > 1 && wide)
             hipLaunchKernelGGL((attn_combine_kernel<128, 4>), dim3(cblocks), dim3(64 * kCombineWaves), 0, stream, p);
         else if (plan.splits > 1)
             hipLaunchKernelGGL((attn_combine_kernel<128, 1>), dim3(cblocks), dim3(64 * kCombineWaves), 0, stream, p);
     } else {
-        hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, p);
+        if (short_slices)
+            hipLaunchKernelGGL((attn_fwd_kernel<64, kAheadShort>), dim3(grid), dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((attn_fwd_kernel<64, kAhead>), dim3(grid), dim3(kThreads), 0, stream, p);
         if (plan.splits > 1 && wide)
             hipLaunchKernelGGL((attn_combine_kernel<64, 4>), dim3(cblocks), dim3(64 * kCombineWaves), 0, stream, p);
         else if (plan.splits > 1)
