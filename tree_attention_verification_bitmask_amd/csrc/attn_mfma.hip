@@ -764,9 +764,9 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
     const int g = (tile / p.row_tiles) % p.hkv;
     const int b = tile / (p.row_tiles * p.hkv);
 
-    // The partials' addresses depend only on (tile, slice, lane), so the first
-    // batch is loaded before the request's sizes arrive: the two memory round
-    // trips overlap.  Slices the request does not have were never written and
+    // The partials' addresses depend only on (tile, slice, lane), so for one
+    // request the first batch is loaded before the request's sizes arrive: the
+    // two memory round trips overlap.  Slices the request does not have were never written and
     // hold arbitrary bits; they are skipped by branches below, never scaled by
     // zero (0 * NaN would poison the sum).
     const int64_t base = (int64_t)tile * p.splits;
@@ -776,7 +776,10 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
     constexpr int64_t kOStride = (int64_t)kWaves * DB * 4 * 64;   // per slice
     float2 m_l[kBatch];
     uint2 o[kBatch][I4W];
-    const int nb0 = min(kBatch, p.splits);  // wave-uniform
+    // (one request: every tile has nearly all slices, so the early loads are
+    // nearly all used; in a ragged batch short requests have few slices, and
+    // the loads wait for the sizes instead)
+    const int nb0 = p.batch == 1 ? min(kBatch, p.splits) : 0;  // wave-uniform
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
         m_l[u] = u < nb0 ? ml[u * kMlStride] : make_float2(-INFINITY, 0.f);
@@ -802,7 +805,7 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
     for (int ii = 0; ii < I4W; ++ii) acc[ii] = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
         const int nb = min(kBatch, nsplit - s0);  // wave-uniform
-        if (s0 > 0) {
+        if (s0 > 0 || nb0 == 0) {
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 // slices past the end issue no load (a uniform branch)
