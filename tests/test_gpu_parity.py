@@ -226,6 +226,24 @@ def test_attn_edge_cases(case):
                           what=f"{case}/{values}")
 
 
+@pytest.mark.parametrize("case", ["c5", "batch_4_tiles", "many_requests"])
+def test_attn_static_order_for_batches(case, monkeypatch):
+    """Batches with the task planner switched off (the order used when a plan
+    would be too large): the static, engine-rotated order gives the same
+    results."""
+    announce(f"attn static batch order {case}")
+    monkeypatch.setenv("TV_MFMA_PLAN", "0")
+    if case == "c5":
+        wl = W.make_workload("c5", seed=1)
+    else:
+        parents, prefixes, hq, hkv, d, dtype = EDGE[case]
+        wl = W.make_from_trees(parents, prefixes, hq=hq, hkv=hkv, d=d, dtype=dtype, seed=3, values="qwen")
+    out = run_attn(wl)
+    rows = sample_rows(wl, 200, 5)
+    assert_attn_close(np.stack([out[t, h] for t, h in rows]), *oracle_attn(wl, rows=rows), wl.dtype,
+                      what=f"{case} static order")
+
+
 def test_attn_largest_tree():
     """1024 nodes (4096 rows per KV head, 16 mask words) over a short prefix."""
     announce("attn 1024-node tree")

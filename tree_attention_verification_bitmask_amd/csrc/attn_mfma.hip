@@ -994,7 +994,9 @@ MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefi
     // Batches that the planner can order take about four rounds of short
     // slices (8 at c5); otherwise about two and a half in the static order.
     const long planned = (long)batch * hkv * plan.row_tiles;  // tasks per slice
-    const bool can_plan = batch > 1;
+    // (TV_MFMA_PLAN=0 keeps the static order for batches too: tuning, and
+    // the tests of that order)
+    const bool can_plan = batch > 1 && env_int("TV_MFMA_PLAN", 1) != 0;
     const long target = batch == 1 ? 256 : (can_plan ? 1024 : 640);
     int splits = (int)((target + base_tasks - 1) / base_tasks);
     splits = env_int("TV_MFMA_SPLITS", splits);
