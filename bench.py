@@ -3,8 +3,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
 
 One step = the whole pass over one batch of synthetic inputs already resident
-in HBM: tree_mask_build -> tree_attn_verify -> tree_accept_greedy ->
-kv_compact_path, each through the C ABI.  The default workload is the
+in HBM: tree_mask_build -> tree_attn_verify -> tree_accept_commit (the
+acceptance walk and the compaction of the accepted path in one launch; with
+--separate-commit, tree_accept_greedy -> kv_compact_path as two launches),
+each through the C ABI.  The default workload is the
 Qwen3-8B-shaped layer (c3: 32 query / 8 KV heads, head_dim 128, prefix 4096,
 best-first tree of 128 nodes), the configuration whose description includes
 all four steps; --workload c2/c4/c5 measure the others the same way.
@@ -237,6 +239,8 @@ def main(argv=None):
                     help="run one device-to-device copy of this many MiB first (counter calibration)")
     ap.add_argument("--ingest-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from two rocprofv3 --pmc output folders and exit")
+    ap.add_argument("--separate-commit", action="store_true",
+                    help="run the walk and the compaction as two launches")
     ap.add_argument("--warm", action="store_true",
                     help="reuse one input set every step (warm Infinity Cache); the default rotates "
                          "over enough copies to keep it cold, and roofline claims use the cold runs")
@@ -347,6 +351,9 @@ def main(argv=None):
                 P_(nxt), C_void(err.data_ptr() + 8), sp)
     cmp_args = [(P_(k), P_(v), P_(cu), P_(ks), P_(P), P_(alen), P_(aidx), B, T, wl.max_depth, k.shape[0], wl.hkv,
                  wl.d, code, P_(newlen), C_void(err.data_ptr() + 12), sp) for (q, k, v) in sets]
+    com_args = [(P_(parent), P_(draft), P_(target), P_(root), P_(cu), P_(ks), P_(P), B, T, wl.max_depth,
+                 k.shape[0], wl.hkv, wl.d, code, P_(k), P_(v), P_(alen), P_(aidx), P_(nxt), P_(newlen),
+                 C_void(err.data_ptr() + 8), sp) for (q, k, v) in sets]
 
     def step(i, ev=None):
         r = i % R
@@ -356,8 +363,11 @@ def main(argv=None):
         st |= L.tree_attn_verify(*attn_args[r])
         if ev is not None:
             ev[1].record(stream)
-        st |= L.tree_accept_greedy(*acc_args)
-        st |= L.kv_compact_path(*cmp_args[r])
+        if args.separate_commit:
+            st |= L.tree_accept_greedy(*acc_args)
+            st |= L.kv_compact_path(*cmp_args[r])
+        else:
+            st |= L.tree_accept_commit(*com_args[r])
         return st
 
     for i in range(args.warmup):
@@ -447,6 +457,7 @@ def main(argv=None):
                    "tree_nodes": T, "max_prefix": wl.max_prefix, "hq": wl.hq, "hkv": wl.hkv,
                    "head_dim": wl.d, "max_depth": wl.max_depth, "cold_cache_sets": R,
                    "cache": "warm" if args.warm else "cold",
+                   "commit": "two launches" if args.separate_commit else "one launch",
                    "workspace_bytes": ws_bytes, "host_enqueue_ms": t_host_enq * 1e3,
                    "spin_ahead_ms": spin_ms},
         "roofline": roof,

@@ -216,6 +216,32 @@ tv_status kv_compact_path(void *k_cache, void *v_cache, const int32_t *cu_nodes,
                           void *stream);
 
 /*
+ * tree_accept_commit -- tree_accept_greedy followed by kv_compact_path, in
+ * one launch.
+ *
+ * Defines: the two calls above ([TSD] "Verification and Acceptance
+ * Algorithms", greedy tree verification; [TSD] "KV Cache Rollback"), with
+ * the same readings; the outputs equal those of tree_accept_greedy then
+ * kv_compact_path on the same arguments.  Saves the second launch and the
+ * round trip through accept_len / accept_idx between them.
+ *
+ * In:  parent, draft_tokens, target_tokens [T]; root_target, kv_start,
+ *      prefix_len [B]; cu_nodes [B+1].
+ * In/out: k_cache, v_cache [kv_rows, hkv, head_dim] (16-byte aligned).
+ * Out: accept_len [B]; accept_idx [B, max_depth] (-1 after the path);
+ *      next_token [B]; new_kv_len [B] = P_b + accept_len[b].
+ * err: BAD_REQUEST (sizes as for tree_attn_verify).  Such a request is left
+ *      untouched: none of its outputs and none of its cache rows is written.
+ */
+tv_status tree_accept_commit(const int32_t *parent, const int32_t *draft_tokens,
+                             const int32_t *target_tokens, const int32_t *root_target,
+                             const int32_t *cu_nodes, const int32_t *kv_start, const int32_t *prefix_len,
+                             int32_t batch, int32_t total_nodes, int32_t max_depth, int64_t kv_rows,
+                             int32_t hkv, int32_t head_dim, tv_dtype dtype, void *k_cache, void *v_cache,
+                             int32_t *accept_len, int32_t *accept_idx, int32_t *next_token,
+                             int32_t *new_kv_len, int32_t *err, void *stream);
+
+/*
  * tree_select_topb -- the draft tree chosen in one step from a frontier ledger.
  *
  * Defines: [DT] section 3.3 and Appendix B: the frontier builder writes every

@@ -135,6 +135,33 @@ def test_compact_host_checks(L):
     assert compact(L, B=0) == OK
 
 
+def commit(L, parent=FAKE, dr=FAKE, tg=FAKE, root=FAKE, cu=FAKE, ks=FAKE, P=FAKE, B=1, T=16, D=16,
+           rows=1000, hkv=8, d=128, dtype=1, k=FAKE, v=FAKE, alen=FAKE, aidx=FAKE, nxt=FAKE, nl=FAKE):
+    return L.tree_accept_commit(parent, dr, tg, root, cu, ks, P, B, T, D, rows, hkv, d, dtype, k, v,
+                                alen, aidx, nxt, nl, None, None)
+
+
+def test_accept_commit_host_checks(L):
+    assert commit(L, parent=None) == NULL
+    assert commit(L, root=None) == NULL
+    assert commit(L, ks=None) == NULL
+    assert commit(L, k=None) == NULL
+    assert commit(L, aidx=None) == NULL
+    assert commit(L, nxt=None) == NULL
+    assert commit(L, nl=None) == NULL
+    assert commit(L, d=80) == DTYPE
+    assert commit(L, dtype=5) == DTYPE
+    assert commit(L, D=0) == SHAPE
+    assert commit(L, hkv=0) == SHAPE
+    assert commit(L, rows=-1) == SHAPE
+    assert commit(L, D=65) == LIMIT
+    assert commit(L, hkv=65536) == LIMIT
+    assert commit(L, B=-2) == SHAPE
+    assert commit(L, v=FAKE_ODD) == ALIGN
+    assert commit(L, B=0) == OK
+    assert commit(L, B=0, T=0, parent=None, dr=None, tg=None) == OK
+
+
 def test_binding_refuses_cpu_tensors(L):
     import torch
     x = torch.zeros(4, dtype=torch.int32)

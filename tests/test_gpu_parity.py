@@ -464,6 +464,104 @@ def test_compact_bad_path_reported_and_untouched():
     assert torch.equal(k0, d["k"])
 
 
+# ---------------------------------------------------------------------------
+# tree_accept_commit: the walk and the compaction in one launch
+# ---------------------------------------------------------------------------
+
+def check_accept_commit(wl, d, md):
+    """The fused call against the oracle's walk followed by its compaction."""
+    k0, v0 = to_np(d["k"]), to_np(d["v"])
+    alen, aidx, nxt, nl, err = B().tree_accept_commit(d["parent"], d["draft"], d["target"], d["root"], d["cu"],
+                                                      d["ks"], d["P"], d["k"], d["v"], md)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ralen, raidx, rnxt = O.accept_greedy(wl.parent, wl.draft, wl.target, wl.root_target, wl.cu_nodes, md)
+    rk, rv, rnl = O.kv_compact(k0, v0, wl.kv_start, wl.prefix_len, ralen, raidx)
+    assert np.array_equal(to_np(alen), ralen) and np.array_equal(to_np(aidx), raidx)
+    assert np.array_equal(to_np(nxt), rnxt) and np.array_equal(to_np(nl), rnl)
+    assert np.array_equal(to_np(d["k"]).view(np.uint32), rk.view(np.uint32))
+    assert np.array_equal(to_np(d["v"]).view(np.uint32), rv.view(np.uint32))
+    return ralen
+
+
+@pytest.mark.parametrize("name,seed,force", [(n, s, f) for n in W.CONFIGS for s in (0, 1) for f in (False, True)])
+def test_accept_commit_parity(name, seed, force):
+    announce(f"accept_commit {name} seed {seed} force={force}")
+    wl = W.make_workload(name, seed=seed, force_path=force)
+    ralen = check_accept_commit(wl, dev_workload(wl), wl.max_depth)
+    if force:
+        assert ralen.max() >= 1
+
+
+@pytest.mark.parametrize("md", [1, 5])
+def test_accept_commit_short_max_depth(md):
+    """A walk cut short by max_depth commits only the rows it accepted."""
+    announce(f"accept_commit max_depth {md}")
+    wl = W.make_workload("c5", seed=3, force_path=True)
+    check_accept_commit(wl, dev_workload(wl), md)
+
+
+def test_accept_commit_ragged_batch():
+    """Empty, single-node, 1023..1500-node (past the register-held walk) and
+    small requests in one call, fp32 cache with head_dim 64: the walk from
+    memory, the register walk and every row width of the gather against the
+    oracle."""
+    announce("accept_commit ragged batch")
+    rng = np.random.default_rng(21)
+    sizes = [0, 1, 1500, 37, 1025, 1024, 2, 130]
+    trees = []
+    for n in sizes:
+        p = (np.arange(n) - 1) // 4            # 4-ary heap keeps 1500 nodes within depth 6
+        p[0:1] = -1
+        trees.append(p.astype(np.int32))
+    wl = W.make_from_trees(trees, [int(x) for x in rng.integers(0, 40, len(sizes))], hq=2, hkv=2, d=64,
+                           dtype="f32", seed=8, vocab=5)
+    # most drafts carry the token their parent's target chose, so paths run deep
+    for b in range(len(sizes)):
+        s = wl.nodes_of(b)
+        p = wl.parent[s]
+        want = np.where(p < 0, wl.root_target[b], wl.target[s][np.maximum(p, 0)])
+        keep = rng.random(len(p)) < 0.8
+        keep[:1] = True                        # the root's only child always matches
+        wl.draft[s] = np.where(keep, want, wl.draft[s])
+    ralen = check_accept_commit(wl, dev_workload(wl), 16)
+    assert ralen[2] >= 3 and ralen[4] >= 3
+
+
+def test_accept_commit_bad_request_untouched():
+    """A request whose sizes do not fit the cache is reported and left alone:
+    no output and no cache row of it is written; the other requests are
+    committed."""
+    announce("accept_commit bad request")
+    wl = W.make_workload("c5", seed=0, force_path=True)
+    d = dev_workload(wl)
+    d["P"][2] = -5
+    k0, v0 = to_np(d["k"]), to_np(d["v"])
+    sentinel = -7
+    B_ = wl.batch
+    alen = torch.full((B_,), sentinel, dtype=torch.int32, device="cuda")
+    aidx = torch.full((B_, wl.max_depth), sentinel, dtype=torch.int32, device="cuda")
+    nxt = torch.full((B_,), sentinel, dtype=torch.int32, device="cuda")
+    nl = torch.full((B_,), sentinel, dtype=torch.int32, device="cuda")
+    _, _, _, _, err = B().tree_accept_commit(d["parent"], d["draft"], d["target"], d["root"], d["cu"], d["ks"],
+                                             d["P"], d["k"], d["v"], wl.max_depth, accept_len=alen,
+                                             accept_idx=aidx, next_token=nxt, new_kv_len=nl)
+    torch.cuda.synchronize()
+    assert int(err.item()) == (3 << 24) | 2
+    assert int(alen[2]) == sentinel and int(nxt[2]) == sentinel and int(nl[2]) == sentinel
+    assert (to_np(aidx)[2] == sentinel).all()
+    ralen, raidx, rnxt = O.accept_greedy(wl.parent, wl.draft, wl.target, wl.root_target, wl.cu_nodes, wl.max_depth)
+    P = wl.prefix_len.copy()
+    ralen_ok = ralen.copy()
+    ralen_ok[2] = 0                               # request 2 commits nothing
+    rk, rv, rnl = O.kv_compact(k0, v0, wl.kv_start, P, ralen_ok, raidx)
+    others = [b for b in range(B_) if b != 2]
+    assert np.array_equal(to_np(alen)[others], ralen[others])
+    assert np.array_equal(to_np(nl)[others], rnl[others])
+    assert np.array_equal(to_np(d["k"]).view(np.uint32), rk.view(np.uint32))
+    assert np.array_equal(to_np(d["v"]).view(np.uint32), rv.view(np.uint32))
+
+
 def test_full_pass_c3():
     """The whole pass on the Qwen3-8B-shaped layer: mask -> attention ->
     acceptance -> compaction, every output against the oracle."""

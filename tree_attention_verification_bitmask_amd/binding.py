@@ -58,6 +58,9 @@ def lib() -> C.CDLL:
     L.kv_compact_path.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, C.c_int,
                                   vp, vp, vp]
     L.kv_compact_path.restype = C.c_int
+    L.tree_accept_commit.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, C.c_int,
+                                     vp, vp, vp, vp, vp, vp, vp, vp]
+    L.tree_accept_commit.restype = C.c_int
     L.tree_select_topb.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp]
     L.tree_select_topb.restype = C.c_int
     L.tree_target_argmax.argtypes = [vp, i32, i32, C.c_int, vp, vp]
@@ -233,6 +236,38 @@ def kv_compact_path(k_cache, v_cache, cu_nodes, kv_start, prefix_len, accept_len
         _ptr(accept_len), _ptr(accept_idx), B, total_nodes, max_depth, rows, hkv, d, code,
         _ptr(new_kv_len), _ptr(err), _stream(stream)))
     return new_kv_len, err
+
+
+def tree_accept_commit(parent, draft_tokens, target_tokens, root_target, cu_nodes, kv_start, prefix_len,
+                       k_cache, v_cache, max_depth: int, accept_len=None, accept_idx=None, next_token=None,
+                       new_kv_len=None, err=None, stream=None):
+    """tree_accept_greedy then kv_compact_path in one launch; gathers the
+    accepted rows in place; -> (accept_len, accept_idx, next_token, new_kv_len, err)."""
+    import torch
+    rows, hkv, d = k_cache.shape
+    code = _dtype_code(k_cache)
+    B = cu_nodes.numel() - 1
+    T = parent.numel()
+    dev = k_cache.device
+    _need(k_cache, "k_cache")
+    _need(v_cache, "v_cache", k_cache.dtype, k_cache.numel())
+    for t, n in ((parent, "parent"), (draft_tokens, "draft_tokens"), (target_tokens, "target_tokens"),
+                 (root_target, "root_target"), (cu_nodes, "cu_nodes"), (kv_start, "kv_start"),
+                 (prefix_len, "prefix_len")):
+        _need(t, n, torch.int32)
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    accept_idx = (torch.empty((B, max_depth), dtype=torch.int32, device=dev)
+                  if accept_idx is None else accept_idx)
+    next_token = torch.empty(B, dtype=torch.int32, device=dev) if next_token is None else next_token
+    new_kv_len = torch.empty(B, dtype=torch.int32, device=dev) if new_kv_len is None else new_kv_len
+    err = torch.zeros(1, dtype=torch.int32, device=dev) if err is None else err
+    _need(accept_idx, "accept_idx", torch.int32, B * max_depth)
+    _check("tree_accept_commit", lib().tree_accept_commit(
+        _ptr(parent), _ptr(draft_tokens), _ptr(target_tokens), _ptr(root_target), _ptr(cu_nodes),
+        _ptr(kv_start), _ptr(prefix_len), B, T, max_depth, rows, hkv, d, code, _ptr(k_cache),
+        _ptr(v_cache), _ptr(accept_len), _ptr(accept_idx), _ptr(next_token), _ptr(new_kv_len),
+        _ptr(err), _stream(stream)))
+    return accept_len, accept_idx, next_token, new_kv_len, err
 
 
 def tree_select_topb(score, parent, token, budget: int, beta: float = 0.0, tree_parent=None,

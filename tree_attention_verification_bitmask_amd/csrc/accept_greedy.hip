@@ -14,50 +14,11 @@
 // target tokens are staged in LDS for the acceptability test and the final
 // next token.  A request above TV_MAX_NODES nodes (the call takes no node
 // cap) falls back to testing candidates from global memory at each step.
-#include "tv_device.h"
+#include "path_walk.h"
 #include "tv_launch.h"
 
 namespace tv {
 namespace {
-
-constexpr int kPerLane = (TV_MAX_NODES + 63) / 64;  // nodes held per lane
-
-// The same walk for a request too large to hold in registers: each step
-// tests the candidates (parent == current, draft == wanted token) 64 at a
-// time from global memory and a ballot picks the lowest matching index.
-__device__ void walk_global(const int32_t *par, const int32_t *dr, const int32_t *tg, int n,
-                            int want, int max_depth, int32_t *idx, int32_t *len_out,
-                            int32_t *next_out) {
-    const int lane = threadIdx.x;
-    int cur = -1;
-    int len = 0;
-    while (len < max_depth) {
-        int found = -1;
-        for (int base = 0; base < n; base += 64) {
-            const int j = base + lane;
-            bool m = false;
-            if (j < n) {
-                const int dj = dr[j];
-                m = (par[j] == cur) && (dj >= 0) && (dj == want);
-            }
-            const unsigned long long bal = __ballot(m);
-            if (bal) {
-                found = base + __builtin_ctzll(bal);
-                break;
-            }
-        }
-        if (found < 0) break;
-        if (lane == 0) idx[len] = found;
-        ++len;
-        cur = found;
-        want = tg[found];
-    }
-    for (int j = len + lane; j < max_depth; j += 64) idx[j] = -1;
-    if (lane == 0) {
-        *len_out = len;
-        *next_out = want;
-    }
-}
 
 __global__ void __launch_bounds__(64) accept_greedy_kernel(
     const int32_t *__restrict__ parent, const int32_t *__restrict__ draft,
@@ -85,64 +46,15 @@ __global__ void __launch_bounds__(64) accept_greedy_kernel(
         walk_global(par, dr, tg, n, root_want, max_depth, idx, accept_len + b, next_token + b);
         return;
     }
-    const int nk = (n + 63) / 64;  // wave-uniform
-
-    int pk[kPerLane];
-    int dk[kPerLane];
-    int tk[kPerLane];
-    // every load first, then the LDS stores: a store right after its load
-    // would wait for it, one memory round trip per 64 nodes
-#pragma unroll
-    for (int k = 0; k < kPerLane; ++k) {
-        const int j = 64 * k + lane;
-        pk[k] = -2;
-        dk[k] = -1;
-        tk[k] = 0;
-        if (k < nk && j < n) {
-            pk[k] = par[j];
-            dk[k] = dr[j];
-            tk[k] = tg[j];
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < kPerLane; ++k) {
-        const int j = 64 * k + lane;
-        if (k < nk && j < n) stg[j] = tk[k];
-    }
+    int pk[kWalkPerLane];
+    int dk[kWalkPerLane];
+    walk_load(par, dr, tg, n, pk, dk, stg);
     __syncthreads();
-    // acceptable[j]: draft[j] == the target's choice at parent[j]
-    uint32_t okbits = 0;
-#pragma unroll
-    for (int k = 0; k < kPerLane; ++k) {
-        if (k < nk) {
-            const int p = pk[k];
-            const int want = p == -1 ? root_want : (p >= 0 && p < n ? stg[p] : -1);
-            if (dk[k] >= 0 && dk[k] == want) okbits |= 1u << k;
-        }
-    }
-
-    int cur = -1;
-    int len = 0;
-    while (len < max_depth) {
-        int found = -1;
-#pragma unroll
-        for (int k = 0; k < kPerLane; ++k) {
-            if (k >= nk) break;
-            const unsigned long long bal = __ballot(((okbits >> k) & 1u) && pk[k] == cur);
-            if (bal) {
-                found = 64 * k + __builtin_ctzll(bal);
-                break;
-            }
-        }
-        if (found < 0) break;
-        if (lane == 0) idx[len] = found;
-        ++len;
-        cur = found;
-    }
-    for (int j = len + lane; j < max_depth; j += 64) idx[j] = -1;
+    int next;
+    const int len = walk_registers(pk, dk, stg, n, root_want, max_depth, idx, &next);
     if (lane == 0) {
         accept_len[b] = len;
-        next_token[b] = cur < 0 ? root_want : stg[cur];
+        next_token[b] = next;
     }
 }
 

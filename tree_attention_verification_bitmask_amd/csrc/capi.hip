@@ -193,6 +193,33 @@ tv_status kv_compact_path(void *k_cache, void *v_cache, const int32_t *cu_nodes,
                                                (hipStream_t)stream));
 }
 
+tv_status tree_accept_commit(const int32_t *parent, const int32_t *draft_tokens,
+                             const int32_t *target_tokens, const int32_t *root_target,
+                             const int32_t *cu_nodes, const int32_t *kv_start, const int32_t *prefix_len,
+                             int32_t batch, int32_t total_nodes, int32_t max_depth, int64_t kv_rows,
+                             int32_t hkv, int32_t head_dim, tv_dtype dtype, void *k_cache, void *v_cache,
+                             int32_t *accept_len, int32_t *accept_idx, int32_t *next_token,
+                             int32_t *new_kv_len, int32_t *err, void *stream) {
+    tv_status st = check_batch(batch, total_nodes);
+    if (st != TV_OK) return st;
+    if (max_depth < 1 || hkv < 1 || kv_rows < 0) return TV_ERR_SHAPE;
+    if (max_depth > TV_MAX_DEPTH || hkv > 65535) return TV_ERR_LIMIT;
+    if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_DTYPE;
+    if (head_dim != 64 && head_dim != 128) return TV_ERR_DTYPE;
+    if (!cu_nodes || !root_target || !kv_start || !prefix_len || !accept_len || !accept_idx ||
+        !next_token || !new_kv_len)
+        return TV_ERR_NULL;
+    if (total_nodes > 0 && (!parent || !draft_tokens || !target_tokens)) return TV_ERR_NULL;
+    if (kv_rows > 0 && (!k_cache || !v_cache)) return TV_ERR_NULL;
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16)) return TV_ERR_ALIGN;
+    if (batch == 0) return TV_OK;
+    return launch_status(tv::launch_accept_commit(parent, draft_tokens, target_tokens, root_target, cu_nodes,
+                                                  kv_start, prefix_len, batch, total_nodes, max_depth,
+                                                  kv_rows, hkv, head_dim, dtype, k_cache, v_cache,
+                                                  accept_len, accept_idx, next_token, new_kv_len, err,
+                                                  (hipStream_t)stream));
+}
+
 tv_status tree_select_topb(const float *score, const int32_t *parent, const int32_t *token,
                            int32_t batch, int32_t depth, int32_t lanes, int32_t budget, float beta,
                            int32_t *tree_parent, int32_t *tree_token, int32_t *n_real, int32_t *err,

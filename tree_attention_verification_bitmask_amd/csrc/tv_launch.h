@@ -19,6 +19,13 @@ hipError_t launch_accept_greedy(const int32_t *parent, const int32_t *draft, con
                                 int total_nodes, int max_depth, int32_t *accept_len, int32_t *accept_idx,
                                 int32_t *next_token, int32_t *err, hipStream_t stream);
 
+hipError_t launch_accept_commit(const int32_t *parent, const int32_t *draft, const int32_t *target,
+                                const int32_t *root_target, const int32_t *cu_nodes,
+                                const int32_t *kv_start, const int32_t *prefix_len, int batch,
+                                int total_nodes, int max_depth, int64_t kv_rows, int hkv, int head_dim,
+                                tv_dtype dtype, void *k, void *v, int32_t *accept_len,
+                                int32_t *accept_idx, int32_t *next_token, int32_t *new_len, int32_t *err,
+                                hipStream_t stream);
 hipError_t launch_kv_compact(void *k, void *v, const int32_t *cu_nodes, const int32_t *kv_start,
                              const int32_t *prefix_len, const int32_t *accept_len,
                              const int32_t *accept_idx, int batch, int total_nodes, int max_depth,
