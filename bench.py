@@ -1,15 +1,19 @@
 """Benchmark of the tree-verification pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5]
 
 One step = the whole pass over one batch of synthetic inputs already resident
 in HBM: tree_mask_build -> tree_attn_verify -> tree_accept_commit (the
 acceptance walk and the compaction of the accepted path in one launch; with
 --separate-commit, tree_accept_greedy -> kv_compact_path as two launches),
-each through the C ABI.  The default workload is the
-Qwen3-8B-shaped layer (c3: 32 query / 8 KV heads, head_dim 128, prefix 4096,
-best-first tree of 128 nodes), the configuration whose description includes
-all four steps; --workload c2/c4/c5 measure the others the same way.
+each through the C ABI.  The default (headline) workload is c5, the largest
+configuration that one GPU holds: eight concurrent requests in the Qwen3-8B
+head layout (32 query / 8 KV heads, head_dim 128) with ragged prefixes of
+2048-8192 tokens and trees of 32-128 nodes in one varlen launch.  The same
+run then measures the two other Qwen3-8B-shaped layers, c3 (prefix 4096,
+128-node best-first tree) and c4 (prefix 8192, 256-node width-first tree), the
+same way and reports them under "per_config"; --secondary none skips them and
+--workload picks another headline.
 
 Timing:
   * cold cache: inputs rotate over R copies with R x footprint >= 512 MiB, so
@@ -231,7 +235,11 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c3", choices=sorted(W.CONFIGS))
+    ap.add_argument("--workload", default="c5", choices=sorted(W.CONFIGS),
+                    help="headline workload (default c5, the largest single-GPU configuration)")
+    ap.add_argument("--secondary", default="",
+                    help="comma-separated workloads measured after the headline and reported under "
+                         "per_config (default c3,c4; 'none' for none)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -304,7 +312,42 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src_c, dst_c
 
-    wl = W.make_workload(args.workload, seed=args.seed, force_path=True)
+    names = [args.workload]
+    if args.secondary != "none":
+        names += [n for n in (args.secondary.split(",") if args.secondary else ("c3", "c4")) if n != args.workload]
+    lines = {}
+    for name in names:
+        seed = args.seed if name == args.workload else 0
+        wl = W.make_workload(name, seed=seed, force_path=True)
+        lines[name] = time_pass(args, torch, BND, L, dev, wl, args.steps, args.warmup)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    line = lines.pop(args.workload)
+    # Secondary denominator: the HBM rate a plain device-to-device copy reaches
+    # on this GPU (read + write bytes over time), measured after the timed
+    # regions.  (Skipped in counter runs: the traffic calibration takes the
+    # largest copy in the trace as its reference.)
+    copy_gbs = hbm_copy_probe(torch, dev) if args.calib_copy_mib == 0 else None
+    for ln in [line, *lines.values()]:
+        roof = ln["roofline"]
+        roof["hbm_copy_probe_gbs"] = copy_gbs
+        roof["frac_of_copy_probe"] = roof["achieved_gbs"] / copy_gbs if copy_gbs else None
+    if lines:
+        line["per_config"] = {
+            name: {"workload": ln["config"]["workload"], "value": ln["value"], "unit": ln["unit"],
+                   "ms_per_step": ln["ms_per_step"], "steps": ln["steps"], "config": ln["config"],
+                   "roofline": ln["roofline"]}
+            for name, ln in lines.items()}
+    if not args.no_cpu_baseline:
+        wl = W.make_workload(args.workload, seed=args.seed, force_path=True)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def time_pass(args, torch, BND, L, dev, wl, steps: int, warmup: int) -> dict:
+    """Times `steps` steps of the pass on workload wl (after `warmup` untimed
+    ones) and returns the JSON line's fields for it (without cpu_baseline)."""
     fdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     code = BND.TV_BF16 if wl.dtype == "bf16" else BND.TV_F32
     es = 2 if wl.dtype == "bf16" else 4
@@ -370,14 +413,14 @@ def main(argv=None):
             st |= L.tree_accept_commit(*com_args[r])
         return st
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         if step(i):
             raise RuntimeError("a call was rejected during warmup")
     torch.cuda.synchronize()
     if int(err.abs().sum().item()) != 0:
         raise RuntimeError(f"device error words {err.tolist()}")
 
-    K = args.steps
+    K = steps
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     # calibrate the spin kernel, then queue enough spin to cover the host's
@@ -400,7 +443,7 @@ def main(argv=None):
     t_host0 = time.perf_counter()
     status = 0
     for i in range(K):
-        status |= step(args.warmup + i, evs[i])
+        status |= step(warmup + i, evs[i])
     end.record(stream)
     t_host_enq = time.perf_counter() - t_host0
     torch.cuda.synchronize()
@@ -422,7 +465,7 @@ def main(argv=None):
     else:
         roof = {"bound": "hbm", "achieved": byts / (attn_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    traffic, tdetail = load_traffic(args.workload)
+    traffic, tdetail = load_traffic(wl.name)
     roof["traffic"] = traffic
     roof["traffic_detail"] = tdetail
     roof.update({"kernel": "tree_attn_verify", "avg_us": attn_us,
@@ -436,9 +479,6 @@ def main(argv=None):
     # on this GPU (read + write bytes over time), measured after the timed region.
     # (Skipped in counter runs: the traffic calibration takes the largest copy
     # in the trace as its reference.)
-    copy_gbs = hbm_copy_probe(torch, dev) if args.calib_copy_mib == 0 else None
-    roof["hbm_copy_probe_gbs"] = copy_gbs
-    roof["frac_of_copy_probe"] = roof["achieved_gbs"] / copy_gbs if copy_gbs else None
 
     line = {
         "metric": METRIC,
@@ -446,7 +486,7 @@ def main(argv=None):
         "unit": "tree-tokens/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -462,10 +502,7 @@ def main(argv=None):
                    "spin_ahead_ms": spin_ms},
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
-    print(json.dumps(line), flush=True)
-    return 0
+    return line
 
 
 def bench_select(args, torch, BND, L, dev):

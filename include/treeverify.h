@@ -163,6 +163,57 @@ tv_status tree_attn_verify(const void *q, const void *k_cache, const void *v_cac
                            void *workspace, size_t workspace_bytes, int32_t *err, void *stream);
 
 /*
+ * Plan overrides for tree_attn_verify: tuning and tests only.
+ *
+ * tree_attn_verify picks its own plan (how many slices of the key axis each
+ * query-row tile is cut into, and for batches whether a device-side planner
+ * orders the tasks longest first) from the host sizes alone, so its workspace
+ * size is a pure function of them.  The _ex variants below take an explicit
+ * override instead; a NULL override, or zero fields, give exactly the plain
+ * calls' plan.  They exist so that tuning sweeps and the tests can reach every
+ * plan the kernels support; the results are the same attention (each slice
+ * count and order computes the same sums, rounded differently).
+ *   splits: key-axis slices per row tile, 0 = the library's choice (clamped
+ *           to [1, number of 32-key chunks]);
+ *   order:  batches only: TV_ORDER_AUTO (the library's choice), TV_ORDER_STATIC
+ *           (workgroups take tasks in a fixed order) or TV_ORDER_PLANNED (a
+ *           planner launch orders them longest first, when the plan is small
+ *           enough for it).
+ */
+enum { TV_ORDER_AUTO = 0, TV_ORDER_STATIC = 1, TV_ORDER_PLANNED = 2 };
+typedef struct {
+    int32_t splits;
+    int32_t order;
+    int32_t reserved[6]; /* must be zero */
+} tv_attn_plan_override;
+
+size_t tree_attn_verify_workspace_size_ex(int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                                          int32_t max_prefix, int32_t hq, int32_t hkv, int32_t head_dim,
+                                          tv_dtype dtype, const tv_attn_plan_override *ov);
+tv_status tree_attn_verify_ex(const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *cu_nodes, const int32_t *kv_start, const int32_t *prefix_len,
+                              const uint64_t *anc_bits, int32_t batch, int32_t total_nodes,
+                              int32_t max_nodes, int32_t max_prefix, int64_t kv_rows, int32_t hq,
+                              int32_t hkv, int32_t head_dim, float scale, tv_dtype dtype, void *out,
+                              void *workspace, size_t workspace_bytes, int32_t *err,
+                              const tv_attn_plan_override *ov, void *stream);
+
+/*
+ * tree_attn_verify_plan -- the plan tree_attn_verify(_ex) would run for these
+ * host sizes (pure host arithmetic; tuning and tests).  Writes info[0..7]:
+ *   [0] 1 = matrix-core kernel, 0 = vector kernel (fp32, or too few rows)
+ *   [1] query rows per workgroup tile   [2] row tiles per (request, KV head)
+ *   [3] key-axis slices                 [4] keys per slice
+ *   [5] 1 = planned (longest-first) task order for a batch
+ *   [6] chunks copied ahead of use      [7] workspace bytes (saturated to
+ *       INT32_MAX)
+ * Returns the same host-side status the call itself would for these sizes.
+ */
+tv_status tree_attn_verify_plan(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_prefix,
+                                int32_t hq, int32_t hkv, int32_t head_dim, tv_dtype dtype,
+                                const tv_attn_plan_override *ov, int32_t *info);
+
+/*
  * tree_accept_greedy -- temperature-0 acceptance walk.
  *
  * Defines: [TSD] "Verification and Acceptance Algorithms", greedy tree
@@ -205,8 +256,10 @@ tv_status tree_accept_greedy(const int32_t *parent, const int32_t *draft_tokens,
  *      [B, max_depth] as produced by tree_accept_greedy.
  * Out: new_kv_len [B] int32.
  * err: BAD_REQUEST (sizes as for tree_attn_verify, or L_b outside
- *      [0, max_depth]); BAD_PATH (an accept_idx entry outside [0, N_b)).
- *      Such a request is left untouched.
+ *      [0, min(max_depth, N_b)], as for kv_rollback_token_table: the gather
+ *      writes rows P_b .. P_b + L_b - 1, which must lie inside the request);
+ *      BAD_PATH (an accept_idx entry outside [0, N_b)).  Such a request is
+ *      left untouched.
  */
 tv_status kv_compact_path(void *k_cache, void *v_cache, const int32_t *cu_nodes,
                           const int32_t *kv_start, const int32_t *prefix_len,
@@ -244,14 +297,15 @@ tv_status tree_accept_commit(const int32_t *parent, const int32_t *draft_tokens,
 /*
  * tree_select_topb -- the draft tree chosen in one step from a frontier ledger.
  *
- * Defines: [DT] section 3.3 and Appendix B: the frontier builder writes every
- * scored candidate to a ledger [batch, D, W*k] with its cumulative
- * log-probability and parent pointer; after the last depth the tree is the
- * ledger's global top B, ordered so parents precede children, parent pointers
- * remapped, short trees padded with dead leaves.  [DAR] "2. Deferred
- * Best-First Pruning": the same global top B with a depth bonus beta added
- * to each candidate's score; for beta <= 0 (and W = B) it equals the
- * sequential best-first heap's tree.
+ * Defines: [DT] section 3.3 and Appendix B.  The drafter records each
+ * candidate it scores in a ledger of shape [batch, D, W*k] (path
+ * log-probability plus the slot of its parent) and picks the tree in one step
+ * once all depths are drafted: the B highest-scoring records of the request,
+ * renumbered parents-first with their parent slots translated, and topped up
+ * with never-accepted leaves when fewer than B records exist.  [DAR]
+ * "2. Deferred Best-First Pruning" adds a per-level bonus beta to every score
+ * before the same pick; with beta <= 0 (and W = B) the pick is the tree a
+ * sequential best-first heap would grow.
  * Readings: key = score + beta * level (level = t + 1 for ledger depth t),
  * evaluated in double; keys rank descending, equal keys by depth then slot;
  * the output lists the chosen candidates in that rank order; a dead leaf has

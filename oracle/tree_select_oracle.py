@@ -6,14 +6,18 @@ library and its Python binding) never does and shares no code with it.
 
 Pages followed:
   [DT]  "DominoTree: Conditional Tree-Structured Drafting with Domino for
-        Speculative Decoding" (arXiv 2607.08642), section 3.3 (the frontier
-        builder: W lanes per request advanced depth by depth, every scored
-        candidate written to a ledger with its cumulative log-probability and
-        parent pointer, the tree selected once as the ledger's global top B)
-        and Appendix B (the selection steps -- global top B, parents before
-        children, parent pointers remapped, short trees padded with dead
-        leaves -- and why, with W = B, the result is the best-first heap's
-        tree: a child never scores above its parent).
+        Speculative Decoding" (arXiv 2607.08642), section 3.3 and Appendix B.
+        In short: the drafter keeps W frontier lanes per request and grows
+        them one depth at a time; each candidate it scores is recorded once
+        (its path log-probability and the slot of its parent), and only after
+        the last depth is the tree picked, in one step, as the B best records
+        overall.  The picked records are then renumbered so that every parent
+        comes before its children, the parent slots are translated into the
+        new numbering, and a request with fewer than B usable records is
+        filled up with leaves that can never be accepted.  Because extending
+        a path never raises its log-probability, the B best records already
+        contain every ancestor of each one they contain, which is why (with
+        W = B) the pick agrees with a best-first heap.
   [DAR] "DARTree: Speculative Diffusion Decoding with Autoregressive Draft
         Trees" (gist.science), Technical Summary, "2. Deferred Best-First
         Pruning": one global top-B over the fixed-width supertree, equal to

@@ -103,6 +103,44 @@ def test_workspace_sizes(L):
     assert L.tree_attn_verify_workspace_size(1, 16, 16, 128, 3, 2, 64, 1) == 0
 
 
+def test_attn_plan_is_a_function_of_its_arguments(L, monkeypatch):
+    """The plan (and so the workspace size) depends on the host sizes and the
+    explicit override only: the process environment plays no part."""
+    sizes = (1, 128, 128, 4096, 32, 8, 128, BND.TV_BF16)
+    base = BND.tree_attn_verify_plan(*sizes)
+    ws = L.tree_attn_verify_workspace_size(*sizes)
+    assert base["mfma"] == 1 and base["workspace_bytes"] == ws
+    for name in ("TV_MFMA_SPLITS", "TV_MFMA_PLAN"):
+        monkeypatch.setenv(name, "3")
+    assert BND.tree_attn_verify_plan(*sizes) == base
+    assert L.tree_attn_verify_workspace_size(*sizes) == ws
+    # the override changes the plan, and the _ex size follows it
+    p3 = BND.tree_attn_verify_plan(*sizes, splits=3)
+    assert p3["splits"] == 3 and p3["keys_per_split"] * 3 >= 4096 + 128
+    assert BND.tree_attn_verify_workspace_size(*sizes, splits=3) == p3["workspace_bytes"] < ws
+    # batches: planned order by default, static on request
+    bsz = (8, 634, 128, 7275, 32, 8, 128, BND.TV_BF16)
+    assert BND.tree_attn_verify_plan(*bsz)["planned"] == 1
+    assert BND.tree_attn_verify_plan(*bsz, order=BND.TV_ORDER_STATIC)["planned"] == 0
+
+
+def test_attn_override_checked(L):
+    ov = BND.PlanOverride(0, 0)
+    info = (C.c_int32 * 8)()
+    args = (1, 128, 128, 4096, 32, 8, 128, 1)
+    assert L.tree_attn_verify_plan(*args, C.byref(ov), info) == OK
+    assert L.tree_attn_verify_plan(*args, C.byref(ov), None) == NULL
+    assert L.tree_attn_verify_plan(*args, None, info) == OK
+    for bad in (BND.PlanOverride(-1, 0), BND.PlanOverride(0, 3), BND.PlanOverride(0, 0, (C.c_int32 * 6)(1))):
+        assert L.tree_attn_verify_plan(*args, C.byref(bad), info) == SHAPE
+        assert L.tree_attn_verify_workspace_size_ex(*args, C.byref(bad)) == 0
+    # the plain call's checks are the _ex call's checks
+    assert L.tree_attn_verify_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 128, 128, 4096, 4224, 30, 8, 128,
+                                 0.088, 1, FAKE, FAKE, 1 << 40, None, None, None) == SHAPE
+    assert L.tree_attn_verify_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 128, 4096, 4224, 32, 8, 128,
+                                 0.088, 1, FAKE, FAKE, 1 << 40, None, C.byref(ov), None) == OK
+
+
 def accept(L, parent=FAKE, dr=FAKE, tg=FAKE, root=FAKE, cu=FAKE, B=1, T=16, D=16, alen=FAKE,
            aidx=FAKE, nxt=FAKE):
     return L.tree_accept_greedy(parent, dr, tg, root, cu, B, T, D, alen, aidx, nxt, None, None)

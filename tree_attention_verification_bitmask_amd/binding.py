@@ -53,6 +53,13 @@ def lib() -> C.CDLL:
     L.tree_attn_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32, i32,
                                    f32, C.c_int, vp, vp, sz, vp, vp]
     L.tree_attn_verify.restype = C.c_int
+    L.tree_attn_verify_workspace_size_ex.argtypes = [i32, i32, i32, i32, i32, i32, i32, C.c_int, vp]
+    L.tree_attn_verify_workspace_size_ex.restype = sz
+    L.tree_attn_verify_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32, i32,
+                                      f32, C.c_int, vp, vp, sz, vp, vp, vp]
+    L.tree_attn_verify_ex.restype = C.c_int
+    L.tree_attn_verify_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, C.c_int, vp, vp]
+    L.tree_attn_verify_plan.restype = C.c_int
     L.tree_accept_greedy.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp]
     L.tree_accept_greedy.restype = C.c_int
     L.kv_compact_path.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, C.c_int,
@@ -154,16 +161,51 @@ def tree_mask_build(parent, cu_nodes, prefix_len, max_nodes: int, max_depth: int
     return anc, level, pos, err
 
 
+TV_ORDER_AUTO, TV_ORDER_STATIC, TV_ORDER_PLANNED = 0, 1, 2
+
+
+class PlanOverride(C.Structure):
+    """tv_attn_plan_override: key-axis slices (0 = the library's choice) and
+    the batch task order (TV_ORDER_*)."""
+    _fields_ = [("splits", C.c_int32), ("order", C.c_int32), ("reserved", C.c_int32 * 6)]
+
+
+def _override(splits: int = 0, order: int = TV_ORDER_AUTO):
+    if not splits and order == TV_ORDER_AUTO:
+        return None
+    return PlanOverride(int(splits), int(order))
+
+
 def tree_attn_verify_workspace_size(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim,
-                                    dtype_code) -> int:
-    return int(lib().tree_attn_verify_workspace_size(batch, total_nodes, max_nodes, max_prefix, hq,
-                                                     hkv, head_dim, dtype_code))
+                                    dtype_code, splits: int = 0, order: int = TV_ORDER_AUTO) -> int:
+    ov = _override(splits, order)
+    if ov is None:
+        return int(lib().tree_attn_verify_workspace_size(batch, total_nodes, max_nodes, max_prefix, hq,
+                                                         hkv, head_dim, dtype_code))
+    return int(lib().tree_attn_verify_workspace_size_ex(batch, total_nodes, max_nodes, max_prefix, hq, hkv,
+                                                        head_dim, dtype_code, C.byref(ov)))
+
+
+PLAN_FIELDS = ("mfma", "rows_per_tile", "row_tiles", "splits", "keys_per_split", "planned", "lookahead",
+               "workspace_bytes")
+
+
+def tree_attn_verify_plan(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype_code,
+                          splits: int = 0, order: int = TV_ORDER_AUTO) -> dict:
+    """The plan tree_attn_verify would run for these host sizes (no GPU needed)."""
+    ov = _override(splits, order)
+    info = (C.c_int32 * 8)()
+    _check("tree_attn_verify_plan", lib().tree_attn_verify_plan(
+        batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype_code,
+        C.byref(ov) if ov is not None else None, info))
+    return dict(zip(PLAN_FIELDS, (int(x) for x in info)))
 
 
 def tree_attn_verify(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc, max_nodes: int,
                      max_prefix: int, scale: float | None = None, out=None, workspace=None,
-                     err=None, stream=None):
-    """q [T, hq, d]; k_cache / v_cache [rows, hkv, d] -> out [T, hq, d] (same dtype)."""
+                     err=None, stream=None, splits: int = 0, order: int = TV_ORDER_AUTO):
+    """q [T, hq, d]; k_cache / v_cache [rows, hkv, d] -> out [T, hq, d] (same dtype).
+    splits / order: a plan override (tree_attn_verify_ex), for tuning and tests."""
     import torch
     T, hq, d = q.shape
     rows, hkv, d2 = k_cache.shape
@@ -181,16 +223,20 @@ def tree_attn_verify(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc, m
     out = torch.empty_like(q) if out is None else out
     _need(out, "out", q.dtype, q.numel())
     err = torch.zeros(1, dtype=torch.int32, device=q.device) if err is None else err
-    ws_bytes = tree_attn_verify_workspace_size(B, T, max_nodes, max_prefix, hq, hkv, d, code)
+    ws_bytes = tree_attn_verify_workspace_size(B, T, max_nodes, max_prefix, hq, hkv, d, code, splits, order)
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if scale is None:
         scale = d ** -0.5
-    _check("tree_attn_verify", lib().tree_attn_verify(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_nodes), _ptr(kv_start), _ptr(prefix_len),
-        _ptr(anc), B, T, max_nodes, max_prefix, rows, hq, hkv, d, float(scale), code, _ptr(out),
-        _ptr(workspace), ws_have, _ptr(err), _stream(stream)))
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_nodes), _ptr(kv_start), _ptr(prefix_len),
+            _ptr(anc), B, T, max_nodes, max_prefix, rows, hq, hkv, d, float(scale), code, _ptr(out),
+            _ptr(workspace), ws_have, _ptr(err))
+    ov = _override(splits, order)
+    if ov is None:
+        _check("tree_attn_verify", lib().tree_attn_verify(*args, _stream(stream)))
+    else:
+        _check("tree_attn_verify_ex", lib().tree_attn_verify_ex(*args, C.byref(ov), _stream(stream)))
     return out
 
 

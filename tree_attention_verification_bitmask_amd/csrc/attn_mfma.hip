@@ -965,16 +965,10 @@ __global__ void __launch_bounds__(kPlanThreads) attn_plan_kernel(KParams p, int 
     }
 }
 
-int env_int(const char *name, int dflt) {
-    const char *s = getenv(name);
-    if (!s || !*s) return dflt;
-    return atoi(s);
-}
-
 }  // namespace
 
 MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefix, int hq, int hkv,
-                        int head_dim, tv_dtype dtype) {
+                        int head_dim, tv_dtype dtype, const tv_attn_plan_override *ov) {
     (void)total_nodes;
     MfmaPlan plan;
     const int G = hkv > 0 ? hq / hkv : 0;
@@ -987,19 +981,17 @@ MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefi
     const int span = max_prefix + max_nodes;  // longest key axis
     const int chunks = (span + kChunk - 1) / kChunk;
     const long base_tasks = (long)batch * hkv * plan.row_tiles;
-    // Fill the chip: one workgroup per CU (256 CUs) for a single request;
-    // about two and a half rounds for several (ragged) requests, so short
-    // ones leave room to balance.  A tuning override (TV_MFMA_SPLITS) may fix
-    // the count instead.
+    // Fill the chip: one workgroup per CU (256 CUs) for a single request.
     // Batches that the planner can order take about four rounds of short
-    // slices (8 at c5); otherwise about two and a half in the static order.
+    // slices (8 at c5); otherwise about two and a half in the static order,
+    // so short requests leave room to balance.  The override (tuning and
+    // tests) may fix the slice count or the batch order instead.
     const long planned = (long)batch * hkv * plan.row_tiles;  // tasks per slice
-    // (TV_MFMA_PLAN=0 keeps the static order for batches too: tuning, and
-    // the tests of that order)
-    const bool can_plan = batch > 1 && env_int("TV_MFMA_PLAN", 1) != 0;
+    const int order = ov ? ov->order : TV_ORDER_AUTO;
+    const bool can_plan = batch > 1 && order != TV_ORDER_STATIC;
     const long target = batch == 1 ? 256 : (can_plan ? 1024 : 640);
     int splits = (int)((target + base_tasks - 1) / base_tasks);
-    splits = env_int("TV_MFMA_SPLITS", splits);
+    if (ov && ov->splits > 0) splits = ov->splits;
     if (splits < 1) splits = 1;
     if (splits > chunks) splits = chunks;
     const int cps = (chunks + splits - 1) / splits;  // chunks per split
@@ -1020,6 +1012,10 @@ MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefi
         }
     }
     return plan;
+}
+
+int attn_mfma_lookahead(const MfmaPlan &plan) {
+    return plan.keys_per_split / kChunk <= kShortSlice ? kAheadShort : kAhead;
 }
 
 hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *workspace, hipStream_t stream) {
@@ -1070,7 +1066,7 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *works
     const bool wide = plan.splits <= 8;
     // short slices: the prologue outweighs the loop, so fewer chunks are
     // copied ahead of the first barrier
-    const bool short_slices = plan.keys_per_split / kChunk <= kShortSlice;
+    const bool short_slices = attn_mfma_lookahead(plan) == kAheadShort;
     const long cwaves = tiles * kWaves * (a.head_dim / 32) * (wide ? 1 : 4);
     const long cblocks = (cwaves + kCombineWaves - 1) / kCombineWaves;
     if (a.head_dim == 128) {

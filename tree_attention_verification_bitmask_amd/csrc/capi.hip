@@ -52,6 +52,32 @@ tv_status check_gdn_conv(int32_t total_or_batch, int32_t channels, int32_t conv_
     return TV_OK;
 }
 
+// Host-side checks of an override: every reserved field zero, known order.
+bool override_ok(const tv_attn_plan_override *ov) {
+    if (!ov) return true;
+    for (int i = 0; i < 6; ++i)
+        if (ov->reserved[i] != 0) return false;
+    return ov->splits >= 0 && ov->order >= TV_ORDER_AUTO && ov->order <= TV_ORDER_PLANNED;
+}
+
+// The size checks shared by the call and its plan query; fills *plan.
+tv_status attn_plan_checked(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_prefix,
+                            int32_t hq, int32_t hkv, int32_t head_dim, tv_dtype dtype,
+                            const tv_attn_plan_override *ov, tv::MfmaPlan *plan) {
+    tv_status st = check_attn_sizes(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype);
+    if (st != TV_OK) return st;
+    if (!override_ok(ov)) return TV_ERR_SHAPE;
+    *plan = tv::plan_attn_mfma(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype, ov);
+    if (plan->use) {
+        // workgroup and merge-wave indices are int on the device
+        const int64_t groups = (int64_t)batch * hkv * plan->splits;
+        const int64_t grid = (groups + 7) / 8 * plan->row_tiles * 8;
+        const int64_t merge_waves = (int64_t)batch * hkv * plan->row_tiles * 8 * (head_dim / 32) * 4;
+        if (grid > INT32_MAX || merge_waves > INT32_MAX) return TV_ERR_LIMIT;
+    }
+    return TV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -89,23 +115,53 @@ tv_status tree_mask_build(const int32_t *parent, const int32_t *cu_nodes, const 
                                                (hipStream_t)stream));
 }
 
-size_t tree_attn_verify_workspace_size(int32_t batch, int32_t total_nodes, int32_t max_nodes,
-                                       int32_t max_prefix, int32_t hq, int32_t hkv, int32_t head_dim,
-                                       tv_dtype dtype) {
+size_t tree_attn_verify_workspace_size_ex(int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                                          int32_t max_prefix, int32_t hq, int32_t hkv, int32_t head_dim,
+                                          tv_dtype dtype, const tv_attn_plan_override *ov) {
     if (check_attn_sizes(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype) != TV_OK)
         return 0;
+    if (!override_ok(ov)) return 0;
     const tv::MfmaPlan plan =
-        tv::plan_attn_mfma(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype);
+        tv::plan_attn_mfma(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype, ov);
     return plan.use ? plan.ws_bytes : 0;
 }
 
-tv_status tree_attn_verify(const void *q, const void *k_cache, const void *v_cache,
-                           const int32_t *cu_nodes, const int32_t *kv_start, const int32_t *prefix_len,
-                           const uint64_t *anc_bits, int32_t batch, int32_t total_nodes,
-                           int32_t max_nodes, int32_t max_prefix, int64_t kv_rows, int32_t hq,
-                           int32_t hkv, int32_t head_dim, float scale, tv_dtype dtype, void *out,
-                           void *workspace, size_t workspace_bytes, int32_t *err, void *stream) {
-    tv_status st = check_attn_sizes(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype);
+size_t tree_attn_verify_workspace_size(int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                                       int32_t max_prefix, int32_t hq, int32_t hkv, int32_t head_dim,
+                                       tv_dtype dtype) {
+    return tree_attn_verify_workspace_size_ex(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim,
+                                              dtype, nullptr);
+}
+
+tv_status tree_attn_verify_plan(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_prefix,
+                                int32_t hq, int32_t hkv, int32_t head_dim, tv_dtype dtype,
+                                const tv_attn_plan_override *ov, int32_t *info) {
+    if (!info) return TV_ERR_NULL;
+    tv::MfmaPlan plan;
+    const tv_status st =
+        attn_plan_checked(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype, ov, &plan);
+    if (st != TV_OK) return st;
+    info[0] = plan.use ? 1 : 0;
+    info[1] = plan.use ? plan.rows_per_tile : 0;
+    info[2] = plan.use ? plan.row_tiles : 0;
+    info[3] = plan.use ? plan.splits : 0;
+    info[4] = plan.use ? plan.keys_per_split : 0;
+    info[5] = plan.use && plan.table ? 1 : 0;
+    info[6] = plan.use ? tv::attn_mfma_lookahead(plan) : 0;
+    info[7] = plan.use ? (int32_t)(plan.ws_bytes > (size_t)INT32_MAX ? INT32_MAX : plan.ws_bytes) : 0;
+    return TV_OK;
+}
+
+tv_status tree_attn_verify_ex(const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *cu_nodes, const int32_t *kv_start, const int32_t *prefix_len,
+                              const uint64_t *anc_bits, int32_t batch, int32_t total_nodes,
+                              int32_t max_nodes, int32_t max_prefix, int64_t kv_rows, int32_t hq,
+                              int32_t hkv, int32_t head_dim, float scale, tv_dtype dtype, void *out,
+                              void *workspace, size_t workspace_bytes, int32_t *err,
+                              const tv_attn_plan_override *ov, void *stream) {
+    tv::MfmaPlan plan;
+    tv_status st =
+        attn_plan_checked(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype, ov, &plan);
     if (st != TV_OK) return st;
     if (kv_rows < 0) return TV_ERR_SHAPE;
     if (!(scale > 0.f) || scale != scale) return TV_ERR_SHAPE;
@@ -115,15 +171,6 @@ tv_status tree_attn_verify(const void *q, const void *k_cache, const void *v_cac
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
         !aligned(anc_bits, 8))
         return TV_ERR_ALIGN;
-    const tv::MfmaPlan plan =
-        tv::plan_attn_mfma(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype);
-    if (plan.use) {
-        // workgroup and merge-wave indices are int on the device
-        const int64_t groups = (int64_t)batch * hkv * plan.splits;
-        const int64_t grid = (groups + 7) / 8 * plan.row_tiles * 8;
-        const int64_t merge_waves = (int64_t)batch * hkv * plan.row_tiles * 8 * (head_dim / 32) * 4;
-        if (grid > INT32_MAX || merge_waves > INT32_MAX) return TV_ERR_LIMIT;
-    }
     if (plan.use && plan.ws_bytes > 0) {
         if (!workspace || workspace_bytes < plan.ws_bytes) return TV_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return TV_ERR_ALIGN;
@@ -151,6 +198,17 @@ tv_status tree_attn_verify(const void *q, const void *k_cache, const void *v_cac
     a.err = err;
     if (plan.use) return launch_status(tv::launch_attn_mfma(a, plan, workspace, (hipStream_t)stream));
     return launch_status(tv::launch_attn_valu(a, (hipStream_t)stream));
+}
+
+tv_status tree_attn_verify(const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *cu_nodes, const int32_t *kv_start, const int32_t *prefix_len,
+                           const uint64_t *anc_bits, int32_t batch, int32_t total_nodes,
+                           int32_t max_nodes, int32_t max_prefix, int64_t kv_rows, int32_t hq,
+                           int32_t hkv, int32_t head_dim, float scale, tv_dtype dtype, void *out,
+                           void *workspace, size_t workspace_bytes, int32_t *err, void *stream) {
+    return tree_attn_verify_ex(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc_bits, batch,
+                               total_nodes, max_nodes, max_prefix, kv_rows, hq, hkv, head_dim, scale, dtype,
+                               out, workspace, workspace_bytes, err, nullptr, stream);
 }
 
 tv_status tree_accept_greedy(const int32_t *parent, const int32_t *draft_tokens,

@@ -42,7 +42,9 @@ __global__ void __launch_bounds__(kCompactThreads) kv_compact_kernel(
     // whatever they are), and the checks use no short-circuit, so all these
     // reads are in flight together instead of one round trip each.
     const int s_raw = tid < max_depth ? accept_idx[(int64_t)b * max_depth + tid] : 0;
-    if ((n < 0) | (P < 0) | (ks < 0) | (ks + P + n > kv_rows) | (L < 0) | (L > max_depth)) {
+    // L > n is rejected too: a path through n nodes is at most n long, and the
+    // gather writes rows P .. P + L - 1, which must stay inside the request.
+    if ((n < 0) | (P < 0) | (ks < 0) | (ks + P + n > kv_rows) | (L < 0) | (L > max_depth) | (L > n)) {
         if (g == 0 && tid == 0) report(err, TV_DEVERR_BAD_REQUEST, b);
         return;
     }

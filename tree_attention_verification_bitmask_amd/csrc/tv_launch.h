@@ -93,8 +93,11 @@ struct MfmaPlan {
     size_t table_off = 0;   // byte offset of the table in the workspace
     size_t ws_bytes = 0;
 };
+// ov may be null (the library's own plan).
 MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefix, int hq, int hkv,
-                        int head_dim, tv_dtype dtype);
+                        int head_dim, tv_dtype dtype, const tv_attn_plan_override *ov);
+// Copy look-ahead (chunks) the launch uses for this plan.
+int attn_mfma_lookahead(const MfmaPlan &plan);
 hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *workspace,
                             hipStream_t stream);
 
