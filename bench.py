@@ -45,6 +45,7 @@ while the attention source it was taken on is unchanged (SHA-256).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import csv
 import glob
 import hashlib
@@ -242,6 +243,10 @@ def main(argv=None):
                          "per_config (default c3,c4; 'none' for none)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--waves", type=int, default=0,
+                    help="tuning: plan override for tree_attn_verify, waves per workgroup (4 or 8; 0 = library)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="tuning: plan override for tree_attn_verify, key-axis slices (0 = library)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (counter calibration)")
@@ -375,7 +380,11 @@ def time_pass(args, torch, BND, L, dev, wl, steps: int, warmup: int) -> dict:
     nxt = torch.empty(B, dtype=torch.int32, device=dev)
     newlen = torch.empty(B, dtype=torch.int32, device=dev)
     err = torch.zeros(4, dtype=torch.int32, device=dev)
-    ws_bytes = BND.tree_attn_verify_workspace_size(B, T, wl.max_nodes, wl.max_prefix, wl.hq, wl.hkv, wl.d, code)
+    ov = BND._override(args.splits, BND.TV_ORDER_AUTO, args.waves)
+    ws_bytes = BND.tree_attn_verify_workspace_size(B, T, wl.max_nodes, wl.max_prefix, wl.hq, wl.hkv, wl.d, code,
+                                                   args.splits, BND.TV_ORDER_AUTO, args.waves)
+    plan = BND.tree_attn_verify_plan(B, T, wl.max_nodes, wl.max_prefix, wl.hq, wl.hkv, wl.d, code,
+                                     args.splits, BND.TV_ORDER_AUTO, args.waves)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sp = C_void(stream.cuda_stream)
@@ -403,7 +412,10 @@ def time_pass(args, torch, BND, L, dev, wl, steps: int, warmup: int) -> dict:
         st = L.tree_mask_build(*mask_args)
         if ev is not None:
             ev[0].record(stream)
-        st |= L.tree_attn_verify(*attn_args[r])
+        if ov is None:
+            st |= L.tree_attn_verify(*attn_args[r])
+        else:
+            st |= L.tree_attn_verify_ex(*attn_args[r][:-1], ctypes.byref(ov), attn_args[r][-1])
         if ev is not None:
             ev[1].record(stream)
         if args.separate_commit:
@@ -498,7 +510,7 @@ def time_pass(args, torch, BND, L, dev, wl, steps: int, warmup: int) -> dict:
                    "head_dim": wl.d, "max_depth": wl.max_depth, "cold_cache_sets": R,
                    "cache": "warm" if args.warm else "cold",
                    "commit": "two launches" if args.separate_commit else "one launch",
-                   "workspace_bytes": ws_bytes, "host_enqueue_ms": t_host_enq * 1e3,
+                   "workspace_bytes": ws_bytes, "plan": plan, "host_enqueue_ms": t_host_enq * 1e3,
                    "spin_ahead_ms": spin_ms},
         "roofline": roof,
     }

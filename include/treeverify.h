@@ -178,13 +178,16 @@ tv_status tree_attn_verify(const void *q, const void *k_cache, const void *v_cac
  *   order:  batches only: TV_ORDER_AUTO (the library's choice), TV_ORDER_STATIC
  *           (workgroups take tasks in a fixed order) or TV_ORDER_PLANNED (a
  *           planner launch orders them longest first, when the plan is small
- *           enough for it).
+ *           enough for it);
+ *   waves:  wavefronts per workgroup of the matrix-core kernel (32 query
+ *           rows each), 0 = the library's choice, else 4 or 8.
  */
 enum { TV_ORDER_AUTO = 0, TV_ORDER_STATIC = 1, TV_ORDER_PLANNED = 2 };
 typedef struct {
     int32_t splits;
     int32_t order;
-    int32_t reserved[6]; /* must be zero */
+    int32_t waves;
+    int32_t reserved[5]; /* must be zero */
 } tv_attn_plan_override;
 
 size_t tree_attn_verify_workspace_size_ex(int32_t batch, int32_t total_nodes, int32_t max_nodes,

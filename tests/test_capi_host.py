@@ -131,9 +131,16 @@ def test_attn_override_checked(L):
     assert L.tree_attn_verify_plan(*args, C.byref(ov), info) == OK
     assert L.tree_attn_verify_plan(*args, C.byref(ov), None) == NULL
     assert L.tree_attn_verify_plan(*args, None, info) == OK
-    for bad in (BND.PlanOverride(-1, 0), BND.PlanOverride(0, 3), BND.PlanOverride(0, 0, (C.c_int32 * 6)(1))):
+    bads = (BND.PlanOverride(-1, 0), BND.PlanOverride(0, 3), BND.PlanOverride(0, 0, 0, (C.c_int32 * 5)(1)),
+            BND.PlanOverride(0, 0, 5), BND.PlanOverride(0, 0, 2))
+    for bad in bads:
         assert L.tree_attn_verify_plan(*args, C.byref(bad), info) == SHAPE
         assert L.tree_attn_verify_workspace_size_ex(*args, C.byref(bad)) == 0
+    # 32 rows per wave: 4 or 8 waves per workgroup
+    d64 = (1, 128, 128, 4096, 16, 4, 64, 1)
+    for a in (args, d64):
+        assert BND.tree_attn_verify_plan(*a, waves=4)["rows_per_tile"] == 128
+        assert BND.tree_attn_verify_plan(*a, waves=8)["rows_per_tile"] == 256
     # the plain call's checks are the _ex call's checks
     assert L.tree_attn_verify_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 128, 128, 4096, 4224, 30, 8, 128,
                                  0.088, 1, FAKE, FAKE, 1 << 40, None, None, None) == SHAPE

@@ -167,18 +167,19 @@ TV_ORDER_AUTO, TV_ORDER_STATIC, TV_ORDER_PLANNED = 0, 1, 2
 class PlanOverride(C.Structure):
     """tv_attn_plan_override: key-axis slices (0 = the library's choice) and
     the batch task order (TV_ORDER_*)."""
-    _fields_ = [("splits", C.c_int32), ("order", C.c_int32), ("reserved", C.c_int32 * 6)]
+    _fields_ = [("splits", C.c_int32), ("order", C.c_int32), ("waves", C.c_int32), ("reserved", C.c_int32 * 5)]
 
 
-def _override(splits: int = 0, order: int = TV_ORDER_AUTO):
-    if not splits and order == TV_ORDER_AUTO:
+def _override(splits: int = 0, order: int = TV_ORDER_AUTO, waves: int = 0):
+    if not splits and order == TV_ORDER_AUTO and not waves:
         return None
-    return PlanOverride(int(splits), int(order))
+    return PlanOverride(int(splits), int(order), int(waves))
 
 
 def tree_attn_verify_workspace_size(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim,
-                                    dtype_code, splits: int = 0, order: int = TV_ORDER_AUTO) -> int:
-    ov = _override(splits, order)
+                                    dtype_code, splits: int = 0, order: int = TV_ORDER_AUTO,
+                                    waves: int = 0) -> int:
+    ov = _override(splits, order, waves)
     if ov is None:
         return int(lib().tree_attn_verify_workspace_size(batch, total_nodes, max_nodes, max_prefix, hq,
                                                          hkv, head_dim, dtype_code))
@@ -191,9 +192,9 @@ PLAN_FIELDS = ("mfma", "rows_per_tile", "row_tiles", "splits", "keys_per_split",
 
 
 def tree_attn_verify_plan(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype_code,
-                          splits: int = 0, order: int = TV_ORDER_AUTO) -> dict:
+                          splits: int = 0, order: int = TV_ORDER_AUTO, waves: int = 0) -> dict:
     """The plan tree_attn_verify would run for these host sizes (no GPU needed)."""
-    ov = _override(splits, order)
+    ov = _override(splits, order, waves)
     info = (C.c_int32 * 8)()
     _check("tree_attn_verify_plan", lib().tree_attn_verify_plan(
         batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype_code,
@@ -203,7 +204,7 @@ def tree_attn_verify_plan(batch, total_nodes, max_nodes, max_prefix, hq, hkv, he
 
 def tree_attn_verify(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc, max_nodes: int,
                      max_prefix: int, scale: float | None = None, out=None, workspace=None,
-                     err=None, stream=None, splits: int = 0, order: int = TV_ORDER_AUTO):
+                     err=None, stream=None, splits: int = 0, order: int = TV_ORDER_AUTO, waves: int = 0):
     """q [T, hq, d]; k_cache / v_cache [rows, hkv, d] -> out [T, hq, d] (same dtype).
     splits / order: a plan override (tree_attn_verify_ex), for tuning and tests."""
     import torch
@@ -223,7 +224,7 @@ def tree_attn_verify(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc, m
     out = torch.empty_like(q) if out is None else out
     _need(out, "out", q.dtype, q.numel())
     err = torch.zeros(1, dtype=torch.int32, device=q.device) if err is None else err
-    ws_bytes = tree_attn_verify_workspace_size(B, T, max_nodes, max_prefix, hq, hkv, d, code, splits, order)
+    ws_bytes = tree_attn_verify_workspace_size(B, T, max_nodes, max_prefix, hq, hkv, d, code, splits, order, waves)
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -232,7 +233,7 @@ def tree_attn_verify(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc, m
     args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_nodes), _ptr(kv_start), _ptr(prefix_len),
             _ptr(anc), B, T, max_nodes, max_prefix, rows, hq, hkv, d, float(scale), code, _ptr(out),
             _ptr(workspace), ws_have, _ptr(err))
-    ov = _override(splits, order)
+    ov = _override(splits, order, waves)
     if ov is None:
         _check("tree_attn_verify", lib().tree_attn_verify(*args, _stream(stream)))
     else:

@@ -8,29 +8,32 @@
 // Rows and tiles.  For one request b and KV head g the query rows are the
 // (node, head-in-group) pairs r = node * G + j, G = hq / hkv: the G heads that
 // share a KV head are stacked so that one K/V stream serves N*G rows.  A
-// workgroup takes a tile of 256 rows and one slice of the key axis; each of
-// its eight wavefronts owns 32 rows (two per SIMD) and keeps its own
+// workgroup of NW wavefronts (4 or 8) takes a tile of 32 * NW rows and one
+// slice of the key axis; each wavefront owns 32 rows and keeps its own
 // online-softmax state for them over the whole slice.
 //
 // K/V staging.  The slice is cut into chunks of 32 keys.  Each chunk's K and
 // V are copied HBM -> LDS by the LDS-DMA form of the global load (16 bytes per
-// lane, no registers) into two rings of eight stages; the eight waves split a
+// lane, no registers) into two rings of eight stages; the waves split a
 // chunk's copies between them.  The copy of chunk c is issued at step
-// c - kAhead.  The DMA is issued from inline assembly (the compiler would
+// c - AH.  The DMA is issued from inline assembly (the compiler would
 // otherwise make every LDS read wait for all outstanding DMA) and the waits
-// are explicit: before the barrier of step i each wave waits for its own part
-// of chunk i + 2, so after the barrier chunk i + 2 is whole in LDS.  Each
-// 16-byte granule of a cached K/V row lands at an XOR-swizzled position in its
-// LDS row so the matrix-operand reads below are free of bank conflicts.
+// are explicit: before the barrier that opens step j each wave waits for its
+// own part of chunk j + 2, so after the barrier chunk j + 2 is whole in LDS.
+// Each 16-byte granule of a cached K/V row lands at an XOR-swizzled position
+// in its LDS row so the matrix-operand reads below are free of bank conflicts.
 //
-// Ping-pong schedule.  Waves 0-3 (group A) and 4-7 (group B) share the four
-// SIMDs, one of each per SIMD.  For chunk j a wave runs a vector phase V(j)
-// (the softmax of S(j)) and a matrix phase M(j) (O += P(j) V(j), then
-// S(j+1) = Q K(j+1)^T, 16 MFMAs, with the operand registers of the next
-// phase refilled from LDS right after each product).  A barrier separates
-// the phases, and group B runs one phase behind group A, so on every SIMD one
-// wave feeds the matrix core while the other computes exponentials.  The
-// operands are read one phase ahead, so LDS latency never stalls a product.
+// Per-wave software pipeline.  Step j of a wavefront issues, in one scheduled
+// block, the products O += P(j-1) V(j-1) and S(j+1) = Q K(j+1)^T (16 MFMAs at
+// head_dim 128) and, interleaved with them, the whole softmax of S(j), which
+// the previous step produced: the matrix core runs while the same wave's
+// vector unit computes exponentials.  (Measured on gfx950: a wave overlaps its
+// own MFMAs with its own vector work almost completely, while a wave that only
+// issues MFMAs next to one that only issues vector work on the same SIMD
+// does not.)  Each product is followed by the LDS read that refills the
+// operand registers it consumed (V(j) after the P V products, K(j+2) after
+// the Q K^T products), so the reads have a whole step to land.  One barrier
+// per step guards the copy ring.
 //
 // Transposed products.  S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = 32 keys
 // x 16 channels of K read from LDS, B = Q^T held in registers.  LDS row i of a
@@ -42,11 +45,18 @@
 // already holds, packed to bf16.  The O^T accumulator again gives each lane one
 // query row, so the online-softmax rescale is lane-local.
 //
-// Softmax.  Probabilities are 2^((s - m) c) with c = scale * log2(e) and m a
-// running reference that is raised only when a chunk's maximum exceeds it by
-// more than 8 / c (the weights then stay below 2^8); the accumulators are
-// rescaled only then.  The row sum adds the bf16-rounded weights (v_dot2 with
-// ones), i.e. exactly the weights the P V product uses.
+// Softmax.  Scores are kept in log2 units: Q is multiplied by c = scale *
+// log2(e) once (and rounded to bf16 again), and the Q K^T accumulator starts
+// from -M, M a running reference per row, so a weight is a bare 2^x of the
+// product's output (one exponential per score, no other arithmetic).  M is
+// raised only when a chunk's maximum exceeds it by more than 8 (the weights
+// then stay below 2^8); the accumulators are rescaled only then.  The weights
+// of chunk j are computed with the reference in force before chunk j, in
+// parallel with its row maximum; in the rare step whose maximum raises the
+// reference they are computed again and the scores already formed for the
+// next chunk are shifted to the new reference (so nothing waits for the
+// maximum in the common case).  The row sum adds the bf16-rounded weights
+// (v_dot2 with ones), i.e. exactly the weights the P V product uses.
 //
 // The ancestor mask is applied per lane, on chunks that reach the tree tail
 // or the end of the slice: the lane takes the 16 bits of its node's packed
@@ -68,8 +78,6 @@
 #include "tv_device.h"
 #include "tv_launch.h"
 
-#include <stdlib.h>
-
 #include <type_traits>
 
 namespace tv {
@@ -82,37 +90,45 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kTileRows = 32 * kWaves;  // query rows per workgroup
 constexpr int kChunk = 32;              // keys per LDS stage
 constexpr int kStages = 8;              // stages per ring (K ring, V ring)
-constexpr int kAhead = 6;               // the DMA of chunk c is issued at step c - kAhead
+constexpr int kBarrierPeriod = 2;       // steps between the barriers that guard the copy ring
+constexpr int kAhead = 5;               // chunks j + kAhead .. j + kAhead + 1 are copied at step j
 constexpr int kAheadShort = 4;          // the same for slices of at most kShortSlice chunks
 constexpr int kShortSlice = 12;
+constexpr int kMinSliceChunks = 5;      // fewest chunks per key-axis slice the plan picks
 constexpr int kXcds = 8;
+constexpr int kMaxTileRows = 256;
 constexpr int kMaxWords = (TV_MAX_NODES + 63) / 64;
-constexpr int kAncBytes = kTileRows * kMaxWords * 8;  // packed rows of the tile's nodes
+constexpr int kAncBytes = kMaxTileRows * kMaxWords * 8;  // packed rows of the tile's nodes
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
-// Step i reads K(i+2) and V(i+1); the copy issued at step i overwrites the
-// stage of chunk i + kAhead - kStages, whose last read (its V) was at step
-// i + kAhead - kStages - 1 <= i - 1.  K(i+2) must have been issued before
-// step i, i.e. kAhead >= 3.
-static_assert(kAhead >= 3 && kAhead <= kStages, "ring depth");
-static_assert(kStages * 2 * 32 * 256 + 256 * 16 * 8 <= 160 * 1024, "K/V rings and ancestor rows fit the 160 KB LDS");
+// Ring safety, with BP = kBarrierPeriod and barriers at the steps j = 0, BP,
+// 2 BP, ...: step j reads chunks j - 1, j and j + 1, so the last read of
+// chunk c is in step c + 1.  The copies issued at the barrier of step j
+// (chunks j + AH .. j + AH + BP - 1) overwrite the stages of chunks
+// j + AH - 8 .. j + AH + BP - 9, last read in step j + AH + BP - 8, which
+// every wave has finished at that barrier when AH + BP <= 7.  Between two
+// barriers the waves read chunks up to j + BP, which must have been copied
+// at the previous barrier: AH >= BP + 1.
+static_assert(kAhead + kBarrierPeriod <= 7 && kAheadShort >= kBarrierPeriod + 1, "ring depth");
+static_assert(kStages * 2 * 32 * 256 + kAncBytes <= 160 * 1024, "K/V rings and ancestor rows fit the 160 KB LDS");
 
-template <int D>
+template <int D, int NW, int RB>
 struct Geo {
     static constexpr int kRowBytes = 2 * D;                 // one head of one cache row
     static constexpr int kGran = D / 8;                     // 16-byte granules per row
     static constexpr int kHalf = kChunk * kRowBytes;        // K (or V) bytes per chunk
     static constexpr int kDmaPerHalf = kHalf / 1024;        // 1 KB per wave-wide DMA
-    static constexpr int kDmaPerWave = kDmaPerHalf / (kWaves / 2);  // per chunk and wave
+    static constexpr int kDmaPerWave = 2 * kDmaPerHalf / NW;  // per chunk and wave (one half only)
     static constexpr int kKS = D / 16;                      // k-steps of Q K^T
     static constexpr int kDB = D / 32;                      // 32-channel blocks of O
     static constexpr int kRingBytes = 2 * kStages * kHalf;  // K ring + V ring
-    static_assert(kDmaPerWave >= 1 && kDmaPerHalf % (kWaves / 2) == 0, "DMA split over a wave group");
+    static constexpr int kTileRows = 32 * NW * RB;  // RB blocks of 32 rows per wave
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+    static_assert(RB == 1 || RB == 2, "one or two 32-row blocks per wave");
+    static_assert(kTileRows <= kMaxTileRows, "ancestor rows of the tile fit their LDS area");
+    static_assert(kDmaPerWave >= 1 && kDmaPerHalf % kDmaPerWave == 0, "DMA split over half the waves");
     // V ring offsets: the lane's base (>= K ring size) lives in a register, the
     // stage and sub-block offsets in the 16-bit immediate of the LDS read.
     static_assert((kStages - 1) * kHalf + 12 * kRowBytes < 65536, "LDS immediate range");
@@ -125,9 +141,9 @@ __device__ __forceinline__ int key_of_slot(int slot) {
 }
 // XOR swizzles of the 16-byte granule position within an LDS row.
 template <int D>
-__device__ __forceinline__ int k_swz(int row) { return row & (Geo<D>::kGran - 1); }
+__device__ __forceinline__ int k_swz(int row) { return row & (D / 8 - 1); }
 template <int D>
-__device__ __forceinline__ int v_swz(int row) { return (4 * row) & (Geo<D>::kGran - 1); }
+__device__ __forceinline__ int v_swz(int row) { return (4 * row) & (D / 8 - 1); }
 
 __device__ __forceinline__ float halves_max(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -180,8 +196,10 @@ __device__ __forceinline__ void wait_vm() {
 // are outstanding (each chunk costs a wave PW instructions).
 template <int PW, int CAP>
 __device__ __forceinline__ void wait_chunks(int n) {
-    static_assert(CAP >= 0 && CAP <= 4, "wait_chunks covers up to four chunks in flight");
-    if (CAP >= 4 && n >= 4) wait_vm<PW * (CAP >= 4 ? 4 : 0)>();
+    static_assert(CAP >= 0 && CAP <= 6 && PW * CAP < 64, "wait_chunks covers up to six chunks in flight");
+    if (CAP >= 6 && n >= 6) wait_vm<PW * (CAP >= 6 ? 6 : 0)>();
+    else if (CAP >= 5 && n >= 5) wait_vm<PW * (CAP >= 5 ? 5 : 0)>();
+    else if (CAP >= 4 && n >= 4) wait_vm<PW * (CAP >= 4 ? 4 : 0)>();
     else if (CAP >= 3 && n >= 3) wait_vm<PW * (CAP >= 3 ? 3 : 0)>();
     else if (CAP >= 2 && n >= 2) wait_vm<PW * (CAP >= 2 ? 2 : 0)>();
     else if (CAP >= 1 && n >= 1) wait_vm<PW * (CAP >= 1 ? 1 : 0)>();
@@ -195,6 +213,7 @@ struct KParams {
     int batch, total_nodes, max_nodes, max_prefix;
     int64_t kv_rows;
     int hq, hkv, words;
+    int rgroups, tile_rows;  // 32-row groups per tile, query rows per tile (32 * rgroups)
     int row_tiles, splits, keys_per_split;
     float c;  // scale * log2(e)
     uint16_t *out;
@@ -301,13 +320,17 @@ __device__ __forceinline__ bool decode_task(const KParams &p, int wid, Task *t) 
     return true;
 }
 
-// AH = copy look-ahead in chunks (AH for long slices, fewer for short ones).
-template <int D, int AH>
-__global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
-    static_assert(AH >= 3 && AH <= kStages && AH - 2 <= 4, "ring depth and counted waits");
-    using Gm = Geo<D>;
-    constexpr int KS = Gm::kKS, DB = Gm::kDB, PW = Gm::kDmaPerWave;
+// NW = waves per workgroup; RB = 32-row blocks per wave (two blocks share
+// every K and V operand read from LDS, halving LDS and L2 traffic per
+// product); AH = copy look-ahead in chunks (AH for long slices, fewer for
+// short ones).
+template <int D, int NW, int RB, int AH>
+__global__ void __launch_bounds__(64 * NW, 1) attn_fwd_kernel(KParams p) {
+    using Gm = Geo<D, NW, RB>;
+    constexpr int KS = Gm::kKS, DB = Gm::kDB, PW = Gm::kDmaPerWave, TR = Gm::kTileRows;
     constexpr uint32_t kHalf = Gm::kHalf;
+    constexpr int BP = kBarrierPeriod;
+    static_assert(AH >= BP + 1 && AH + BP <= 7, "ring safety");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Gm::kRingBytes + kAncBytes];
 
     Task tk;
@@ -323,9 +346,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
     }
     const int G = p.hq / p.hkv;
     const int rows_b = n_nodes * G;
-    const int row0 = rt * kTileRows;
+    const int row0 = rt * TR;
     if (row0 >= rows_b) return;
-    const int row_end = min(rows_b, row0 + kTileRows);
+    const int row_end = min(rows_b, row0 + TR);
     const int node_first = row0 / G;
     const int node_last = (row_end - 1) / G;
     const int key_end = P + node_last + 1;  // tree keys past the tile's last node are never visible
@@ -348,14 +371,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
     const char *vbase = reinterpret_cast<const char *>(p.v) + (ks + k_lo) * row_stride + (int64_t)g * D * 2;
     const uint32_t ring = (uint32_t)(uintptr_t)smem;
 
-    // ---- DMA role: group A (waves 0 .. kWaves/2 - 1) copies the K half of
-    // every chunk, group B the V half; wave w copies parts part0 .. part0 +
-    // PW - 1 of its half.  Lane offsets are chunk-relative source bytes; for
-    // the last chunk the keys are clamped to the slice, so every source row is
-    // a valid row of the request.
-    const bool grp_b = wave >= kWaves / 2;
-    const bool dv = grp_b;
-    const int part0 = (wave % (kWaves / 2)) * PW;
+    // ---- DMA role: the first NW/2 waves copy the K half of every chunk, the
+    // others the V half; wave w copies parts part0 .. part0 + PW - 1 of its
+    // half.  Lane offsets are chunk-relative source bytes; for the last chunk
+    // the keys are clamped to the slice, so every source row is a valid row of
+    // the request.
+    const bool dv = wave >= NW / 2;
+    const int part0 = (wave % (NW / 2)) * PW;
     const char *dbase = dv ? vbase : kbase;
     const uint32_t dlds = ring + (dv ? kStages * kHalf : 0u) + part0 * 1024;
     const int last_keys = (k_hi - k_lo) - (n - 1) * kChunk;  // 1..32
@@ -401,37 +423,76 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
         const int nbytes = (node_last - node_first + 1) * p.words * 8;
         const char *src = reinterpret_cast<const char *>(p.anc + ((int64_t)lo + node_first) * p.words);
         const int nblk = (nbytes + 255) / 256;
-        for (int blk = wave; blk < nblk; blk += kWaves) {
+        for (int blk = wave; blk < nblk; blk += NW) {
             const uint32_t off = (uint32_t)min(blk * 256 + lane * 4, nbytes - 4);
             dma4(src, off, __builtin_amdgcn_readfirstlane(ring + Gm::kRingBytes + blk * 256));
         }
     }
-    // (2) this lane's query row -> registers (asynchronous; waited below).
-    const int r = row0 + wave * 32 + col;
-    const bool row_ok = r < row_end;
-    const bool active = row0 + wave * 32 < row_end;  // wave-uniform: the wave has rows
-    const int node = row_ok ? r / G : node_last;      // rows past the tile repeat a valid one
-    const int head = g * G + (row_ok ? r % G : 0);
-    const int64_t t = (int64_t)lo + node;
-    bf16x8_t qb[KS];
-    {
-        const uint16_t *qrow = p.q + (t * p.hq + head) * D + 8 * half;
+    // (2) this lane's query rows (one per 32-row block) -> registers
+    // (asynchronous; waited below).  Rows past the tile repeat a valid one.
+    const bool active = row0 + wave * 32 * RB < row_end;  // wave-uniform: the wave has rows
+    int r[RB], node[RB], head[RB];
+    bool row_ok[RB];
+    bf16x8_t qb[RB][KS];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        r[rb] = row0 + (wave * RB + rb) * 32 + col;
+        row_ok[rb] = r[rb] < row_end;
+        node[rb] = row_ok[rb] ? r[rb] / G : node_last;
+        head[rb] = g * G + (row_ok[rb] ? r[rb] % G : 0);
+        const uint16_t *qrow = p.q + (((int64_t)lo + node[rb]) * p.hq + head[rb]) * D + 8 * half;
 #pragma unroll
         for (int k16 = 0; k16 < KS; ++k16)
             asm volatile("global_load_dwordx4 %0, %1, off offset:%2"
-                         : "=v"(qb[k16])
+                         : "=v"(qb[rb][k16])
                          : "v"(qrow), "n"(32 * k16)
                          : "memory");
     }
-    // (3) the first AH chunks.  After the wait everything but chunks
-    // 2 .. AH-1 has landed.
+    // (3) the first AH chunks.  While they land, Q is multiplied by
+    // c = scale * log2(e) (scores in log2 units) and rounded to bf16 again;
+    // after the second wait everything but chunks 2 .. AH-1 has landed (the
+    // ancestor rows, Q, chunks 0 and 1).
 #pragma unroll
-    for (int c = 0; c < AH; ++c)
-        if (c < n) issue(c, c);
+    for (int ch = 0; ch < AH; ++ch)
+        if (ch < n) issue(ch, ch);
+    wait_chunks<PW, AH>(min(n, AH));  // Q and the ancestor rows
+    const float c = p.c;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int k16 = 0; k16 < KS; ++k16) {
+            asm volatile("" : "+v"(qb[rb][k16]));
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const f32x2_t x = {(float)qb[rb][k16][2 * e2] * c, (float)qb[rb][k16][2 * e2 + 1] * c};
+                const bf16x2_t y = __builtin_convertvector(x, bf16x2_t);
+                qb[rb][k16][2 * e2] = y[0];
+                qb[rb][k16][2 * e2 + 1] = y[1];
+            }
+        }
     wait_chunks<PW, AH - 2>(min(n, AH) - 2);
-#pragma unroll
-    for (int k16 = 0; k16 < KS; ++k16) asm volatile("" : "+v"(qb[k16]));
     lds_barrier();
+
+    // Top of step j, at every BP-th step: this wave's part of chunk
+    // min(j + BP, n - 1) has landed (chunks j + BP + 1 .. j + AH - 1 may still
+    // be in flight), then the barrier makes every wave's part visible, then
+    // the copies of chunks j + AH .. j + AH + BP - 1 start.  Between barriers
+    // the waves drift freely, so the two waves of a SIMD fill each other's
+    // gaps.
+    auto step_top = [&](int j) {
+        if (j % BP == 0) {
+            wait_chunks<PW, AH - 1 - BP>(min(AH - 1 - BP, n - 1 - BP - j));
+            lds_barrier();
+#pragma unroll
+            for (int c = j + AH; c < j + AH + BP; ++c)
+                if (c < n) issue(c, (uint32_t)(c % kStages));
+        }
+    };
+    if (!active) {
+        // A wave without rows only keeps the copy schedule and the barriers.
+        for (int j = 0; j < n; ++j) step_top(j);
+        return;
+    }
 
     // ---- per-lane LDS read offsets ----------------------------------------------
     // K (A of S^T): LDS row col, logical granule 2*k16 + half, stored at
@@ -455,145 +516,85 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
     // compiler forms the addresses in the loop (one v_xad each) instead of
     // keeping one hoisted register per address live across the loop.
     // Single operands: K granule pair k16 and the V^T operand (tt, db).
-    auto read_k1 = [&](uint32_t base, uint32_t t, int k16) {
-        return *reinterpret_cast<const bf16x8_t *>(smem + (((32u * k16) ^ t) + base));
+    auto read_k1 = [&](uint32_t base, uint32_t tx, int k16) {
+        return *reinterpret_cast<const bf16x8_t *>(smem + (((32u * k16) ^ tx) + base));
     };
-    auto read_v1 = [&](uint32_t base, uint32_t t, int tt, int db) {
-        const uint32_t a0 = ((64u * db) ^ t) + base + (8 * tt) * Gm::kRowBytes;
+    auto read_v1 = [&](uint32_t base, uint32_t tx, int tt, int db) {
+        const uint32_t a0 = ((64u * db) ^ tx) + base + (8 * tt) * Gm::kRowBytes;
         const bf16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(smem + a0));
         const bf16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(smem + a0 + 4 * Gm::kRowBytes));
         return bf16x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
     };
-    auto read_k = [&](bf16x8_t(&kk)[KS], uint32_t st) {
-        const uint32_t base = kb + st;
-        uint32_t t = kt;
-        asm volatile("" : "+v"(t));
-#pragma unroll
-        for (int k16 = 0; k16 < KS; ++k16)
-            kk[k16] = *reinterpret_cast<const bf16x8_t *>(smem + (((32u * k16) ^ t) + base));
-    };
-    auto read_v = [&](bf16x8_t(&vv)[2][DB], uint32_t st) {
-        const uint32_t base = vb + st;
-        uint32_t t = vt;
-        asm volatile("" : "+v"(t));
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const uint32_t a = ((64u * db) ^ t) + base;
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const uint32_t a0 = a + (8 * tt) * Gm::kRowBytes;
-                const bf16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(smem + a0));
-                const bf16x4_t hi4 =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(smem + a0 + 4 * Gm::kRowBytes));
-                vv[tt][db] = bf16x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-            }
-        }
-    };
 
-    // ---- ping-pong schedule -------------------------------------------------------
-    // Group A = waves 0 .. kWaves/2 - 1, group B = the others; every SIMD holds
-    // one wave of each.  For chunk j a wave runs
-    //   V(j): the softmax of S(j) -> P(j) (vector work only);
-    //   M(j): O += P(j) V(j) and S(j+1) = Q K(j+1)^T (16 products), plus the
-    //         reads of V(j+1) and K(j+2) from LDS into registers.
-    // V(j) starts with the wave's copies (K for A, V for B) of chunk
-    // j + AH: the vector phase has issue slots to spare.
-    // Every wave runs V(0) M(0) V(1) M(1) ... with a barrier after each item;
-    // group B first passes one barrier alone, so it runs one item behind and
-    // on each SIMD one wave feeds the matrix core while the other runs the
-    // exponentials.  Barrier 2j+1 starts A's M(j): before it A waits for its
-    // part of K(j+2) and B (at the end of its M(j-1)) for its part of V(j+1).
-    // A copy issued in V(j) overwrites the stage of chunk j + AH - 8,
-    // whose last reads (B's M of chunk j + AH - 9) were consumed at least
-    // two items earlier.
-    auto copy_ahead = [&](int j) {
-        if (j + AH < n) issue(j + AH, (uint32_t)((j + AH) % kStages));
-    };
-    auto copy_ahead1 = [&](int j, int jj) {
-        if (j + AH < n) issue1(j + AH, (uint32_t)((j + AH) % kStages), jj);
-    };
-    // Waits ahead of the barrier that opens A's M(j) (A: K(j+2)) and the one
-    // that opens A's M(j+1) (B, after its M(j): V(j+2)).
-    auto wait_before_m = [&](int j) {
-        if (!grp_b) wait_chunks<PW, AH - 2>(n - (j + 3));
-    };
-    auto wait_after_m = [&](int j) {
-        if (grp_b) wait_chunks<PW, AH - 2>(n - (j + 3));
-    };
-    if (!active) {
-        // A wave without rows only keeps the copy schedule and the barriers.
-        if (grp_b) lds_barrier();
-        for (int j = 0; j < n; ++j) {
-            copy_ahead(j);
-            wait_before_m(j);
-            lds_barrier();
-            wait_after_m(j);
-            lds_barrier();
-        }
-        if (!grp_b) lds_barrier();
-        return;
-    }
-
-    f32x16_t oacc[DB];
+    f32x16_t oacc[RB][DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[rb][db][e] = 0.f;
     const f32x16_t zero16 = {};
-    float m_run = -INFINITY, l_run = 0.f;
-    float nb = 0.f;           // -m_ref * c
-    const float c = p.c;
-    const float thr = kRescaleLog2 / c;
+    // m_run: the reference M in log2 units (-inf until a row sees a key);
+    // nb = -M (0 while M is -inf), also held as a splat vector, the starting
+    // value of the Q K^T accumulator.
+    float m_run[RB], l_run[RB], nb[RB];
+    f32x16_t nbv[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        m_run[rb] = -INFINITY;
+        l_run[rb] = 0.f;
+        nb[rb] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) nbv[rb][e] = 0.f;
+    }
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-    lds_u64_t *arow = reinterpret_cast<lds_u64_t *>(
-        (uint32_t)(uintptr_t)anc_lds + (uint32_t)((node - node_first) * p.words * 8));
+    lds_u64_t *arow[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+        arow[rb] = reinterpret_cast<lds_u64_t *>((uint32_t)(uintptr_t)anc_lds +
+                                                 (uint32_t)((node[rb] - node_first) * p.words * 8));
 
-    auto qk = [&](const bf16x8_t(&kk)[KS]) {
-        f32x16_t acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[0], qb[0], zero16, 0, 0, 0);
+    // One score accumulator per 32-row block (S(j), then S(j+1) over it),
+    // and two weight sets that alternate between steps: step j takes the
+    // softmax of S(j) into W[j & 1] while its products use W[(j+1) & 1] =
+    // P(j-1).
+    f32x16_t S[RB];
+    bf16x8_t W0[RB][2], W1[RB][2];
+    // Operand ring: a product's K or V operand is read from LDS kLead
+    // operands ahead of its use into slot (operand number) % kSlots, so only
+    // a few operands are in flight instead of a whole step's.
+    constexpr int kLead = 2;
+    constexpr int kSlots = 4;
+    static_assert(kLead < kSlots && KS % kSlots == 0 && (2 * DB) % kSlots == 0, "operand ring");
+    bf16x8_t opr[kSlots];
+
+    // Mask of chunk j on the scores (a uniform branch before the scheduled
+    // block: only chunks that reach the tree tail or the slice end need it).
+    auto apply_mask = [&](f32x16_t(&sv)[RB], int j) {
+        if (j >= c_mask) {
 #pragma unroll
-        for (int k16 = 1; k16 < KS; ++k16) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[k16], qb[k16], acc, 0, 0, 0);
-        return acc;
-    };
-    // Softmax of chunk i, first part: mask, row max, and (rarely) a raise of
-    // the reference m with the rescale of l and O.
-    auto prep = [&](f32x16_t &sv, int i) {
-        if (i >= c_mask) {
-            const uint32_t vis = visible16(arow, p.words, k_lo + i * kChunk + 16 * half, P, k_hi);
-            if (vis != 0xFFFFu) {
+            for (int rb = 0; rb < RB; ++rb) {
+                const uint32_t vis = visible16(arow[rb], p.words, k_lo + j * kChunk + 16 * half, P, k_hi);
+                if (vis != 0xFFFFu) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    if (!((vis >> e) & 1u)) sv[e] = -INFINITY;
+                    for (int e = 0; e < 16; ++e)
+                        if (!((vis >> e) & 1u)) sv[rb][e] = -INFINITY;
+                }
             }
         }
-        // row max over the lane's 16 scores as a three-level tree of max3
-        const float a0 = fmaxf(fmaxf(sv[0], sv[1]), sv[2]), a1 = fmaxf(fmaxf(sv[3], sv[4]), sv[5]);
-        const float a2 = fmaxf(fmaxf(sv[6], sv[7]), sv[8]), a3 = fmaxf(fmaxf(sv[9], sv[10]), sv[11]);
-        const float a4 = fmaxf(fmaxf(sv[12], sv[13]), sv[14]);
-        const float b0 = fmaxf(fmaxf(a0, a1), a2), b1 = fmaxf(fmaxf(a3, a4), sv[15]);
-        const float mx = halves_max(fmaxf(b0, b1));
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + thr) != 0) {
-            const float mn = fmaxf(m_run, mx);
-            const float mref = (mn == -INFINITY) ? 0.f : mn;
-            const float alpha = __builtin_amdgcn_exp2f((m_run - mref) * c);
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-            m_run = mn;
-            nb = -mref * c;
-        }
     };
-    // Second part: the weights 2^(s c - m c), rounded to bf16, and their sum.
-    // (Two partial sums halve the dependent chain of the row sum.)
-    auto weights = [&](const f32x16_t &sv, bf16x8_t(&pw)[2]) {
+    // The weights 2^(s c - m c) at the current reference, rounded to bf16,
+    // and their sum (two partial sums halve the dependent chain).
+    // The weights 2^(x + shift) of the 16 scores x of one row block, rounded
+    // to bf16, and their sum (two partial sums halve the dependent chain).
+    auto weights = [&](const f32x16_t &sv, bf16x8_t(&pw)[2], float shift) {
         float l0 = 0.f, l1 = 0.f;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
             for (int j2 = 0; j2 < 4; ++j2) {
-                const f32x2_t pf = {__builtin_amdgcn_exp2f(fmaf(sv[8 * tt + 2 * j2], c, nb)),
-                                    __builtin_amdgcn_exp2f(fmaf(sv[8 * tt + 2 * j2 + 1], c, nb))};
+                const f32x2_t pf = {__builtin_amdgcn_exp2f(sv[8 * tt + 2 * j2] + shift),
+                                    __builtin_amdgcn_exp2f(sv[8 * tt + 2 * j2 + 1] + shift)};
                 const bf16x2_t pp = __builtin_convertvector(pf, bf16x2_t);
                 if (j2 & 1) l1 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l1, false);
                 else l0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l0, false);
@@ -601,143 +602,246 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
                 pw[tt][2 * j2 + 1] = pp[1];
             }
         }
-        l_run += l0 + l1;
+        return l0 + l1;
     };
-    auto pv = [&](const bf16x8_t(&vv)[2][DB], const bf16x8_t(&pw)[2]) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv[tt][db], pw[tt], oacc[db], 0, 0, 0);
-    };
-
-    // Prologue products: S(0), and the operands K(1), V(0).
-    bf16x8_t kr[KS], vr[2][DB], pw[2];
-    read_k(kr, 0);
-    f32x16_t sv = qk(kr);
-    if (n > 1) read_k(kr, kHalf);
-    read_v(vr, 0);
-    auto vphase = [&](int j) {
-        prep(sv, j);
-        weights(sv, pw);
-    };
-    // M(j): each product is followed by the read that refills the operand
-    // registers it consumed (V(j+1) after the P V products, K(j+2) after the
-    // Q K^T products), so the reads hide under the matrix core and each
-    // operand set stays single.  STEADY: j + 2 < n (both refills exist).
-    auto mphase = [&](auto steady_, int j) {
-        constexpr bool STEADY = decltype(steady_)::value;
-        const bool nx1 = STEADY || j + 1 < n, nx2 = STEADY || j + 2 < n;
-        const uint32_t vbase = vb + (uint32_t)((j + 1) % kStages) * kHalf;
-        const uint32_t kbase = kb + (uint32_t)((j + 2) % kStages) * kHalf;
+    // One step, in two halves of segments that the compiler may not reorder
+    // across (sched_barrier); each segment issues the LDS read of the operand
+    // kLead places ahead and the RB products (one per row block) that share
+    // the current operand.  First half: O += P(j-1) V(j-1) (V^T blocks
+    // (tt, db) of chunk j-1), each segment also taking a slice of the
+    // softmax of S(j): the weights at the reference in force (speculatively)
+    // and the row maxima.  Then the rare raise of a reference (rescale of l
+    // and O, the weights again).  Second half: S(j+1) = Q K(j+1)^T (K blocks
+    // k16 of chunk j+1), written over S(j), starting from -M.  The step ends
+    // with the reads of the first kLead operands of the next PV products,
+    // V(j).  Step 0 has no PV products and step n-1 no QK products.
+    constexpr int NPVO = 2 * DB;           // PV operands per step
+    constexpr int NE = 16 * RB;            // score elements per lane
+    constexpr int EPP = (NE + NPVO * RB - 1) / (NPVO * RB);  // elements per PV segment
+    auto step = [&](auto pv_, auto qk_, bf16x8_t(&wprev)[RB][2], bf16x8_t(&wcur)[RB][2], int j) {
+        constexpr bool PV = decltype(pv_)::value, QK = decltype(qk_)::value;
+        step_top(j);
+        apply_mask(S, j);
+        const uint32_t vprev = vb + (uint32_t)(max(j - 1, 0) % kStages) * kHalf;  // V(j-1), V(0) at step 0
+        const uint32_t kcur = kb + (uint32_t)(min(j + 1, n - 1) % kStages) * kHalf;  // K(j+1)
+        const uint32_t vcur = vb + (uint32_t)(j % kStages) * kHalf;                // V(j)
         uint32_t vtt = vt, ktt = kt;
         asm volatile("" : "+v"(vtt), "+v"(ktt));
-        // The wave feeding the matrix core outranks its SIMD partner (in its
-        // softmax phase) for issue, so the products and their operand reads go
-        // out back to back; the partner's vector work fills the gaps.
-        // Measured: c4 53.4 -> 51.8 us, c5 105.8 -> 101.7 us.
-        __builtin_amdgcn_s_setprio(1);
+        auto read_op = [&](int o) {
+            return o < NPVO ? read_v1(vprev, vtt, o / DB, o % DB) : read_k1(kcur, ktt, o - NPVO);
+        };
+        float pf[NE];
+        float mxp[RB], l0[RB], l1[RB];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int rb = 0; rb < RB; ++rb) {
+            mxp[rb] = -INFINITY;
+            l0[rb] = 0.f;
+            l1[rb] = 0.f;
+        }
+        // softmax slice: score elements e0 .. e0 + EPP - 1 (element e is
+        // entry e % 16 of row block e / 16)
+        auto vec_piece = [&](int e0) {
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int idx = tt * DB + db;
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[tt][db], pw[tt], oacc[db], 0, 0, 0);
-                if (nx1) vr[tt][db] = read_v1(vbase, vtt, tt, db);
-                __builtin_amdgcn_sched_barrier(0);
+            for (int e = e0; e < e0 + EPP; ++e) {
+                if (e < NE) {
+                    const int rb = e / 16, el = e % 16;
+                    pf[e] = __builtin_amdgcn_exp2f(S[rb][el]);
+                    if (el & 1) {
+                        mxp[rb] = fmaxf(fmaxf(mxp[rb], S[rb][el - 1]), S[rb][el]);
+                        const f32x2_t pr = {pf[e - 1], pf[e]};
+                        const bf16x2_t pp = __builtin_convertvector(pr, bf16x2_t);
+                        wcur[rb][el >> 3][(el & 7) - 1] = pp[0];
+                        wcur[rb][el >> 3][el & 7] = pp[1];
+                        if ((el >> 1) & 1) l1[rb] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l1[rb], false);
+                        else l0[rb] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l0[rb], false);
+                    }
+                }
             }
-        if (nx1) {
-            sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[0], qb[0], zero16, 0, 0, 0);
-            if (nx2) kr[0] = read_k1(kbase, ktt, 0);
-            __builtin_amdgcn_sched_barrier(0);
+        };
+        // first half: PV products with the softmax of S(j) (step 0 has no
+        // products: the softmax runs alone, and the QK half's first operands
+        // are read here instead)
+        if constexpr (PV) {
 #pragma unroll
-            for (int k16 = 1; k16 < KS; ++k16) {
-                sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[k16], qb[k16], sv, 0, 0, 0);
-                if (nx2) kr[k16] = read_k1(kbase, ktt, k16);
-                __builtin_amdgcn_sched_barrier(0);
+            for (int o = 0; o < NPVO; ++o) {
+                opr[(o + kLead) % kSlots] = read_op(o + kLead);  // (o + kLead < NPVO + KS always)
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const int tt = o / DB, db = o % DB;
+                    oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opr[o % kSlots], wprev[rb][tt],
+                                                                           oacc[rb][db], 0, 0, 0);
+                    vec_piece((o * RB + rb) * EPP);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int o = NPVO; o < NPVO + kLead; ++o) opr[o % kSlots] = read_op(o);
+#pragma unroll
+            for (int e0 = 0; e0 < NE; e0 += EPP) vec_piece(e0);
+        }
+        float lsum[RB], mx[RB];
+        bool raise = false;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            lsum[rb] = l0[rb] + l1[rb];
+            mx[rb] = halves_max(mxp[rb]);  // relative to the reference in force
+            raise |= (mx[rb] > kRescaleLog2) | ((m_run[rb] == -INFINITY) & (mx[rb] > -INFINITY));
+            // (the speculative weights are used whatever the branch below
+            // does, so they stay interleaved with the products above)
+            asm volatile("" : "+v"(wcur[rb][0]), "+v"(wcur[rb][1]), "+v"(lsum[rb]));
+        }
+        // Rare: the chunk raises a reference (or gives a row its first).
+        // Rescale l and O (which now includes P(j-1) V(j-1)) and take the
+        // weights again.  A row whose maximum stays within its threshold may
+        // be raised too, which changes nothing but rounding.
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const float mn = fmaxf(m_run[rb], mx[rb] - nb[rb]);  // new reference
+                const float nbn = (mn == -INFINITY) ? 0.f : -mn;       // (a row with no key yet keeps 0)
+                const float delta = nbn - nb[rb];
+                const float alpha = __builtin_amdgcn_exp2f(m_run[rb] + nbn);  // 0 while m_run is -inf
+                l_run[rb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) oacc[rb][db][e] *= alpha;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) nbv[rb][e] = nbn;
+                m_run[rb] = mn;
+                nb[rb] = nbn;
+                lsum[rb] = weights(S[rb], wcur[rb], delta);
             }
         }
-        __builtin_amdgcn_s_setprio(0);
-        // Results of the phase are pinned here: register-only work must not
-        // drift across the barriers into the other phase.
-        asm volatile("" : "+v"(sv));
 #pragma unroll
-        for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(oacc[db]));
+        for (int rb = 0; rb < RB; ++rb) l_run[rb] += lsum[rb];
+        // second half: QK products, S(j+1) over S(j) (none at the last step)
+        if constexpr (QK) {
+#pragma unroll
+            for (int o = NPVO; o < NPVO + KS; ++o) {
+                if (o + kLead < NPVO + KS) opr[(o + kLead) % kSlots] = read_op(o + kLead);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const int k16 = o - NPVO;
+                    S[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opr[o % kSlots], qb[rb][k16],
+                                                                    k16 ? S[rb] : nbv[rb], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+        // the next PV products' first operands: V(j) blocks 0 .. kLead-1
+#pragma unroll
+        for (int o = 0; o < kLead; ++o) opr[o] = read_v1(vcur, vtt, o / DB, o % DB);
     };
-    using Steady = std::true_type;
-    using Tail = std::false_type;
-    auto vphase_pinned = [&](int j) {
-        copy_ahead(j);
-        vphase(j);
-        asm volatile("" : "+v"(pw[0]), "+v"(pw[1]));
-    };
-    if (grp_b) lds_barrier();
-    int j = 0;
-    for (; j < n - 2; ++j) {
-        vphase_pinned(j);
-        wait_before_m(j);
-        lds_barrier();
-        mphase(Steady{}, j);
-        wait_after_m(j);
-        lds_barrier();
+
+    // Prologue products: S(0) = Q K(0)^T.
+    {
+        uint32_t ktt = kt, vtt = vt;
+        asm volatile("" : "+v"(ktt), "+v"(vtt));
+#pragma unroll
+        for (int k16 = 0; k16 < KS; ++k16) {
+            const bf16x8_t kop = read_k1(kb, ktt, k16);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                S[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qb[rb][k16], k16 ? S[rb] : zero16, 0, 0, 0);
+        }
+        (void)vtt;
     }
-    for (; j < n; ++j) {
-        vphase_pinned(j);
-        lds_barrier();
-        mphase(Tail{}, j);
-        lds_barrier();
+    // Steps alternate the weight sets: even steps take the softmax into W0,
+    // odd steps into W1.  Step 0 (no PV products) and step n-1 (no QK
+    // products) are peeled off the loop.
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    if (n == 1) {
+        step(F_{}, F_{}, W1, W0, 0);
+    } else {
+        step(F_{}, T_{}, W1, W0, 0);
+        int j = 1;
+        for (; j + 2 < n; j += 2) {
+            step(T_{}, T_{}, W0, W1, j);      // odd j
+            step(T_{}, T_{}, W1, W0, j + 1);  // even j
+        }
+        if (j + 1 < n) {  // one full step left (odd j)
+            step(T_{}, T_{}, W0, W1, j);
+            ++j;
+        }
+        if (j & 1) step(T_{}, F_{}, W0, W1, j);  // j == n - 1
+        else step(T_{}, F_{}, W1, W0, j);
     }
-    if (!grp_b) lds_barrier();
+    // Last products: O += P(n-1) V(n-1) (V(n-1) blocks 0 .. kLead-1 were read
+    // at the end of step n - 1).
+    {
+        const bool odd = (n - 1) & 1;
+        const uint32_t vlast = vb + (uint32_t)((n - 1) % kStages) * kHalf;
+        uint32_t vtt = vt;
+        asm volatile("" : "+v"(vtt));
+#pragma unroll
+        for (int o = 0; o < 2 * DB; ++o) {
+            if (o + kLead < 2 * DB) opr[(o + kLead) % kSlots] = read_v1(vlast, vtt, (o + kLead) / DB, (o + kLead) % DB);
+            const int tt = o / DB, db = o % DB;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opr[o % kSlots], odd ? W1[rb][tt] : W0[rb][tt],
+                                                                       oacc[rb][db], 0, 0, 0);
+        }
+    }
 
     // ---- epilogue ----------------------------------------------------------------
-    l_run = halves_sum(l_run);
-    if (p.splits == 1) {
-        if (!row_ok) return;
-        const float inv = 1.f / l_run;
-        uint16_t *orow = p.out + (t * p.hq + head) * D;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+    for (int rb = 0; rb < RB; ++rb) {
+        const float lr = halves_sum(l_run[rb]);
+        if (p.splits == 1) {
+            if (!row_ok[rb]) continue;
+            const float inv = 1.f / lr;
+            uint16_t *orow = p.out + (((int64_t)lo + node[rb]) * p.hq + head[rb]) * D;
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const int d = db * 32 + 8 * i4 + 4 * half;
-                const uint32_t w0 = pack_bf16x2(oacc[db][4 * i4 + 0] * inv, oacc[db][4 * i4 + 1] * inv);
-                const uint32_t w1 = pack_bf16x2(oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv);
-                *reinterpret_cast<uint2 *>(orow + d) = make_uint2(w0, w1);
-            }
-    } else {
-        // Partial of this slice: O / l rounded to bf16 (a convex combination of
-        // V rows, so bf16 keeps its range) plus the fp32 (m, l).  Lane-native
-        // layout [tile][split][wave][DB*4 x 4 bf16][64 lanes].  A row that sees
-        // no key of the slice has l = 0 and stores zeros.  The stores are
-        // relaxed atomics at agent scope, which write through this XCD's L2:
-        // the merge kernel reads them from another XCD anyway, and the end of
-        // this kernel then has no dirty partials left to write back
-        // (measured: 1.5 us less per call at 240 workgroups).
-        const int tile = (b * p.hkv + g) * p.row_tiles + rt;
-        const int64_t unit = ((int64_t)tile * p.splits + s) * kWaves + wave;
-        uint2 *po = p.ws_o + unit * (DB * 4 * 64) + lane;
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const int d = db * 32 + 8 * i4 + 4 * half;
+                    const uint32_t w0 = pack_bf16x2(oacc[rb][db][4 * i4 + 0] * inv, oacc[rb][db][4 * i4 + 1] * inv);
+                    const uint32_t w1 = pack_bf16x2(oacc[rb][db][4 * i4 + 2] * inv, oacc[rb][db][4 * i4 + 3] * inv);
+                    *reinterpret_cast<uint2 *>(orow + d) = make_uint2(w0, w1);
+                }
+        } else {
+            // Partial of this slice for one 32-row group: O / l rounded to
+            // bf16 (a convex combination of V rows, so bf16 keeps its range)
+            // plus the fp32 (m, l).  Lane-native layout
+            // [tile][split][row group][DB*4 x 4 bf16][64 lanes].  A row that
+            // sees no key of the slice has l = 0 and stores zeros.  The
+            // stores are relaxed atomics at agent scope, which write through
+            // this XCD's L2: the merge kernel reads them from another XCD
+            // anyway, and the end of this kernel then has no dirty partials
+            // left to write back (measured: 1.5 us less per call at 240
+            // workgroups).
+            const int tile = (b * p.hkv + g) * p.row_tiles + rt;
+            const int64_t unit = ((int64_t)tile * p.splits + s) * (NW * RB) + wave * RB + rb;
+            uint2 *po = p.ws_o + unit * (DB * 4 * 64) + lane;
+            const float inv = lr > 0.f ? 1.f / lr : 0.f;
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const uint64_t w =
-                    (uint64_t)pack_bf16x2(oacc[db][4 * i4 + 0] * inv, oacc[db][4 * i4 + 1] * inv) |
-                    ((uint64_t)pack_bf16x2(oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv) << 32);
-                __hip_atomic_store(reinterpret_cast<uint64_t *>(po + (db * 4 + i4) * 64), w, __ATOMIC_RELAXED,
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const uint64_t w =
+                        (uint64_t)pack_bf16x2(oacc[rb][db][4 * i4 + 0] * inv, oacc[rb][db][4 * i4 + 1] * inv) |
+                        ((uint64_t)pack_bf16x2(oacc[rb][db][4 * i4 + 2] * inv, oacc[rb][db][4 * i4 + 3] * inv)
+                         << 32);
+                    __hip_atomic_store(reinterpret_cast<uint64_t *>(po + (db * 4 + i4) * 64), w, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+            if (half == 0) {
+                const uint64_t w = (uint64_t)__float_as_uint(m_run[rb]) | ((uint64_t)__float_as_uint(lr) << 32);
+                __hip_atomic_store(reinterpret_cast<uint64_t *>(p.ws_ml + unit * 32 + col), w, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
             }
-        if (half == 0) {
-            const uint64_t w = (uint64_t)__float_as_uint(m_run) | ((uint64_t)__float_as_uint(l_run) << 32);
-            __hip_atomic_store(reinterpret_cast<uint64_t *>(p.ws_ml + unit * 32 + col), w, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
 
 // Merge the per-slice partials of one row of one (tile, 32-row group,
-// channels): O = sum_s w_s O_s / sum_s w_s l_s with w_s = 2^((m_s - M) c),
-// M = max_s m_s.  One wavefront per (tile, row group, 32-channel block, I4W of
+// channels): O = sum_s w_s O_s / sum_s w_s l_s with w_s = 2^(m_s - M),
+// M = max_s m_s (the slices' references, in log2 units).  One wavefront per (tile, row group, 32-channel block, I4W of
 // the 4 float4 slots), four per workgroup; lane layout as the partials (lane
 // half h holds channels 32 db + 8 i4 + 4 h .. +3 of row col).  The slices are
 // taken in batches whose loads are all issued before any is used, so a batch
@@ -747,16 +851,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(KParams p) {
 constexpr int kCombineWaves = 4;
 template <int D, int I4W>
 __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParams p) {
-    constexpr int DB = Geo<D>::kDB;
+    constexpr int DB = D / 32;
     constexpr int kGroups = 4 / I4W;                 // waves per (tile, row group, channel block)
     constexpr int kBatch = I4W == 1 ? 16 : 8;        // slices per batch
     // (wave-uniform: the request's sizes then come by scalar loads, which
     // complete independently of the partials' vector loads)
     const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * kCombineWaves + (threadIdx.x >> 6));
+    const int nw = p.rgroups;  // 32-row groups per tile
     const int i4b = (gw % kGroups) * I4W;
     const int db = (gw / kGroups) % DB;
-    const int rg = (gw / (kGroups * DB)) % kWaves;
-    const int tile = gw / (kGroups * DB * kWaves);
+    const int rg = (gw / (kGroups * DB)) % nw;
+    const int tile = gw / (kGroups * DB * nw);
     if (tile >= p.batch * p.hkv * p.row_tiles) return;
     const int lane = threadIdx.x & 63;
     const int col = lane & 31, half = lane >> 5;
@@ -770,10 +875,10 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
     // hold arbitrary bits; they are skipped by branches below, never scaled by
     // zero (0 * NaN would poison the sum).
     const int64_t base = (int64_t)tile * p.splits;
-    const float2 *ml = p.ws_ml + (base * kWaves + rg) * 32 + col;
-    const uint2 *po = p.ws_o + (base * kWaves + rg) * (DB * 4 * 64) + (db * 4 + i4b) * 64 + lane;
-    constexpr int64_t kMlStride = kWaves * 32;                    // per slice
-    constexpr int64_t kOStride = (int64_t)kWaves * DB * 4 * 64;   // per slice
+    const float2 *ml = p.ws_ml + (base * nw + rg) * 32 + col;
+    const uint2 *po = p.ws_o + (base * nw + rg) * (DB * 4 * 64) + (db * 4 + i4b) * 64 + lane;
+    const int64_t kMlStride = (int64_t)nw * 32;                   // per slice
+    const int64_t kOStride = (int64_t)nw * DB * 4 * 64;           // per slice
     float2 m_l[kBatch];
     uint2 o[kBatch][I4W];
     // (one request: every tile has nearly all slices, so the early loads are
@@ -792,9 +897,9 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
     const int lo = rq.lo, n = rq.n, P = rq.P;
     const int G = p.hq / p.hkv;
     const int rows_b = n * G;
-    const int row0 = rt * kTileRows;
+    const int row0 = rt * p.tile_rows;
     if (row0 + rg * 32 >= rows_b) return;  // (wave-uniform) no rows in this group
-    const int row_end = min(rows_b, row0 + kTileRows);
+    const int row_end = min(rows_b, row0 + p.tile_rows);
     const int key_end = P + (row_end - 1) / G + 1;
     const int nsplit = min(p.splits, (key_end + p.keys_per_split - 1) / p.keys_per_split);
     const int r = row0 + rg * 32 + col;
@@ -821,7 +926,7 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
         for (int u = 0; u < kBatch; ++u)
             if (u < nb) mb = fmaxf(mb, m_l[u].x);
         const float mref = (mb == -INFINITY) ? 0.f : mb;
-        const float a = __builtin_amdgcn_exp2f((M - mref) * p.c);  // 0 when M = -inf
+        const float a = __builtin_amdgcn_exp2f(M - mref);  // 0 when M = -inf (references in log2 units)
         L *= a;
 #pragma unroll
         for (int ii = 0; ii < I4W; ++ii) {
@@ -834,7 +939,7 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
         for (int u = 0; u < kBatch; ++u) {
             if (u < nb) {
                 // slice weight times its sum: the partial holds O / l
-                const float wl = __builtin_amdgcn_exp2f((m_l[u].x - mref) * p.c) * m_l[u].y;
+                const float wl = __builtin_amdgcn_exp2f(m_l[u].x - mref) * m_l[u].y;
                 L += wl;
 #pragma unroll
                 for (int ii = 0; ii < I4W; ++ii) {
@@ -881,9 +986,9 @@ __device__ __forceinline__ int tile_chunks(const KParams &p, const Req &rq, int 
     if (!rq.ok) return 0;
     const int G = p.hq / p.hkv;
     const int rows_b = rq.n * G;
-    const int row0 = rt * kTileRows;
+    const int row0 = rt * p.tile_rows;
     if (row0 >= rows_b) return 0;
-    const int row_end = min(rows_b, row0 + kTileRows);
+    const int row_end = min(rows_b, row0 + p.tile_rows);
     const int key_end = rq.P + (row_end - 1) / G + 1;
     const int k_lo = s * p.keys_per_split;
     if (k_lo >= key_end) return 0;
@@ -976,8 +1081,19 @@ MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefi
     if (dtype != TV_BF16 || (head_dim != 64 && head_dim != 128) || batch <= 0 || max_nodes * G < 32)
         return plan;
     plan.use = true;
-    plan.rows_per_tile = kTileRows;
-    plan.row_tiles = (max_nodes * G + kTileRows - 1) / kTileRows;
+    // Each wave owns one 32-row block.  8 waves (256-row tiles, two waves
+    // per SIMD) let the waves of a SIMD fill each other's gaps; 4 waves
+    // (128-row tiles) halve the rows per tile, so a single request needs
+    // half the key-axis slices to fill the chip, and writes half the split
+    // partials.  Measured (us per call, cold cache): a single request with at
+    // most 512 rows per KV head is faster with 4 (c3 28.4 against 30.5, c2
+    // 17.3 against 21.4), larger ones and batches with 8 (c4 53.0 against
+    // 65.7, c5 89.6 against 111).
+    const bool small = batch == 1 && (long)max_nodes * G <= 512;
+    plan.waves = (ov && ov->waves) ? ov->waves : (small ? 4 : 8);
+    plan.row_blocks = 1;
+    plan.rows_per_tile = 32 * plan.waves * plan.row_blocks;
+    plan.row_tiles = (max_nodes * G + plan.rows_per_tile - 1) / plan.rows_per_tile;
     const int span = max_prefix + max_nodes;  // longest key axis
     const int chunks = (span + kChunk - 1) / kChunk;
     const long base_tasks = (long)batch * hkv * plan.row_tiles;
@@ -991,6 +1107,10 @@ MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefi
     const bool can_plan = batch > 1 && order != TV_ORDER_STATIC;
     const long target = batch == 1 ? 256 : (can_plan ? 1024 : 640);
     int splits = (int)((target + base_tasks - 1) / base_tasks);
+    // A slice covers at least kMinSliceChunks chunks: below that its split
+    // partial (256 B per row) costs more than the keys it streams save
+    // (c2, 1088 keys: 7 slices 17.3 us, 12 slices 18.3 us, 17 slices 21.4 us).
+    splits = max(1, min(splits, chunks / kMinSliceChunks));
     if (ov && ov->splits > 0) splits = ov->splits;
     if (splits < 1) splits = 1;
     if (splits > chunks) splits = chunks;
@@ -998,7 +1118,7 @@ MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefi
     plan.keys_per_split = cps * kChunk;
     plan.splits = (chunks + cps - 1) / cps;
     if (plan.splits > 1) {
-        const size_t rows = (size_t)base_tasks * plan.splits * kTileRows;
+        const size_t rows = (size_t)base_tasks * plan.splits * plan.rows_per_tile;
         plan.ws_bytes = rows * head_dim * sizeof(uint16_t);
         plan.ws_bytes = (plan.ws_bytes + 255) & ~(size_t)255;
         plan.ws_bytes += rows * sizeof(float2);
@@ -1018,6 +1138,16 @@ int attn_mfma_lookahead(const MfmaPlan &plan) {
     return plan.keys_per_split / kChunk <= kShortSlice ? kAheadShort : kAhead;
 }
 
+namespace {
+template <int D, int NW, int RB>
+void launch_fwd(const KParams &p, const MfmaPlan &plan, long grid, hipStream_t stream) {
+    if (attn_mfma_lookahead(plan) == kAheadShort)
+        hipLaunchKernelGGL((attn_fwd_kernel<D, NW, RB, kAheadShort>), dim3(grid), dim3(64 * NW), 0, stream, p);
+    else
+        hipLaunchKernelGGL((attn_fwd_kernel<D, NW, RB, kAhead>), dim3(grid), dim3(64 * NW), 0, stream, p);
+}
+}  // namespace
+
 hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *workspace, hipStream_t stream) {
     KParams p;
     p.q = (const uint16_t *)a.q;
@@ -1035,6 +1165,8 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *works
     p.hq = a.hq;
     p.hkv = a.hkv;
     p.words = (a.max_nodes + 63) / 64;
+    p.rgroups = plan.rows_per_tile / 32;
+    p.tile_rows = plan.rows_per_tile;
     p.row_tiles = plan.row_tiles;
     p.splits = plan.splits;
     p.keys_per_split = plan.keys_per_split;
@@ -1045,7 +1177,7 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *works
     p.ws_ml = nullptr;
     p.task_table = nullptr;
     if (plan.splits > 1) {
-        const size_t rows = (size_t)a.batch * a.hkv * plan.row_tiles * plan.splits * kTileRows;
+        const size_t rows = (size_t)a.batch * a.hkv * plan.row_tiles * plan.splits * plan.rows_per_tile;
         size_t off = rows * a.head_dim * sizeof(uint16_t);
         off = (off + 255) & ~(size_t)255;
         p.ws_o = (uint2 *)workspace;
@@ -1064,25 +1196,18 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *works
     const long tiles = (long)a.batch * a.hkv * plan.row_tiles;
     // few slices: one merge wave covers all four float4 slots of its channels
     const bool wide = plan.splits <= 8;
-    // short slices: the prologue outweighs the loop, so fewer chunks are
-    // copied ahead of the first barrier
-    const bool short_slices = attn_mfma_lookahead(plan) == kAheadShort;
-    const long cwaves = tiles * kWaves * (a.head_dim / 32) * (wide ? 1 : 4);
+    const long cwaves = tiles * (plan.rows_per_tile / 32) * (a.head_dim / 32) * (wide ? 1 : 4);
     const long cblocks = (cwaves + kCombineWaves - 1) / kCombineWaves;
     if (a.head_dim == 128) {
-        if (short_slices)
-            hipLaunchKernelGGL((attn_fwd_kernel<128, kAheadShort>), dim3(grid), dim3(kThreads), 0, stream, p);
-        else
-            hipLaunchKernelGGL((attn_fwd_kernel<128, kAhead>), dim3(grid), dim3(kThreads), 0, stream, p);
+        if (plan.waves == 8) launch_fwd<128, 8, 1>(p, plan, grid, stream);
+        else launch_fwd<128, 4, 1>(p, plan, grid, stream);
         if (plan.splits > 1 && wide)
             hipLaunchKernelGGL((attn_combine_kernel<128, 4>), dim3(cblocks), dim3(64 * kCombineWaves), 0, stream, p);
         else if (plan.splits > 1)
             hipLaunchKernelGGL((attn_combine_kernel<128, 1>), dim3(cblocks), dim3(64 * kCombineWaves), 0, stream, p);
     } else {
-        if (short_slices)
-            hipLaunchKernelGGL((attn_fwd_kernel<64, kAheadShort>), dim3(grid), dim3(kThreads), 0, stream, p);
-        else
-            hipLaunchKernelGGL((attn_fwd_kernel<64, kAhead>), dim3(grid), dim3(kThreads), 0, stream, p);
+        if (plan.waves == 8) launch_fwd<64, 8, 1>(p, plan, grid, stream);
+        else launch_fwd<64, 4, 1>(p, plan, grid, stream);
         if (plan.splits > 1 && wide)
             hipLaunchKernelGGL((attn_combine_kernel<64, 4>), dim3(cblocks), dim3(64 * kCombineWaves), 0, stream, p);
         else if (plan.splits > 1)

@@ -55,9 +55,10 @@ tv_status check_gdn_conv(int32_t total_or_batch, int32_t channels, int32_t conv_
 // Host-side checks of an override: every reserved field zero, known order.
 bool override_ok(const tv_attn_plan_override *ov) {
     if (!ov) return true;
-    for (int i = 0; i < 6; ++i)
+    for (int i = 0; i < 5; ++i)
         if (ov->reserved[i] != 0) return false;
-    return ov->splits >= 0 && ov->order >= TV_ORDER_AUTO && ov->order <= TV_ORDER_PLANNED;
+    return ov->splits >= 0 && ov->order >= TV_ORDER_AUTO && ov->order <= TV_ORDER_PLANNED &&
+           (ov->waves == 0 || ov->waves == 4 || ov->waves == 8);
 }
 
 // The size checks shared by the call and its plan query; fills *plan.
@@ -72,7 +73,8 @@ tv_status attn_plan_checked(int32_t batch, int32_t total_nodes, int32_t max_node
         // workgroup and merge-wave indices are int on the device
         const int64_t groups = (int64_t)batch * hkv * plan->splits;
         const int64_t grid = (groups + 7) / 8 * plan->row_tiles * 8;
-        const int64_t merge_waves = (int64_t)batch * hkv * plan->row_tiles * 8 * (head_dim / 32) * 4;
+        const int64_t merge_waves =
+            (int64_t)batch * hkv * plan->row_tiles * (plan->rows_per_tile / 32) * (head_dim / 32) * 4;
         if (grid > INT32_MAX || merge_waves > INT32_MAX) return TV_ERR_LIMIT;
     }
     return TV_OK;

@@ -84,6 +84,8 @@ hipError_t launch_attn_valu(const AttnArgs &a, hipStream_t stream);
 // Plan of the MFMA path (split over the key axis, fp32 partials, combine).
 struct MfmaPlan {
     bool use = false;      // MFMA path selected for these sizes
+    int waves = 0;         // wavefronts per workgroup (4 or 8)
+    int row_blocks = 0;    // 32-row blocks per wave (1 or 2)
     int rows_per_tile = 0; // query rows (node x GQA-head pairs) per workgroup
     int row_tiles = 0;     // per (request, KV head), sized for max_nodes
     int splits = 0;        // key-axis splits per row tile (1 = no combine)
