@@ -62,7 +62,8 @@ typedef enum {
     TV_ERR_LIMIT = 4,     /* a size above a library limit (TV_MAX_*)                  */
     TV_ERR_WORKSPACE = 5, /* workspace smaller than the call's *_workspace_size()      */
     TV_ERR_LAUNCH = 6,    /* the HIP runtime refused a launch                         */
-    TV_ERR_ALIGN = 7      /* a pointer breaks the stated alignment                    */
+    TV_ERR_ALIGN = 7,     /* a pointer breaks the stated alignment                    */
+    TV_ERR_SCRATCH = 8    /* the call needs more than the static scratch buffer holds */
 } tv_status;
 
 typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
@@ -215,6 +216,32 @@ tv_status tree_attn_verify_ex(const void *q, const void *k_cache, const void *v_
 tv_status tree_attn_verify_plan(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_prefix,
                                 int32_t hq, int32_t hkv, int32_t head_dim, tv_dtype dtype,
                                 const tv_attn_plan_override *ov, int32_t *info);
+
+/*
+ * tree_attn_verify_noalloc -- tree_attn_verify for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It takes no workspace and calls no
+ * allocating routine.  The split partials and the task table live instead in
+ * a static device buffer of TV_NOALLOC_SCRATCH_BYTES per GPU, which each GPU
+ * the library runs on holds until the process ends; its address on a device
+ * is looked up once, the first time the call runs with that device current.
+ *
+ * Arguments, plan, kernels and results (bit for bit) are those of
+ * tree_attn_verify with the same arguments; so are the errors, plus
+ * TV_ERR_SCRATCH (before anything is enqueued) when the plan needs more than
+ * TV_NOALLOC_SCRATCH_BYTES, i.e. when tree_attn_verify_workspace_size(...)
+ * exceeds it.  All calls on one GPU share that GPU's buffer and each call
+ * overwrites it (nothing in it needs to start at zero): two calls that may
+ * run at the same time on one GPU (streams without ordering between them)
+ * race; order them on one stream.
+ */
+#define TV_NOALLOC_SCRATCH_BYTES (80u << 20) /* 80 MiB per GPU */
+tv_status tree_attn_verify_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                   const int32_t *cu_nodes, const int32_t *kv_start,
+                                   const int32_t *prefix_len, const uint64_t *anc_bits, int32_t batch,
+                                   int32_t total_nodes, int32_t max_nodes, int32_t max_prefix,
+                                   int64_t kv_rows, int32_t hq, int32_t hkv, int32_t head_dim, float scale,
+                                   tv_dtype dtype, void *out, int32_t *err, void *stream);
 
 /*
  * tree_accept_greedy -- temperature-0 acceptance walk.

@@ -148,6 +148,29 @@ def test_attn_override_checked(L):
                                  0.088, 1, FAKE, FAKE, 1 << 40, None, C.byref(ov), None) == OK
 
 
+def test_attn_noalloc_host_checks(L):
+    """The allocation-free call checks its arguments like tree_attn_verify and
+    refuses plans larger than its static scratch before touching the GPU."""
+    def call(B=1, T=128, max_nodes=128, max_prefix=4096, hq=32, hkv=8, d=128, q=FAKE, out=FAKE):
+        return L.tree_attn_verify_noalloc(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, T, max_nodes, max_prefix,
+                                          max_prefix + max_nodes, hq, hkv, d, 0.088, 1, out, None, None)
+    assert call(q=None) == NULL
+    assert call(hq=30) == SHAPE
+    assert call(d=96) == DTYPE
+    assert call(out=FAKE_ODD) == ALIGN
+    assert call(B=0, T=0) == OK
+    # a batch whose split partials exceed the static buffer: 125 requests of
+    # 32 nodes x 8 KV heads are 1000 one-tile tasks, which the planner cuts
+    # into two key slices (2000 x 256 rows x 264 bytes of partials)
+    big = (125, 125 * 32, 32, 4096, 32, 8, 128, 1)
+    assert L.tree_attn_verify_workspace_size(*big) > BND.TV_NOALLOC_SCRATCH_BYTES
+    assert call(*big[:7]) == 8            # TV_ERR_SCRATCH
+    assert b"SCRATCH" in L.tv_status_string(8)
+    # every configuration of the benchmark fits
+    for B, T, n, P in ((1, 64, 64, 1024), (1, 128, 128, 4096), (1, 256, 256, 8192), (8, 1024, 128, 8192)):
+        assert L.tree_attn_verify_workspace_size(B, T, n, P, 32, 8, 128, 1) <= BND.TV_NOALLOC_SCRATCH_BYTES
+
+
 def accept(L, parent=FAKE, dr=FAKE, tg=FAKE, root=FAKE, cu=FAKE, B=1, T=16, D=16, alen=FAKE,
            aidx=FAKE, nxt=FAKE):
     return L.tree_accept_greedy(parent, dr, tg, root, cu, B, T, D, alen, aidx, nxt, None, None)

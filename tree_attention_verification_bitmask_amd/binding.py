@@ -60,6 +60,9 @@ def lib() -> C.CDLL:
     L.tree_attn_verify_ex.restype = C.c_int
     L.tree_attn_verify_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, C.c_int, vp, vp]
     L.tree_attn_verify_plan.restype = C.c_int
+    L.tree_attn_verify_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32, i32,
+                                           f32, C.c_int, vp, vp, vp]
+    L.tree_attn_verify_noalloc.restype = C.c_int
     L.tree_accept_greedy.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp]
     L.tree_accept_greedy.restype = C.c_int
     L.kv_compact_path.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, C.c_int,
@@ -238,6 +241,39 @@ def tree_attn_verify(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc, m
         _check("tree_attn_verify", lib().tree_attn_verify(*args, _stream(stream)))
     else:
         _check("tree_attn_verify_ex", lib().tree_attn_verify_ex(*args, C.byref(ov), _stream(stream)))
+    return out
+
+
+TV_NOALLOC_SCRATCH_BYTES = 80 << 20
+
+
+def tree_attn_verify_noalloc(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc, max_nodes: int,
+                             max_prefix: int, scale: float | None = None, out=None, err=None, stream=None):
+    """tree_attn_verify with no workspace: the library's static per-GPU scratch
+    buffer holds the split partials (calls on one GPU must not overlap)."""
+    import torch
+    T, hq, d = q.shape
+    rows, hkv, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q / k_cache / v_cache shapes disagree")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share a dtype")
+    code = _dtype_code(q)
+    B = cu_nodes.numel() - 1
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n)
+    for t, n in ((cu_nodes, "cu_nodes"), (kv_start, "kv_start"), (prefix_len, "prefix_len")):
+        _need(t, n, torch.int32)
+    _need(anc, "anc", torch.int64, T * ((max_nodes + 63) // 64))
+    out = torch.empty_like(q) if out is None else out
+    _need(out, "out", q.dtype, q.numel())
+    err = torch.zeros(1, dtype=torch.int32, device=q.device) if err is None else err
+    if scale is None:
+        scale = d ** -0.5
+    _check("tree_attn_verify_noalloc", lib().tree_attn_verify_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_nodes), _ptr(kv_start), _ptr(prefix_len),
+        _ptr(anc), B, T, max_nodes, max_prefix, rows, hq, hkv, d, float(scale), code, _ptr(out),
+        _ptr(err), _stream(stream)))
     return out
 
 

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "treeverify.h"
 #include "tv_launch.h"
 
@@ -80,6 +82,85 @@ tv_status attn_plan_checked(int32_t batch, int32_t total_nodes, int32_t max_node
     return TV_OK;
 }
 
+// Every host check of tree_attn_verify except the workspace's; fills *plan.
+tv_status attn_args_checked(const void *q, const void *k_cache, const void *v_cache, const int32_t *cu_nodes,
+                            const int32_t *kv_start, const int32_t *prefix_len, const uint64_t *anc_bits,
+                            int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_prefix,
+                            int64_t kv_rows, int32_t hq, int32_t hkv, int32_t head_dim, float scale, tv_dtype dtype,
+                            const void *out, const tv_attn_plan_override *ov, tv::MfmaPlan *plan) {
+    tv_status st =
+        attn_plan_checked(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype, ov, plan);
+    if (st != TV_OK) return st;
+    if (kv_rows < 0) return TV_ERR_SHAPE;
+    if (!(scale > 0.f) || scale != scale) return TV_ERR_SHAPE;
+    if (!cu_nodes || !kv_start || !prefix_len) return TV_ERR_NULL;
+    if (total_nodes > 0 && (!q || !out || !anc_bits)) return TV_ERR_NULL;
+    if (kv_rows > 0 && (!k_cache || !v_cache)) return TV_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+        !aligned(anc_bits, 8))
+        return TV_ERR_ALIGN;
+    return TV_OK;
+}
+
+// Enqueues the call whose arguments have passed the checks above.
+tv_status attn_launch(const void *q, const void *k_cache, const void *v_cache, const int32_t *cu_nodes,
+                      const int32_t *kv_start, const int32_t *prefix_len, const uint64_t *anc_bits, int32_t batch,
+                      int32_t total_nodes, int32_t max_nodes, int32_t max_prefix, int64_t kv_rows, int32_t hq,
+                      int32_t hkv, int32_t head_dim, float scale, tv_dtype dtype, void *out, void *workspace,
+                      int32_t *err, const tv::MfmaPlan &plan, void *stream) {
+    if (batch == 0 || total_nodes == 0) return TV_OK;
+    tv::AttnArgs a;
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.cu_nodes = cu_nodes;
+    a.kv_start = kv_start;
+    a.prefix_len = prefix_len;
+    a.anc = anc_bits;
+    a.batch = batch;
+    a.total_nodes = total_nodes;
+    a.max_nodes = max_nodes;
+    a.max_prefix = max_prefix;
+    a.kv_rows = kv_rows;
+    a.hq = hq;
+    a.hkv = hkv;
+    a.head_dim = head_dim;
+    a.scale = scale;
+    a.dtype = dtype;
+    a.out = out;
+    a.err = err;
+    if (plan.use) return launch_status(tv::launch_attn_mfma(a, plan, workspace, (hipStream_t)stream));
+    return launch_status(tv::launch_attn_valu(a, (hipStream_t)stream));
+}
+
+// Scratch of tree_attn_verify_noalloc: one copy per GPU, for the whole
+// process.  In host code `scratch` names a host-side stand-in, not device
+// memory; the device address of each GPU's copy is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is
+// ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[TV_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up on first use.
+hipError_t scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -94,6 +175,9 @@ const char *tv_status_string(int status) {
         case TV_ERR_WORKSPACE: return "TV_ERR_WORKSPACE: workspace too small or misaligned";
         case TV_ERR_LAUNCH: return "TV_ERR_LAUNCH: the HIP runtime refused a launch";
         case TV_ERR_ALIGN: return "TV_ERR_ALIGN: a pointer breaks the required alignment";
+        case TV_ERR_SCRATCH:
+            return "TV_ERR_SCRATCH: the call needs more than the static scratch buffer "
+                   "(TV_NOALLOC_SCRATCH_BYTES) of tree_attn_verify_noalloc holds";
         default: return "unknown tv_status";
     }
 }
@@ -162,44 +246,39 @@ tv_status tree_attn_verify_ex(const void *q, const void *k_cache, const void *v_
                               void *workspace, size_t workspace_bytes, int32_t *err,
                               const tv_attn_plan_override *ov, void *stream) {
     tv::MfmaPlan plan;
-    tv_status st =
-        attn_plan_checked(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype, ov, &plan);
+    const tv_status st = attn_args_checked(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc_bits, batch,
+                                           total_nodes, max_nodes, max_prefix, kv_rows, hq, hkv, head_dim, scale,
+                                           dtype, out, ov, &plan);
     if (st != TV_OK) return st;
-    if (kv_rows < 0) return TV_ERR_SHAPE;
-    if (!(scale > 0.f) || scale != scale) return TV_ERR_SHAPE;
-    if (!cu_nodes || !kv_start || !prefix_len) return TV_ERR_NULL;
-    if (total_nodes > 0 && (!q || !out || !anc_bits)) return TV_ERR_NULL;
-    if (kv_rows > 0 && (!k_cache || !v_cache)) return TV_ERR_NULL;
-    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
-        !aligned(anc_bits, 8))
-        return TV_ERR_ALIGN;
     if (plan.use && plan.ws_bytes > 0) {
         if (!workspace || workspace_bytes < plan.ws_bytes) return TV_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return TV_ERR_ALIGN;
     }
+    return attn_launch(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc_bits, batch, total_nodes, max_nodes,
+                       max_prefix, kv_rows, hq, hkv, head_dim, scale, dtype, out, workspace, err, plan, stream);
+}
+
+tv_status tree_attn_verify_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                   const int32_t *cu_nodes, const int32_t *kv_start,
+                                   const int32_t *prefix_len, const uint64_t *anc_bits, int32_t batch,
+                                   int32_t total_nodes, int32_t max_nodes, int32_t max_prefix,
+                                   int64_t kv_rows, int32_t hq, int32_t hkv, int32_t head_dim, float scale,
+                                   tv_dtype dtype, void *out, int32_t *err, void *stream) {
+    // Every host check first (nothing touches the runtime before they pass),
+    // then the plan's workspace against the buffer's size.
+    tv::MfmaPlan plan;
+    const tv_status st = attn_args_checked(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc_bits, batch,
+                                           total_nodes, max_nodes, max_prefix, kv_rows, hq, hkv, head_dim, scale,
+                                           dtype, out, nullptr, &plan);
+    if (st != TV_OK) return st;
+    if (plan.use && plan.ws_bytes > (size_t)TV_NOALLOC_SCRATCH_BYTES) return TV_ERR_SCRATCH;
     if (batch == 0 || total_nodes == 0) return TV_OK;
-    tv::AttnArgs a;
-    a.q = q;
-    a.k = k_cache;
-    a.v = v_cache;
-    a.cu_nodes = cu_nodes;
-    a.kv_start = kv_start;
-    a.prefix_len = prefix_len;
-    a.anc = anc_bits;
-    a.batch = batch;
-    a.total_nodes = total_nodes;
-    a.max_nodes = max_nodes;
-    a.max_prefix = max_prefix;
-    a.kv_rows = kv_rows;
-    a.hq = hq;
-    a.hkv = hkv;
-    a.head_dim = head_dim;
-    a.scale = scale;
-    a.dtype = dtype;
-    a.out = out;
-    a.err = err;
-    if (plan.use) return launch_status(tv::launch_attn_mfma(a, plan, workspace, (hipStream_t)stream));
-    return launch_status(tv::launch_attn_valu(a, (hipStream_t)stream));
+    // The current device's buffer (looked up once per device) when the plan
+    // needs a workspace at all.
+    void *ws = nullptr;
+    if (plan.use && plan.ws_bytes > 0 && scratch_address(&ws) != hipSuccess) return TV_ERR_LAUNCH;
+    return attn_launch(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc_bits, batch, total_nodes, max_nodes,
+                       max_prefix, kv_rows, hq, hkv, head_dim, scale, dtype, out, ws, err, plan, stream);
 }
 
 tv_status tree_attn_verify(const void *q, const void *k_cache, const void *v_cache,
