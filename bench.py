@@ -415,7 +415,8 @@ def time_pass(args, torch, BND, L, dev, wl, steps: int, warmup: int) -> dict:
         if ov is None:
             st |= L.tree_attn_verify(*attn_args[r])
         else:
-            st |= L.tree_attn_verify_ex(*attn_args[r][:-1], ctypes.byref(ov), attn_args[r][-1])
+            a = attn_args[r]   # (..., scale, dtype, out, workspace, bytes, err, stream): no optional inputs
+            st |= L.tree_attn_verify_ex(*a[:17], None, *a[17:-1], ctypes.byref(ov), a[-1])
         if ev is not None:
             ev[1].record(stream)
         if args.separate_commit:

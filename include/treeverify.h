@@ -84,6 +84,7 @@ typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
 #define TV_DEVERR_BAD_PATH 4    /* accepted path entry out of range; index = b           */
 #define TV_DEVERR_BAD_LEDGER 5  /* chosen slot whose parent is unusable; index = b       */
 #define TV_DEVERR_LIMIT 6       /* a request above a per-request limit; index = b        */
+#define TV_DEVERR_BAD_SLOT 7    /* token-table entry outside [0, kv_rows); index = b     */
 
 /* Human-readable name of a tv_status value (static string). */
 const char *tv_status_string(int status);
@@ -141,7 +142,7 @@ size_t tree_attn_verify_workspace_size(int32_t batch, int32_t total_nodes, int32
  *   out[i,h] = sum_t softmax_t(scale * q[i,h] . k[t,g]) v[t,g]
  *   over t in {kv_start[b] + 0 .. P_b-1} U {kv_start[b] + P_b + j : j in anc(i)}.
  * Q and K arrive with positions already applied (pos_ids above feed the
- * caller's RoPE).
+ * caller's RoPE, or tree_attn_verify_ex applies it).
  *
  * In:  q [T, hq, head_dim]; k_cache, v_cache [kv_rows, hkv, head_dim]
  *      (dtype elements, 16-byte aligned); cu_nodes, kv_start, prefix_len
@@ -162,6 +163,37 @@ tv_status tree_attn_verify(const void *q, const void *k_cache, const void *v_cac
                            int32_t max_nodes, int32_t max_prefix, int64_t kv_rows, int32_t hq,
                            int32_t hkv, int32_t head_dim, float scale, tv_dtype dtype, void *out,
                            void *workspace, size_t workspace_bytes, int32_t *err, void *stream);
+
+/*
+ * Optional inputs of tree_attn_verify_ex (a NULL pointer: none of them).
+ *
+ * RoPE inside the call (rope_base > 0).  Defines: [TSD] "The Tree Attention
+ * Mechanism", part 3 "Tree Positional IDs": node t is rotated at position
+ * pos_ids[t] (from tree_mask_build).  The rotation is tree_rope_apply's (same
+ * reading, same base): q is rotated as the kernel loads it (q itself is not
+ * written), and the tree's K rows are rotated in place in k_cache, bit for bit
+ * as tree_rope_apply writes them, so the cache holds rotated keys for the
+ * rounds that follow acceptance.  The call then reads q and the tree's K rows
+ * unrotated, i.e. as they come out of the projections.  The workspace also
+ * holds each node's cosines and sines (4 * head_dim bytes per node).
+ *
+ * K/V through a token table (req_to_token != NULL).  Defines: [TSD] "KV
+ * Cache Rollback" (paged caches drop unaccepted nodes by page-table updates;
+ * kv_rollback_token_table keeps such a table).  Key position p of request b
+ * (prefix positions 0 .. P_b - 1, then tree node j at P_b + j) is cache row
+ * req_to_token[b * table_stride + p]; kv_start is not read and may be NULL.
+ * Every request needs P_b + N_b <= table_stride (else BAD_REQUEST, its output
+ * rows not written); an entry outside [0, kv_rows) is reported as BAD_SLOT
+ * and row 0 is read in its place (that request's output is then meaningless).
+ * req_to_token is 4-byte aligned.
+ */
+typedef struct {
+    const int32_t *pos_ids;      /* [T]; read when rope_base > 0 */
+    const int32_t *req_to_token; /* [B, table_stride], or NULL: contiguous rows from kv_start */
+    int64_t table_stride;        /* >= 1 when req_to_token is set */
+    float rope_base;             /* 0: no rotation; else > 0 and finite (the model's rope theta) */
+    int32_t reserved[5];         /* must be zero */
+} tv_attn_inputs;
 
 /*
  * Plan overrides for tree_attn_verify: tuning and tests only.
@@ -191,16 +223,28 @@ typedef struct {
     int32_t reserved[5]; /* must be zero */
 } tv_attn_plan_override;
 
+/*
+ * tree_attn_verify_ex -- tree_attn_verify with the optional inputs above
+ * (in, may be NULL) and a plan override (ov, may be NULL).  With
+ * in->rope_base > 0 the call writes k_cache (the tree's K rows); otherwise it
+ * only reads it.  With both NULL it is tree_attn_verify.  Its workspace is
+ * tree_attn_verify_workspace_size_ex(...) with the same in and ov.
+ * Host errors as tree_attn_verify's, plus: TV_ERR_SHAPE for nonzero reserved
+ * fields, a rope_base that is negative or not finite, or table_stride < 1 with
+ * a table; TV_ERR_NULL for a missing pos_ids (rope on), or a missing kv_start
+ * without a table; TV_ERR_ALIGN for a req_to_token not 4-byte aligned.
+ */
 size_t tree_attn_verify_workspace_size_ex(int32_t batch, int32_t total_nodes, int32_t max_nodes,
                                           int32_t max_prefix, int32_t hq, int32_t hkv, int32_t head_dim,
-                                          tv_dtype dtype, const tv_attn_plan_override *ov);
-tv_status tree_attn_verify_ex(const void *q, const void *k_cache, const void *v_cache,
-                              const int32_t *cu_nodes, const int32_t *kv_start, const int32_t *prefix_len,
-                              const uint64_t *anc_bits, int32_t batch, int32_t total_nodes,
-                              int32_t max_nodes, int32_t max_prefix, int64_t kv_rows, int32_t hq,
-                              int32_t hkv, int32_t head_dim, float scale, tv_dtype dtype, void *out,
-                              void *workspace, size_t workspace_bytes, int32_t *err,
-                              const tv_attn_plan_override *ov, void *stream);
+                                          tv_dtype dtype, const tv_attn_inputs *in,
+                                          const tv_attn_plan_override *ov);
+tv_status tree_attn_verify_ex(const void *q, void *k_cache, const void *v_cache, const int32_t *cu_nodes,
+                              const int32_t *kv_start, const int32_t *prefix_len, const uint64_t *anc_bits,
+                              int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_prefix,
+                              int64_t kv_rows, int32_t hq, int32_t hkv, int32_t head_dim, float scale,
+                              tv_dtype dtype, const tv_attn_inputs *in, void *out, void *workspace,
+                              size_t workspace_bytes, int32_t *err, const tv_attn_plan_override *ov,
+                              void *stream);
 
 /*
  * tree_attn_verify_plan -- the plan tree_attn_verify(_ex) would run for these
@@ -209,8 +253,8 @@ tv_status tree_attn_verify_ex(const void *q, const void *k_cache, const void *v_
  *   [1] query rows per workgroup tile   [2] row tiles per (request, KV head)
  *   [3] key-axis slices                 [4] keys per slice
  *   [5] 1 = planned (longest-first) task order for a batch
- *   [6] chunks copied ahead of use      [7] workspace bytes (saturated to
- *       INT32_MAX)
+ *   [6] chunks copied ahead of use      [7] workspace bytes without
+ *       tv_attn_inputs (saturated to INT32_MAX)
  * Returns the same host-side status the call itself would for these sizes.
  */
 tv_status tree_attn_verify_plan(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_prefix,

@@ -135,7 +135,7 @@ def test_attn_override_checked(L):
             BND.PlanOverride(0, 0, 5), BND.PlanOverride(0, 0, 2))
     for bad in bads:
         assert L.tree_attn_verify_plan(*args, C.byref(bad), info) == SHAPE
-        assert L.tree_attn_verify_workspace_size_ex(*args, C.byref(bad)) == 0
+        assert L.tree_attn_verify_workspace_size_ex(*args, None, C.byref(bad)) == 0
     # 32 rows per wave: 4 or 8 waves per workgroup
     d64 = (1, 128, 128, 4096, 16, 4, 64, 1)
     for a in (args, d64):
@@ -143,9 +143,47 @@ def test_attn_override_checked(L):
         assert BND.tree_attn_verify_plan(*a, waves=8)["rows_per_tile"] == 256
     # the plain call's checks are the _ex call's checks
     assert L.tree_attn_verify_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 128, 128, 4096, 4224, 30, 8, 128,
-                                 0.088, 1, FAKE, FAKE, 1 << 40, None, None, None) == SHAPE
+                                 0.088, 1, None, FAKE, FAKE, 1 << 40, None, None, None) == SHAPE
     assert L.tree_attn_verify_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 128, 4096, 4224, 32, 8, 128,
-                                 0.088, 1, FAKE, FAKE, 1 << 40, None, C.byref(ov), None) == OK
+                                 0.088, 1, None, FAKE, FAKE, 1 << 40, None, C.byref(ov), None) == OK
+
+
+def test_attn_inputs_checked(L):
+    """tv_attn_inputs: RoPE and token-table options are checked on the host,
+    and RoPE adds the nodes' (cos, sin) pairs to the workspace."""
+    T, d = 128, 128
+    sizes = (1, T, 128, 4096, 32, 8, d, 1)
+
+    def ex(inp, ks=FAKE, B=1, T_=T, rows=4224, ws=1 << 40):
+        return L.tree_attn_verify_ex(FAKE, FAKE, FAKE, FAKE, ks, FAKE, FAKE, B, T_, 128, 4096, rows, 32, 8, d, 0.088,
+                                     1, C.byref(inp) if inp is not None else None, FAKE, FAKE, ws, None, None, None)
+
+    FA = FAKE.value
+
+    def inp(pos=FA, tab=None, stride=0, base=0.0, res=0):
+        r = (C.c_int32 * 5)()
+        r[2] = res
+        return BND.AttnInputs(pos, tab, stride, base, r)
+    assert ex(inp(res=1)) == SHAPE                       # reserved field set
+    assert ex(inp(base=-1.0)) == SHAPE
+    assert ex(inp(base=float("nan"))) == SHAPE
+    assert ex(inp(base=float("inf"))) == SHAPE
+    assert ex(inp(tab=FA, stride=0)) == SHAPE          # a table needs a stride
+    assert ex(inp(pos=None, base=1e6)) == NULL           # RoPE needs positions
+    assert ex(inp(tab=None), ks=None) == NULL            # contiguous rows need kv_start
+    assert ex(inp(tab=FA + 2, stride=4224), ks=None) == ALIGN
+    assert ex(inp(tab=FA, stride=4224), ks=None, rows=0) == SHAPE   # row 0 must exist
+    assert ex(inp(pos=None, base=1e6), B=0, T_=0) == OK  # nothing to do: nothing read
+    # workspace: the plan's, then T * d/2 (cos, sin) pairs at a 256-byte boundary
+    base = L.tree_attn_verify_workspace_size(*sizes)
+    rope = L.tree_attn_verify_workspace_size_ex(*sizes, C.byref(inp(base=1e6)), None)
+    assert rope == ((base + 255) // 256 * 256) + T * (d // 2) * 8
+    assert L.tree_attn_verify_workspace_size_ex(*sizes, C.byref(inp(tab=FA, stride=9000)), None) == base
+    assert L.tree_attn_verify_workspace_size_ex(*sizes, C.byref(inp(res=1)), None) == 0
+    assert ex(inp(base=1e6), ws=rope - 1) == WS
+    # the vector path (fp32) needs only the pairs
+    f32 = (1, T, 128, 4096, 32, 8, d, 0)
+    assert L.tree_attn_verify_workspace_size_ex(*f32, C.byref(inp(base=1e6)), None) == T * (d // 2) * 8
 
 
 def test_attn_noalloc_host_checks(L):

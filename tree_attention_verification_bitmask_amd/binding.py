@@ -20,6 +20,7 @@ TV_F32, TV_BF16 = 0, 1
 TV_MAX_NODES, TV_MAX_DEPTH, TV_MAX_LEDGER, TV_MAX_VOCAB = 1024, 64, 8192, 16777216
 DEVERR_BAD_PARENT, DEVERR_TOO_DEEP, DEVERR_BAD_REQUEST, DEVERR_BAD_PATH, DEVERR_BAD_LEDGER = 1, 2, 3, 4, 5
 DEVERR_LIMIT = 6
+DEVERR_BAD_SLOT = 7
 TV_GDN_HEAD_DIM, TV_GDN_MAX_NODES, TV_GDN_MAX_TABLE = 128, 256, 4096
 
 
@@ -53,10 +54,10 @@ def lib() -> C.CDLL:
     L.tree_attn_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32, i32,
                                    f32, C.c_int, vp, vp, sz, vp, vp]
     L.tree_attn_verify.restype = C.c_int
-    L.tree_attn_verify_workspace_size_ex.argtypes = [i32, i32, i32, i32, i32, i32, i32, C.c_int, vp]
+    L.tree_attn_verify_workspace_size_ex.argtypes = [i32, i32, i32, i32, i32, i32, i32, C.c_int, vp, vp]
     L.tree_attn_verify_workspace_size_ex.restype = sz
     L.tree_attn_verify_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32, i32,
-                                      f32, C.c_int, vp, vp, sz, vp, vp, vp]
+                                      f32, C.c_int, vp, vp, vp, sz, vp, vp, vp]
     L.tree_attn_verify_ex.restype = C.c_int
     L.tree_attn_verify_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, C.c_int, vp, vp]
     L.tree_attn_verify_plan.restype = C.c_int
@@ -179,15 +180,31 @@ def _override(splits: int = 0, order: int = TV_ORDER_AUTO, waves: int = 0):
     return PlanOverride(int(splits), int(order), int(waves))
 
 
+class AttnInputs(C.Structure):
+    """tv_attn_inputs: RoPE inside the call (rope_base > 0, positions pos_ids)
+    and K/V rows through a token table (req_to_token [B, table_stride])."""
+    _fields_ = [("pos_ids", C.c_void_p), ("req_to_token", C.c_void_p), ("table_stride", C.c_int64),
+                ("rope_base", C.c_float), ("reserved", C.c_int32 * 5)]
+
+
+def _inputs(pos_ids=None, rope_base: float = 0.0, req_to_token=None):
+    if not rope_base and req_to_token is None:
+        return None
+    stride = 0 if req_to_token is None else int(req_to_token.shape[-1])
+    addr = lambda t: None if t is None else int(t.data_ptr())
+    return AttnInputs(addr(pos_ids) if rope_base else None, addr(req_to_token), stride, float(rope_base))
+
+
 def tree_attn_verify_workspace_size(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim,
                                     dtype_code, splits: int = 0, order: int = TV_ORDER_AUTO,
-                                    waves: int = 0) -> int:
+                                    waves: int = 0, inputs=None) -> int:
     ov = _override(splits, order, waves)
-    if ov is None:
+    if ov is None and inputs is None:
         return int(lib().tree_attn_verify_workspace_size(batch, total_nodes, max_nodes, max_prefix, hq,
                                                          hkv, head_dim, dtype_code))
-    return int(lib().tree_attn_verify_workspace_size_ex(batch, total_nodes, max_nodes, max_prefix, hq, hkv,
-                                                        head_dim, dtype_code, C.byref(ov)))
+    return int(lib().tree_attn_verify_workspace_size_ex(
+        batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype_code,
+        C.byref(inputs) if inputs is not None else None, C.byref(ov) if ov is not None else None))
 
 
 PLAN_FIELDS = ("mfma", "rows_per_tile", "row_tiles", "splits", "keys_per_split", "planned", "lookahead",
@@ -207,9 +224,14 @@ def tree_attn_verify_plan(batch, total_nodes, max_nodes, max_prefix, hq, hkv, he
 
 def tree_attn_verify(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc, max_nodes: int,
                      max_prefix: int, scale: float | None = None, out=None, workspace=None,
-                     err=None, stream=None, splits: int = 0, order: int = TV_ORDER_AUTO, waves: int = 0):
+                     err=None, stream=None, splits: int = 0, order: int = TV_ORDER_AUTO, waves: int = 0,
+                     pos_ids=None, rope_base: float = 0.0, req_to_token=None):
     """q [T, hq, d]; k_cache / v_cache [rows, hkv, d] -> out [T, hq, d] (same dtype).
-    splits / order: a plan override (tree_attn_verify_ex), for tuning and tests."""
+    splits / order / waves: a plan override, for tuning and tests; pos_ids and
+    rope_base > 0: RoPE inside the call (the tree's K rows of k_cache are
+    rotated in place); req_to_token [B, stride] int32: K/V rows through a token
+    table (kv_start may then be None).  Any of these goes through
+    tree_attn_verify_ex."""
     import torch
     T, hq, d = q.shape
     rows, hkv, d2 = k_cache.shape
@@ -222,25 +244,34 @@ def tree_attn_verify(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc, m
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _need(t, n)
     for t, n in ((cu_nodes, "cu_nodes"), (kv_start, "kv_start"), (prefix_len, "prefix_len")):
-        _need(t, n, torch.int32)
+        if t is not None or n != "kv_start" or req_to_token is None:
+            _need(t, n, torch.int32)
+    if req_to_token is not None:
+        _need(req_to_token, "req_to_token", torch.int32, B * int(req_to_token.shape[-1]))
+    if rope_base:
+        _need(pos_ids, "pos_ids", torch.int32, T)
     _need(anc, "anc", torch.int64, T * ((max_nodes + 63) // 64))
     out = torch.empty_like(q) if out is None else out
     _need(out, "out", q.dtype, q.numel())
     err = torch.zeros(1, dtype=torch.int32, device=q.device) if err is None else err
-    ws_bytes = tree_attn_verify_workspace_size(B, T, max_nodes, max_prefix, hq, hkv, d, code, splits, order, waves)
+    inputs = _inputs(pos_ids, rope_base, req_to_token)
+    ws_bytes = tree_attn_verify_workspace_size(B, T, max_nodes, max_prefix, hq, hkv, d, code, splits, order, waves,
+                                               inputs)
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if scale is None:
         scale = d ** -0.5
-    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_nodes), _ptr(kv_start), _ptr(prefix_len),
-            _ptr(anc), B, T, max_nodes, max_prefix, rows, hq, hkv, d, float(scale), code, _ptr(out),
-            _ptr(workspace), ws_have, _ptr(err))
+    head = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_nodes), _ptr(kv_start), _ptr(prefix_len),
+            _ptr(anc), B, T, max_nodes, max_prefix, rows, hq, hkv, d, float(scale), code)
+    tail = (_ptr(out), _ptr(workspace), ws_have, _ptr(err))
     ov = _override(splits, order, waves)
-    if ov is None:
-        _check("tree_attn_verify", lib().tree_attn_verify(*args, _stream(stream)))
+    if ov is None and inputs is None:
+        _check("tree_attn_verify", lib().tree_attn_verify(*head, *tail, _stream(stream)))
     else:
-        _check("tree_attn_verify_ex", lib().tree_attn_verify_ex(*args, C.byref(ov), _stream(stream)))
+        _check("tree_attn_verify_ex", lib().tree_attn_verify_ex(
+            *head, C.byref(inputs) if inputs is not None else None, *tail,
+            C.byref(ov) if ov is not None else None, _stream(stream)))
     return out
 
 

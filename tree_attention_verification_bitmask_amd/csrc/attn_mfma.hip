@@ -125,6 +125,7 @@ struct Geo {
     static constexpr int kDB = D / 32;                      // 32-channel blocks of O
     static constexpr int kRingBytes = 2 * kStages * kHalf;  // K ring + V ring
     static constexpr int kTileRows = 32 * NW * RB;  // RB blocks of 32 rows per wave
+    static constexpr int kRowsPerDma = 1024 / kRowBytes;   // cache rows one wave-wide copy covers
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     static_assert(RB == 1 || RB == 2, "one or two 32-row blocks per wave");
     static_assert(kTileRows <= kMaxTileRows, "ancestor rows of the tile fit their LDS area");
@@ -169,8 +170,27 @@ __device__ __forceinline__ void dma16(const char *base, uint32_t voff, uint32_t 
         : "v"(voff), "s"(base), "s"(lds)
         : "memory");
 }
+// The same from a per-lane 64-bit address.
+__device__ __forceinline__ void dma16_at(const char *addr, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(addr), "s"(lds)
+        : "memory");
+}
 // The same with 4 bytes per lane (to lds + 4 * lane).
-__device__ __forceinline__ void dma4(const char *base, uint32_t voff, uint32_t lds) {
+__device__ __forceinline__ void dma4(const char *base_in, uint32_t voff, uint32_t lds) {
+    // (the base is wave-uniform; said explicitly, so that it stays in scalar
+    // registers whatever the compiler's uniformity analysis concludes)
+    const uint64_t bu = (uint64_t)(uintptr_t)base_in;
+    const uint32_t blo = __builtin_amdgcn_readfirstlane((uint32_t)bu);
+    const uint32_t bhi = __builtin_amdgcn_readfirstlane((uint32_t)(bu >> 32));
+    const char *base = (const char *)(uintptr_t)(((uint64_t)bhi << 32) | blo);
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
@@ -221,6 +241,10 @@ struct KParams {
     float2 *ws_ml;  // partial (m, l) per row
     const int32_t *task_table;  // batches: task of each workgroup, longest first (or null)
     int32_t *err;
+    const int32_t *table;    // token table [batch, tstride]: cache row of each key position (or null)
+    int64_t tstride;
+    int kvr32;               // min(kv_rows, INT32_MAX): bound of a table entry
+    const float2 *rope_cs;   // (cos, sin) [T, D/2] to rotate q at load (or null)
 };
 
 // Sizes of request b, with all four reads issued before any test: a chain of
@@ -236,11 +260,14 @@ __device__ __forceinline__ Req load_request(const KParams &p, int b) {
     const int c0 = p.cu_nodes[b];
     const int c1 = p.cu_nodes[b + 1];
     r.P = p.prefix_len[b];
-    r.ks = p.kv_start[b];
+    r.ks = p.table ? 0 : p.kv_start[b];
     r.lo = c0;
     r.n = c1 - c0;
+    // through a token table the request's positions must fit its table row;
+    // otherwise its rows must fit the cache
+    const bool rows_bad = p.table ? ((int64_t)r.P + r.n > p.tstride) : ((r.ks < 0) | (r.ks + r.P + r.n > p.kv_rows));
     const bool bad = (c0 < 0) | (c1 < c0) | (c1 > p.total_nodes) | (r.n > p.max_nodes) | (r.P < 0) |
-                     (r.P > p.max_prefix) | (r.ks < 0) | (r.ks + r.P + r.n > p.kv_rows);
+                     (r.P > p.max_prefix) | rows_bad;
     r.ok = !bad;
     return r;
 }
@@ -323,8 +350,8 @@ __device__ __forceinline__ bool decode_task(const KParams &p, int wid, Task *t) 
 // NW = waves per workgroup; RB = 32-row blocks per wave (two blocks share
 // every K and V operand read from LDS, halving LDS and L2 traffic per
 // product); AH = copy look-ahead in chunks (AH for long slices, fewer for
-// short ones).
-template <int D, int NW, int RB, int AH>
+// short ones); PAGED: K/V rows through the token table.
+template <int D, int NW, int RB, int AH, bool PAGED>
 __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_kernel(KParams p) {
     using Gm = Geo<D, NW, RB>;
     constexpr int KS = Gm::kKS, DB = Gm::kDB, PW = Gm::kDmaPerWave, TR = Gm::kTileRows;
@@ -367,8 +394,11 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_kernel(KParams p) {
 
     const int64_t row_stride = (int64_t)p.hkv * D * 2;  // bytes per cache row
     const int64_t chunk_bytes = kChunk * row_stride;
-    const char *kbase = reinterpret_cast<const char *>(p.k) + (ks + k_lo) * row_stride + (int64_t)g * D * 2;
-    const char *vbase = reinterpret_cast<const char *>(p.v) + (ks + k_lo) * row_stride + (int64_t)g * D * 2;
+    // (through a token table a chunk's rows are anywhere: the bases are the
+    // head's column of row 0, and each copy adds its own row)
+    const int64_t kv_off = PAGED ? (int64_t)g * D * 2 : (ks + k_lo) * row_stride + (int64_t)g * D * 2;
+    const char *kbase = reinterpret_cast<const char *>(p.k) + kv_off;
+    const char *vbase = reinterpret_cast<const char *>(p.v) + kv_off;
     const uint32_t ring = (uint32_t)(uintptr_t)smem;
 
     // ---- DMA role: the first NW/2 waves copy the K half of every chunk, the
@@ -415,6 +445,73 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_kernel(KParams p) {
         for (int jj = 0; jj < PW; ++jj) issue1(c, stage, jj);
     };
 
+    // ---- token-table path.  A copy needs the cache row of each of its keys.
+    // In the loop the rows come by scalar loads (their own counter, apart
+    // from the copies' vector-memory counter, so the copy waits are the same
+    // as without a table): the rows of the next period's chunks are loaded
+    // right after this period's chunks are copied, into the same registers,
+    // and have a whole period to arrive.  A copy covers groups of 4 cache rows
+    // whose keys are consecutive (also in the K order key_of_slot), so a lane
+    // picks its row from the 4 values of its group.  Keys past the slice end
+    // are clamped to its last key, as in the contiguous path.
+    constexpr int RPD = Gm::kRowsPerDma;
+    constexpr int G4 = RPD / 4;  // groups of 4 rows per copy
+    typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+    const_i32_t *tab =
+        reinterpret_cast<const_i32_t *>((uintptr_t)(PAGED ? p.table + (int64_t)b * p.tstride + k_lo : nullptr));
+    // first key of group gi of copy jj of this wave (wave-uniform)
+    auto group_key = [&](int jj, int gi) __attribute__((always_inline)) {
+        const int row = (part0 + jj) * RPD + 4 * gi;
+        return dv ? row : key_of_slot(row);
+    };
+    uint32_t goff[PW];  // the lane's 16-byte granule within its row (as in dma_off)
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+        const int byte = (part0 + j) * 1024 + lane * 16;
+        const int row = byte / Gm::kRowBytes;
+        const int pos = (byte % Gm::kRowBytes) >> 4;
+        goff[j] = (uint32_t)((pos ^ (dv ? v_swz<D>(row) : k_swz<D>(row))) << 4);
+    }
+    const int lrow = (lane * 16) / Gm::kRowBytes;  // the lane's row within a copy (0 .. RPD-1)
+    bool slot_bad = false;  // a table entry outside the cache (reported at the end)
+    // Copy jj of chunk c into ring stage `stage` from cache row `row`.
+    auto copy_row = [&](uint32_t stage, int jj, int32_t row_in) __attribute__((always_inline)) {
+        uint32_t row = (uint32_t)row_in;
+        if (row >= (uint32_t)p.kvr32) {
+            slot_bad = true;
+            row = 0;
+        }
+        const char *a = dbase + (int64_t)row * row_stride + goff[jj];
+        dma16_at(a, __builtin_amdgcn_readfirstlane(dlds + stage * kHalf + jj * 1024));
+    };
+    // The rows of one period's chunks, wave-uniform (scalar registers).
+    int32_t srow[PAGED ? BP : 1][PW][G4][4];
+    auto load_rows = [&](int cc, int c) __attribute__((always_inline)) {
+        const int cap = c == clamp_c ? last_keys - 1 : kChunk - 1;
+#pragma unroll
+        for (int jj = 0; jj < PW; ++jj)
+#pragma unroll
+            for (int gi = 0; gi < G4; ++gi)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) srow[cc][jj][gi][e] = tab[c * kChunk + min(group_key(jj, gi) + e, cap)];
+    };
+    // (each candidate goes through an empty asm first: the selection is then
+    // among plain values, which the compiler cannot turn back into an indexed
+    // load from the array, an index that would move the array to scratch)
+    auto issue_rows = [&](int cc, int c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int jj = 0; jj < PW; ++jj) {
+            int32_t v = 0;
+#pragma unroll
+            for (int k = 0; k < 4 * G4; ++k) {
+                int32_t x = srow[cc][jj][k >> 2][k & 3];
+                asm volatile("" : "+s"(x));
+                v = lrow == k ? x : v;
+            }
+            copy_row((uint32_t)(c % kStages), jj, v);
+        }
+    };
+
     // ---- prologue --------------------------------------------------------------
     // (1) the packed ancestor rows of the tile's nodes -> LDS, if the slice
     // reaches the tree tail (4 bytes per lane; offsets clamped into the rows).
@@ -448,28 +545,105 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_kernel(KParams p) {
                          : "v"(qrow), "n"(32 * k16)
                          : "memory");
     }
+    // (2b) RoPE on: the (cos, sin) pairs of the lane's channels i < D/2
+    // (channel i is paired with i + D/2: q granule k16 with k16 + KS/2, same
+    // lane), 8 pairs per granule.
+    const bool rope = p.rope_cs != nullptr;  // uniform
+    float4 csv[RB][KS / 2][4];
+    if (rope) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const float2 *csrow = p.rope_cs + ((int64_t)lo + node[rb]) * (D / 2) + 8 * half;
+#pragma unroll
+            for (int k16 = 0; k16 < KS / 2; ++k16)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    asm volatile("global_load_dwordx4 %0, %1, off offset:%2"
+                                 : "=v"(csv[rb][k16][u])
+                                 : "v"(csrow), "n"(128 * k16 + 16 * u)
+                                 : "memory");
+        }
+    }
+    // (2c) token table: each lane loads the rows of its copies of chunks
+    // 0 .. AH-1 (all of them, chunks past the slice re-reading its last one,
+    // so that they are all in flight at once), and the first period's chunks
+    // AH .. AH+BP-1 come by scalar loads.
+    int32_t prow[PAGED ? AH : 1][PW];
+    if constexpr (PAGED) {
+        const int32_t *tabv = p.table + (int64_t)b * p.tstride + k_lo;
+#pragma unroll
+        for (int ch = 0; ch < AH; ++ch) {
+            const int chc = min(ch, n - 1);
+            const int cap = chc == clamp_c ? last_keys - 1 : kChunk - 1;
+#pragma unroll
+            for (int jj = 0; jj < PW; ++jj)
+                prow[ch][jj] = tabv[chc * kChunk + min(group_key(jj, lrow >> 2) + (lrow & 3), cap)];
+        }
+#pragma unroll
+        for (int cc = 0; cc < BP; ++cc)
+            if (AH + cc < n) load_rows(cc, AH + cc);
+        // One wait for all of them here (the compiler's, for this use), not
+        // one per copy below: a compiler wait between two copies would also
+        // wait for the copies already issued, which it does not count.
+#pragma unroll
+        for (int ch = 0; ch < AH; ++ch)
+#pragma unroll
+            for (int jj = 0; jj < PW; ++jj) asm volatile("" : "+v"(prow[ch][jj]));
+    }
     // (3) the first AH chunks.  While they land, Q is multiplied by
-    // c = scale * log2(e) (scores in log2 units) and rounded to bf16 again;
-    // after the second wait everything but chunks 2 .. AH-1 has landed (the
-    // ancestor rows, Q, chunks 0 and 1).
+    // c = scale * log2(e) (scores in log2 units; rotated first when RoPE is
+    // on) and rounded to bf16 again; after the second wait everything but
+    // chunks 2 .. AH-1 has landed (the ancestor rows, Q, chunks 0 and 1).
 #pragma unroll
-    for (int ch = 0; ch < AH; ++ch)
-        if (ch < n) issue(ch, ch);
-    wait_chunks<PW, AH>(min(n, AH));  // Q and the ancestor rows
-    const float c = p.c;
+    for (int ch = 0; ch < AH; ++ch) {
+        if (ch < n) {
+            if constexpr (PAGED) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int k16 = 0; k16 < KS; ++k16) {
-            asm volatile("" : "+v"(qb[rb][k16]));
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const f32x2_t x = {(float)qb[rb][k16][2 * e2] * c, (float)qb[rb][k16][2 * e2 + 1] * c};
-                const bf16x2_t y = __builtin_convertvector(x, bf16x2_t);
-                qb[rb][k16][2 * e2] = y[0];
-                qb[rb][k16][2 * e2 + 1] = y[1];
+                for (int jj = 0; jj < PW; ++jj) copy_row((uint32_t)ch, jj, prow[ch][jj]);
+            } else {
+                issue(ch, ch);
             }
         }
+    }
+    wait_chunks<PW, AH>(min(n, AH));  // Q, the ancestor rows, the (cos, sin) pairs
+    const float c = p.c;
+    if (rope) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int k16 = 0; k16 < KS / 2; ++k16) {
+                asm volatile("" : "+v"(qb[rb][k16]), "+v"(qb[rb][k16 + KS / 2]));
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const float4 cs4 = csv[rb][k16][e2];  // (cos, sin) of channels 2 e2, 2 e2 + 1
+                    const float a0 = (float)qb[rb][k16][2 * e2], a1 = (float)qb[rb][k16][2 * e2 + 1];
+                    const float b0 = (float)qb[rb][k16 + KS / 2][2 * e2];
+                    const float b1 = (float)qb[rb][k16 + KS / 2][2 * e2 + 1];
+                    const f32x2_t x = {(a0 * cs4.x - b0 * cs4.y) * c, (a1 * cs4.z - b1 * cs4.w) * c};
+                    const f32x2_t y = {(b0 * cs4.x + a0 * cs4.y) * c, (b1 * cs4.z + a1 * cs4.w) * c};
+                    const bf16x2_t xb = __builtin_convertvector(x, bf16x2_t);
+                    const bf16x2_t yb = __builtin_convertvector(y, bf16x2_t);
+                    qb[rb][k16][2 * e2] = xb[0];
+                    qb[rb][k16][2 * e2 + 1] = xb[1];
+                    qb[rb][k16 + KS / 2][2 * e2] = yb[0];
+                    qb[rb][k16 + KS / 2][2 * e2 + 1] = yb[1];
+                }
+            }
+    } else {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int k16 = 0; k16 < KS; ++k16) {
+                asm volatile("" : "+v"(qb[rb][k16]));
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const f32x2_t x = {(float)qb[rb][k16][2 * e2] * c, (float)qb[rb][k16][2 * e2 + 1] * c};
+                    const bf16x2_t y = __builtin_convertvector(x, bf16x2_t);
+                    qb[rb][k16][2 * e2] = y[0];
+                    qb[rb][k16][2 * e2 + 1] = y[1];
+                }
+            }
+    }
     wait_chunks<PW, AH - 2>(min(n, AH) - 2);
     lds_barrier();
 
@@ -479,18 +653,30 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_kernel(KParams p) {
     // the copies of chunks j + AH .. j + AH + BP - 1 start.  Between barriers
     // the waves drift freely, so the two waves of a SIMD fill each other's
     // gaps.
-    auto step_top = [&](int j) {
+    // (Token table: this period's chunks are copied with the rows loaded one
+    // period earlier, then the next period's rows are loaded.)
+    auto step_top = [&](int j) __attribute__((always_inline)) {
         if (j % BP == 0) {
             wait_chunks<PW, AH - 1 - BP>(min(AH - 1 - BP, n - 1 - BP - j));
             lds_barrier();
+            if constexpr (PAGED) {
 #pragma unroll
-            for (int c = j + AH; c < j + AH + BP; ++c)
-                if (c < n) issue(c, (uint32_t)(c % kStages));
+                for (int cc = 0; cc < BP; ++cc)
+                    if (j + AH + cc < n) issue_rows(cc, j + AH + cc);
+#pragma unroll
+                for (int cc = 0; cc < BP; ++cc)
+                    if (j + AH + BP + cc < n) load_rows(cc, j + AH + BP + cc);
+            } else {
+#pragma unroll
+                for (int c = j + AH; c < j + AH + BP; ++c)
+                    if (c < n) issue(c, (uint32_t)(c % kStages));
+            }
         }
     };
     if (!active) {
         // A wave without rows only keeps the copy schedule and the barriers.
         for (int j = 0; j < n; ++j) step_top(j);
+        if (PAGED && slot_bad) report(p.err, TV_DEVERR_BAD_SLOT, b);
         return;
     }
 
@@ -788,6 +974,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_kernel(KParams p) {
     }
 
     // ---- epilogue ----------------------------------------------------------------
+    if (PAGED && slot_bad) report(p.err, TV_DEVERR_BAD_SLOT, b);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const float lr = halves_sum(l_run[rb]);
@@ -1139,12 +1326,17 @@ int attn_mfma_lookahead(const MfmaPlan &plan) {
 }
 
 namespace {
+template <int D, int NW, int RB, bool PAGED>
+void launch_fwd_t(const KParams &p, const MfmaPlan &plan, long grid, hipStream_t stream) {
+    if (attn_mfma_lookahead(plan) == kAheadShort)
+        hipLaunchKernelGGL((attn_fwd_kernel<D, NW, RB, kAheadShort, PAGED>), dim3(grid), dim3(64 * NW), 0, stream, p);
+    else
+        hipLaunchKernelGGL((attn_fwd_kernel<D, NW, RB, kAhead, PAGED>), dim3(grid), dim3(64 * NW), 0, stream, p);
+}
 template <int D, int NW, int RB>
 void launch_fwd(const KParams &p, const MfmaPlan &plan, long grid, hipStream_t stream) {
-    if (attn_mfma_lookahead(plan) == kAheadShort)
-        hipLaunchKernelGGL((attn_fwd_kernel<D, NW, RB, kAheadShort>), dim3(grid), dim3(64 * NW), 0, stream, p);
-    else
-        hipLaunchKernelGGL((attn_fwd_kernel<D, NW, RB, kAhead>), dim3(grid), dim3(64 * NW), 0, stream, p);
+    if (p.table) launch_fwd_t<D, NW, RB, true>(p, plan, grid, stream);
+    else launch_fwd_t<D, NW, RB, false>(p, plan, grid, stream);
 }
 }  // namespace
 
@@ -1173,6 +1365,10 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *works
     p.c = a.scale * kLog2e;
     p.out = (uint16_t *)a.out;
     p.err = a.err;
+    p.table = a.table;
+    p.tstride = a.table_stride;
+    p.kvr32 = (int)(a.kv_rows < INT32_MAX ? a.kv_rows : INT32_MAX);
+    p.rope_cs = a.rope_cs;
     p.ws_o = nullptr;
     p.ws_ml = nullptr;
     p.task_table = nullptr;

@@ -13,6 +13,11 @@
 // 64 probabilities, reading V rows coalesced.  Tree keys j > i are never
 // ancestors of node i (parents precede children), so the key loop stops at
 // P + i + 1.  All arithmetic is fp32; exp is expf.
+//
+// Optional inputs: with a token table the cache row of key position p is
+// req_to_token[b][p] (each lane looks up its own key; the V loop takes key
+// u's row from lane u); with RoPE on, q is rotated as it is staged in LDS,
+// from the per-node (cos, sin) pairs that the RoPE pre-pass stored.
 #include "tv_device.h"
 #include "tv_launch.h"
 
@@ -62,7 +67,8 @@ __global__ void __launch_bounds__(64) attn_valu_kernel(
     const int32_t *__restrict__ cu_nodes, const int32_t *__restrict__ kv_start,
     const int32_t *__restrict__ prefix_len, const uint64_t *__restrict__ anc, int total_nodes,
     int max_nodes, int max_prefix, int64_t kv_rows, int hq, int hkv, float scale, T *__restrict__ out,
-    int32_t *__restrict__ err) {
+    int32_t *__restrict__ err, const int32_t *__restrict__ table, int64_t table_stride,
+    const float2 *__restrict__ rope_cs) {
     constexpr int CPL = D / 64;  // output channels per lane
     __shared__ float qs[D];
     __shared__ float ps[64];
@@ -73,8 +79,9 @@ __global__ void __launch_bounds__(64) attn_valu_kernel(
     int lo;
     const int n = request_nodes(cu_nodes, b, total_nodes, max_nodes, &lo);
     const int P = prefix_len[b];
-    const int64_t ks = kv_start[b];
-    if (n < 0 || P < 0 || P > max_prefix || ks < 0 || ks + P + n > kv_rows) {
+    const int64_t ks = table ? 0 : kv_start[b];
+    const bool rows_bad = table ? ((int64_t)P + n > table_stride) : (ks < 0 || ks + P + n > kv_rows);
+    if (n < 0 || P < 0 || P > max_prefix || rows_bad) {
         if (i == 0 && h == 0 && lane == 0) report(err, TV_DEVERR_BAD_REQUEST, b);
         return;
     }
@@ -85,12 +92,24 @@ __global__ void __launch_bounds__(64) attn_valu_kernel(
     const int64_t t = (int64_t)lo + i;
     const uint64_t *arow = anc + t * words;
 
-    for (int e = lane; e < D; e += 64) qs[e] = Elem<T>::ld(q, (t * hq + h) * D + e);
+    if (rope_cs) {
+        // channel e paired with e + D/2, rotated in fp32 by the node's angle
+        for (int e = lane; e < D / 2; e += 64) {
+            const float x1 = Elem<T>::ld(q, (t * hq + h) * D + e);
+            const float x2 = Elem<T>::ld(q, (t * hq + h) * D + e + D / 2);
+            const float2 cs = rope_cs[t * (D / 2) + e];
+            qs[e] = x1 * cs.x - x2 * cs.y;
+            qs[e + D / 2] = x2 * cs.x + x1 * cs.y;
+        }
+    } else {
+        for (int e = lane; e < D; e += 64) qs[e] = Elem<T>::ld(q, (t * hq + h) * D + e);
+    }
     __syncthreads();
 
     const int64_t kv_stride = (int64_t)hkv * D;  // elements per cache row
-    const T *kbase = k + ks * kv_stride + (int64_t)g * D;
-    const T *vbase = v + ks * kv_stride + (int64_t)g * D;
+    const T *kbase = k + (int64_t)g * D;
+    const T *vbase = v + (int64_t)g * D;
+    const int32_t *trow = table ? table + (int64_t)b * table_stride : nullptr;
     const int nkeys = P + i + 1;
 
     float m = -INFINITY, l = 0.f;
@@ -105,9 +124,18 @@ __global__ void __launch_bounds__(64) attn_valu_kernel(
             const int j = key - P;
             ok = (arow[j >> 6] >> (j & 63)) & 1ull;
         }
+        // cache row of this lane's key (key u's row is read from lane u below)
+        int64_t krow = ks + key;
+        if (trow && key < nkeys) {
+            krow = trow[key];
+            if (krow < 0 || krow >= kv_rows) {
+                report(err, TV_DEVERR_BAD_SLOT, b);
+                krow = 0;
+            }
+        }
         float s = -INFINITY;
         if (ok) {
-            const T *kr = kbase + (int64_t)key * kv_stride;
+            const T *kr = kbase + krow * kv_stride;
             float dot = 0.f;
 #pragma unroll 4
             for (int e = 0; e < D; e += 8) {
@@ -136,7 +164,7 @@ __global__ void __launch_bounds__(64) attn_valu_kernel(
         for (int u = 0; u < cnt; ++u) {
             const float pu = ps[u];
             if (pu == 0.f) continue;  // masked key (uniform branch)
-            const T *vr = vbase + (int64_t)(c0 + u) * kv_stride;
+            const T *vr = vbase + (int64_t)__shfl((long long)krow, u, 64) * kv_stride;
 #pragma unroll
             for (int c = 0; c < CPL; ++c) acc[c] = fmaf(pu, Elem<T>::ld(vr, lane + 64 * c), acc[c]);
         }
@@ -153,7 +181,7 @@ hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((attn_valu_kernel<T, D>), grid, dim3(64), 0, stream, (const T *)a.q,
                        (const T *)a.k, (const T *)a.v, a.cu_nodes, a.kv_start, a.prefix_len, a.anc,
                        a.total_nodes, a.max_nodes, a.max_prefix, a.kv_rows, a.hq, a.hkv, a.scale,
-                       (T *)a.out, a.err);
+                       (T *)a.out, a.err, a.table, a.table_stride, a.rope_cs);
     return hipGetLastError();
 }
 

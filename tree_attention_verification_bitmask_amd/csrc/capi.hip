@@ -82,34 +82,78 @@ tv_status attn_plan_checked(int32_t batch, int32_t total_nodes, int32_t max_node
     return TV_OK;
 }
 
-// Every host check of tree_attn_verify except the workspace's; fills *plan.
+// Host checks of the optional inputs (null: none): reserved fields zero,
+// rope_base 0 or positive and finite, a table with a positive stride.
+bool inputs_ok(const tv_attn_inputs *in) {
+    if (!in) return true;
+    for (int i = 0; i < 5; ++i)
+        if (in->reserved[i] != 0) return false;
+    if (!(in->rope_base >= 0.f) || !(in->rope_base < INFINITY)) return false;
+    return !in->req_to_token || in->table_stride >= 1;
+}
+bool rope_on(const tv_attn_inputs *in) { return in && in->rope_base > 0.f; }
+
+// Workspace of the call: the plan's, then with RoPE on the nodes' (cos, sin)
+// pairs (8 bytes per channel pair) at the next 256-byte boundary.
+size_t attn_ws_bytes(const tv::MfmaPlan &plan, const tv_attn_inputs *in, int32_t total_nodes, int32_t head_dim,
+                     size_t *rope_off) {
+    const size_t ws = plan.use ? plan.ws_bytes : 0;
+    const size_t off = (ws + 255) & ~(size_t)255;
+    if (rope_off) *rope_off = off;
+    if (rope_on(in) && total_nodes > 0) return off + (size_t)total_nodes * (size_t)(head_dim / 2) * 8;
+    return ws;
+}
+
+// Every host check of tree_attn_verify(_ex) except the workspace's; fills *plan.
 tv_status attn_args_checked(const void *q, const void *k_cache, const void *v_cache, const int32_t *cu_nodes,
                             const int32_t *kv_start, const int32_t *prefix_len, const uint64_t *anc_bits,
                             int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_prefix,
                             int64_t kv_rows, int32_t hq, int32_t hkv, int32_t head_dim, float scale, tv_dtype dtype,
-                            const void *out, const tv_attn_plan_override *ov, tv::MfmaPlan *plan) {
+                            const tv_attn_inputs *in, const void *out, const tv_attn_plan_override *ov,
+                            tv::MfmaPlan *plan) {
     tv_status st =
         attn_plan_checked(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype, ov, plan);
     if (st != TV_OK) return st;
     if (kv_rows < 0) return TV_ERR_SHAPE;
     if (!(scale > 0.f) || scale != scale) return TV_ERR_SHAPE;
-    if (!cu_nodes || !kv_start || !prefix_len) return TV_ERR_NULL;
+    if (!inputs_ok(in)) return TV_ERR_SHAPE;
+    const bool paged = in && in->req_to_token;
+    if (!cu_nodes || !prefix_len || (!paged && !kv_start)) return TV_ERR_NULL;
     if (total_nodes > 0 && (!q || !out || !anc_bits)) return TV_ERR_NULL;
+    if (total_nodes > 0 && rope_on(in) && !in->pos_ids) return TV_ERR_NULL;
     if (kv_rows > 0 && (!k_cache || !v_cache)) return TV_ERR_NULL;
+    // a table entry that is out of range is replaced by row 0, which must exist
+    if (paged && total_nodes > 0 && kv_rows < 1) return TV_ERR_SHAPE;
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
-        !aligned(anc_bits, 8))
+        !aligned(anc_bits, 8) || (paged && !aligned(in->req_to_token, 4)))
         return TV_ERR_ALIGN;
     return TV_OK;
 }
 
-// Enqueues the call whose arguments have passed the checks above.
-tv_status attn_launch(const void *q, const void *k_cache, const void *v_cache, const int32_t *cu_nodes,
+// Enqueues the call whose arguments have passed the checks above: with RoPE
+// on, first the pre-pass (the nodes' (cos, sin) into the workspace at
+// rope_off, the tree's K rows rotated in place), then the attention.
+tv_status attn_launch(const void *q, void *k_cache, const void *v_cache, const int32_t *cu_nodes,
                       const int32_t *kv_start, const int32_t *prefix_len, const uint64_t *anc_bits, int32_t batch,
                       int32_t total_nodes, int32_t max_nodes, int32_t max_prefix, int64_t kv_rows, int32_t hq,
-                      int32_t hkv, int32_t head_dim, float scale, tv_dtype dtype, void *out, void *workspace,
-                      int32_t *err, const tv::MfmaPlan &plan, void *stream) {
+                      int32_t hkv, int32_t head_dim, float scale, tv_dtype dtype, const tv_attn_inputs *in,
+                      void *out, void *workspace, size_t rope_off, int32_t *err, const tv::MfmaPlan &plan,
+                      void *stream) {
     if (batch == 0 || total_nodes == 0) return TV_OK;
     tv::AttnArgs a;
+    if (in && in->req_to_token) {
+        a.table = in->req_to_token;
+        a.table_stride = in->table_stride;
+    }
+    if (rope_on(in)) {
+        float2 *cs = (float2 *)((char *)workspace + rope_off);
+        const hipError_t e =
+            tv::launch_rope_prep(k_cache, in->pos_ids, cu_nodes, kv_start, prefix_len, a.table, a.table_stride,
+                                 batch, total_nodes, kv_rows, hkv, head_dim, in->rope_base, dtype, cs, err,
+                                 (hipStream_t)stream);
+        if (e != hipSuccess) return TV_ERR_LAUNCH;
+        a.rope_cs = cs;
+    }
     a.q = q;
     a.k = k_cache;
     a.v = v_cache;
@@ -203,20 +247,21 @@ tv_status tree_mask_build(const int32_t *parent, const int32_t *cu_nodes, const 
 
 size_t tree_attn_verify_workspace_size_ex(int32_t batch, int32_t total_nodes, int32_t max_nodes,
                                           int32_t max_prefix, int32_t hq, int32_t hkv, int32_t head_dim,
-                                          tv_dtype dtype, const tv_attn_plan_override *ov) {
+                                          tv_dtype dtype, const tv_attn_inputs *in,
+                                          const tv_attn_plan_override *ov) {
     if (check_attn_sizes(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype) != TV_OK)
         return 0;
-    if (!override_ok(ov)) return 0;
+    if (!override_ok(ov) || !inputs_ok(in)) return 0;
     const tv::MfmaPlan plan =
         tv::plan_attn_mfma(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype, ov);
-    return plan.use ? plan.ws_bytes : 0;
+    return attn_ws_bytes(plan, in, total_nodes, head_dim, nullptr);
 }
 
 size_t tree_attn_verify_workspace_size(int32_t batch, int32_t total_nodes, int32_t max_nodes,
                                        int32_t max_prefix, int32_t hq, int32_t hkv, int32_t head_dim,
                                        tv_dtype dtype) {
     return tree_attn_verify_workspace_size_ex(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim,
-                                              dtype, nullptr);
+                                              dtype, nullptr, nullptr);
 }
 
 tv_status tree_attn_verify_plan(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_prefix,
@@ -238,24 +283,27 @@ tv_status tree_attn_verify_plan(int32_t batch, int32_t total_nodes, int32_t max_
     return TV_OK;
 }
 
-tv_status tree_attn_verify_ex(const void *q, const void *k_cache, const void *v_cache,
-                              const int32_t *cu_nodes, const int32_t *kv_start, const int32_t *prefix_len,
-                              const uint64_t *anc_bits, int32_t batch, int32_t total_nodes,
-                              int32_t max_nodes, int32_t max_prefix, int64_t kv_rows, int32_t hq,
-                              int32_t hkv, int32_t head_dim, float scale, tv_dtype dtype, void *out,
-                              void *workspace, size_t workspace_bytes, int32_t *err,
-                              const tv_attn_plan_override *ov, void *stream) {
+tv_status tree_attn_verify_ex(const void *q, void *k_cache, const void *v_cache, const int32_t *cu_nodes,
+                              const int32_t *kv_start, const int32_t *prefix_len, const uint64_t *anc_bits,
+                              int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_prefix,
+                              int64_t kv_rows, int32_t hq, int32_t hkv, int32_t head_dim, float scale,
+                              tv_dtype dtype, const tv_attn_inputs *in, void *out, void *workspace,
+                              size_t workspace_bytes, int32_t *err, const tv_attn_plan_override *ov,
+                              void *stream) {
     tv::MfmaPlan plan;
     const tv_status st = attn_args_checked(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc_bits, batch,
                                            total_nodes, max_nodes, max_prefix, kv_rows, hq, hkv, head_dim, scale,
-                                           dtype, out, ov, &plan);
+                                           dtype, in, out, ov, &plan);
     if (st != TV_OK) return st;
-    if (plan.use && plan.ws_bytes > 0) {
-        if (!workspace || workspace_bytes < plan.ws_bytes) return TV_ERR_WORKSPACE;
+    size_t rope_off = 0;
+    const size_t need = attn_ws_bytes(plan, in, total_nodes, head_dim, &rope_off);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return TV_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return TV_ERR_ALIGN;
     }
     return attn_launch(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc_bits, batch, total_nodes, max_nodes,
-                       max_prefix, kv_rows, hq, hkv, head_dim, scale, dtype, out, workspace, err, plan, stream);
+                       max_prefix, kv_rows, hq, hkv, head_dim, scale, dtype, in, out, workspace, rope_off, err,
+                       plan, stream);
 }
 
 tv_status tree_attn_verify_noalloc(const void *q, const void *k_cache, const void *v_cache,
@@ -269,7 +317,7 @@ tv_status tree_attn_verify_noalloc(const void *q, const void *k_cache, const voi
     tv::MfmaPlan plan;
     const tv_status st = attn_args_checked(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc_bits, batch,
                                            total_nodes, max_nodes, max_prefix, kv_rows, hq, hkv, head_dim, scale,
-                                           dtype, out, nullptr, &plan);
+                                           dtype, nullptr, out, nullptr, &plan);
     if (st != TV_OK) return st;
     if (plan.use && plan.ws_bytes > (size_t)TV_NOALLOC_SCRATCH_BYTES) return TV_ERR_SCRATCH;
     if (batch == 0 || total_nodes == 0) return TV_OK;
@@ -277,8 +325,9 @@ tv_status tree_attn_verify_noalloc(const void *q, const void *k_cache, const voi
     // needs a workspace at all.
     void *ws = nullptr;
     if (plan.use && plan.ws_bytes > 0 && scratch_address(&ws) != hipSuccess) return TV_ERR_LAUNCH;
-    return attn_launch(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc_bits, batch, total_nodes, max_nodes,
-                       max_prefix, kv_rows, hq, hkv, head_dim, scale, dtype, out, ws, err, plan, stream);
+    return attn_launch(q, const_cast<void *>(k_cache), v_cache, cu_nodes, kv_start, prefix_len, anc_bits, batch,
+                       total_nodes, max_nodes, max_prefix, kv_rows, hq, hkv, head_dim, scale, dtype, nullptr, out, ws,
+                       0, err, plan, stream);
 }
 
 tv_status tree_attn_verify(const void *q, const void *k_cache, const void *v_cache,
@@ -287,9 +336,10 @@ tv_status tree_attn_verify(const void *q, const void *k_cache, const void *v_cac
                            int32_t max_nodes, int32_t max_prefix, int64_t kv_rows, int32_t hq,
                            int32_t hkv, int32_t head_dim, float scale, tv_dtype dtype, void *out,
                            void *workspace, size_t workspace_bytes, int32_t *err, void *stream) {
-    return tree_attn_verify_ex(q, k_cache, v_cache, cu_nodes, kv_start, prefix_len, anc_bits, batch,
-                               total_nodes, max_nodes, max_prefix, kv_rows, hq, hkv, head_dim, scale, dtype,
-                               out, workspace, workspace_bytes, err, nullptr, stream);
+    // (no optional inputs: k_cache is only read)
+    return tree_attn_verify_ex(q, const_cast<void *>(k_cache), v_cache, cu_nodes, kv_start, prefix_len, anc_bits,
+                               batch, total_nodes, max_nodes, max_prefix, kv_rows, hq, hkv, head_dim, scale, dtype,
+                               nullptr, out, workspace, workspace_bytes, err, nullptr, stream);
 }
 
 tv_status tree_accept_greedy(const int32_t *parent, const int32_t *draft_tokens,

@@ -13,6 +13,13 @@
 // read and one write of every rotated element.  A K row finds its request by
 // a binary search over cu_nodes.
 //
+// rope_prep_kernel (RoPE inside tree_attn_verify_ex): one thread per (node,
+// channel pair) takes the same angle, sine and cosine in double, stores the
+// pair as fp32 (the attention kernel rotates q with it as q is loaded) and
+// rotates the node's K row of every KV head in place exactly as rope_kernel
+// does, so the cache ends up bit for bit as after tree_rope_apply.  The K row
+// is found from kv_start or through the token table.
+//
 // kv_rollback_token_table: one wavefront per request.  Lane j < L writes
 // position P + j of the request's token table; the unaccepted nodes' slots are
 // compacted in node order with one ballot per 64 nodes.
@@ -88,6 +95,55 @@ __global__ void __launch_bounds__(kRopeThreads) rope_kernel(
     store_el<T>(base + i + h, bb * c + a * s);
 }
 
+template <typename T>
+__global__ void __launch_bounds__(kRopeThreads) rope_prep_kernel(
+    T *__restrict__ k, const int32_t *__restrict__ pos, const int32_t *__restrict__ cu_nodes,
+    const int32_t *__restrict__ kv_start, const int32_t *__restrict__ prefix_len, const int32_t *__restrict__ table,
+    int64_t table_stride, int batch, int total_nodes, int64_t kv_rows, int hkv, int d, double log2_base,
+    float2 *__restrict__ cs, int32_t *__restrict__ err) {
+    const int h = d / 2;
+    const int64_t w = (int64_t)blockIdx.x * kRopeThreads + threadIdx.x;
+    if (w >= (int64_t)total_nodes * h) return;
+    const int t = (int)(w / h);
+    const int i = (int)(w - (int64_t)t * h);
+    const double inv = exp2(-2.0 * i / d * log2_base);
+    const double ang = (double)pos[t] * inv;
+    double s, c;
+    sincos(ang, &s, &c);
+    cs[w] = make_float2((float)c, (float)s);
+    const int b = request_of(cu_nodes, batch, t);
+    if (b < 0) {
+        report(err, TV_DEVERR_BAD_REQUEST, 0);
+        return;
+    }
+    const int j = t - cu_nodes[b];
+    const int P = prefix_len[b];
+    int64_t crow;
+    if (table) {
+        if (P < 0 || (int64_t)P + (cu_nodes[b + 1] - cu_nodes[b]) > table_stride) {
+            report(err, TV_DEVERR_BAD_REQUEST, b);
+            return;
+        }
+        crow = table[(int64_t)b * table_stride + P + j];
+        if (crow < 0 || crow >= kv_rows) {
+            report(err, TV_DEVERR_BAD_SLOT, b);
+            return;
+        }
+    } else {
+        crow = (int64_t)kv_start[b] + P + j;
+        if (crow < 0 || crow >= kv_rows || kv_start[b] < 0 || P < 0) {
+            report(err, TV_DEVERR_BAD_REQUEST, b);
+            return;
+        }
+    }
+    for (int g = 0; g < hkv; ++g) {
+        T *base = k + (crow * hkv + g) * d;
+        const double a = load_el<T>(base + i), bb = load_el<T>(base + i + h);
+        store_el<T>(base + i, a * c - bb * s);
+        store_el<T>(base + i + h, bb * c + a * s);
+    }
+}
+
 __global__ void __launch_bounds__(64) rollback_kernel(
     int32_t *__restrict__ table, int64_t stride, const int32_t *__restrict__ tree_slots,
     const int32_t *__restrict__ cu_nodes, const int32_t *__restrict__ prefix_len,
@@ -149,6 +205,25 @@ hipError_t launch_tree_rope(void *q, void *k, const int32_t *pos, const int32_t 
         hipLaunchKernelGGL(rope_kernel<float>, dim3((unsigned)blocks), dim3(kRopeThreads), 0, stream, (float *)q,
                            (float *)k, pos, cu_nodes, kv_start, prefix_len, batch, total_nodes, kv_rows, hq, hkv,
                            head_dim, lb, err);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_prep(void *k, const int32_t *pos, const int32_t *cu_nodes, const int32_t *kv_start,
+                            const int32_t *prefix_len, const int32_t *table, int64_t table_stride, int batch,
+                            int total_nodes, int64_t kv_rows, int hkv, int head_dim, float base, tv_dtype dtype,
+                            float2 *cs, int32_t *err, hipStream_t stream) {
+    if (batch == 0 || total_nodes == 0) return hipSuccess;
+    const int64_t items = (int64_t)total_nodes * (head_dim / 2);
+    const int64_t blocks = (items + kRopeThreads - 1) / kRopeThreads;
+    const double lb = log2((double)base);
+    if (dtype == TV_BF16)
+        hipLaunchKernelGGL(rope_prep_kernel<uint16_t>, dim3((unsigned)blocks), dim3(kRopeThreads), 0, stream,
+                           (uint16_t *)k, pos, cu_nodes, kv_start, prefix_len, table, table_stride, batch,
+                           total_nodes, kv_rows, hkv, head_dim, lb, cs, err);
+    else
+        hipLaunchKernelGGL(rope_prep_kernel<float>, dim3((unsigned)blocks), dim3(kRopeThreads), 0, stream,
+                           (float *)k, pos, cu_nodes, kv_start, prefix_len, table, table_stride, batch,
+                           total_nodes, kv_rows, hkv, head_dim, lb, cs, err);
     return hipGetLastError();
 }
 

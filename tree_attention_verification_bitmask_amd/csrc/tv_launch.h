@@ -43,6 +43,13 @@ int64_t target_sample_blocks(int rows, int vocab);
 hipError_t launch_target_sample(const void *logits, int rows, int vocab, tv_dtype dtype, double inv_t,
                                 const double *u, int32_t *token, void *workspace, hipStream_t stream);
 
+// The tree part of RoPE inside tree_attn_verify: (cos, sin) of every node's
+// angles into cs [T, d/2] (float2) and the tree's K rows rotated in place
+// (contiguous rows from kv_start, or through the token table when non-null).
+hipError_t launch_rope_prep(void *k, const int32_t *pos, const int32_t *cu_nodes, const int32_t *kv_start,
+                            const int32_t *prefix_len, const int32_t *table, int64_t table_stride, int batch,
+                            int total_nodes, int64_t kv_rows, int hkv, int head_dim, float base, tv_dtype dtype,
+                            float2 *cs, int32_t *err, hipStream_t stream);
 hipError_t launch_tree_rope(void *q, void *k, const int32_t *pos, const int32_t *cu_nodes, const int32_t *kv_start,
                             const int32_t *prefix_len, int batch, int total_nodes, int64_t kv_rows, int hq, int hkv,
                             int head_dim, float base, tv_dtype dtype, int32_t *err, hipStream_t stream);
@@ -76,6 +83,11 @@ struct AttnArgs {
     tv_dtype dtype;
     void *out;
     int32_t *err;
+    // optional inputs: K/V rows through a token table (null: kv_start + p),
+    // and each node's (cos, sin) per channel pair for rotating q (null: off)
+    const int32_t *table = nullptr;
+    int64_t table_stride = 0;
+    const float2 *rope_cs = nullptr;
 };
 
 // Generic VALU path: one wavefront per (node, query head); fp32 or bf16.
