@@ -385,6 +385,92 @@ def tree_rope(q, k, pos, cu_nodes, kv_start, prefix_len, base: float):
 
 
 # ---------------------------------------------------------------------------
+# Stochastic acceptance ([TSD] "Verification and Acceptance Algorithms",
+# section "Exact Sampling Equivalence": a candidate x proposed with draft
+# probability q(x) is accepted with probability min(1, p(x)/q(x)); after a
+# rejection a replacement is drawn from (p - q)+ normalised)
+# ---------------------------------------------------------------------------
+
+def _softmax64(logits_row, temperature: float) -> np.ndarray:
+    """softmax(x / T) in float64: y = x * (1/T), w = exp(y - max y), w / sum w."""
+    y = np.asarray(logits_row, dtype=np.float64) * (1.0 / float(temperature))
+    w = np.exp(y - y.max())
+    return w / w.sum()
+
+
+def _draw(weights, u: float) -> int:
+    """Inverse transform over unnormalised weights (index order): the smallest
+    i whose cumulative weight exceeds u * total; if rounding leaves none, the
+    last index with positive weight."""
+    c = np.cumsum(np.asarray(weights, dtype=np.float64))
+    i = int(np.searchsorted(c, float(u) * c[-1], side="right"))
+    return i if i < len(c) else int(np.flatnonzero(np.asarray(weights) > 0)[-1])
+
+
+def accept_stochastic_one(parent, draft, root_logits, node_logits, temperature: float, root_q, node_q,
+                          u_accept, u_final: float, max_depth: int):
+    """The stochastic walk for one request (float64 throughout).
+
+    At the current node v (first the implicit root) the target distribution
+    is p = softmax(logits_v / T) and the drafter's is q_v (the distribution
+    v's children were drawn from).  The children are tried in ascending index
+    with r = p: child c with token x is accepted iff u_accept[c] < min(1,
+    r(x) / q_v(x)) (a token with q_v(x) = 0 is accepted iff r(x) > 0); after a
+    rejection r becomes (r - q_v)+ / sum (r - q_v)+ (if that sum is 0, r is
+    kept).  An accepted child becomes the current node (the walk stops after
+    max_depth accepted nodes); when no child is accepted, or v has none, the
+    next token is drawn from r with u_final by inverse transform.  Children
+    with a negative draft token (dead leaves) are skipped.
+    Returns (path node indices, next token)."""
+    n = len(parent)
+    cur = -1
+    path = []
+    while True:
+        p = _softmax64(root_logits if cur < 0 else node_logits[cur], temperature)
+        q = np.asarray(root_q if cur < 0 else node_q[cur], dtype=np.float64)
+        r = p
+        kids = [j for j in range(n) if int(parent[j]) == cur] if len(path) < max_depth else []
+        accepted = None
+        for c in kids:                      # ascending index
+            x = int(draft[c])
+            if x < 0:
+                continue
+            a = min(1.0, r[x] / q[x]) if q[x] > 0 else (1.0 if r[x] > 0 else 0.0)
+            if float(u_accept[c]) < a:
+                accepted = c
+                break
+            res = np.maximum(r - q, 0.0)
+            tot = res.sum()
+            if tot > 0:
+                r = res / tot
+        if accepted is None:
+            return path, _draw(r, u_final)
+        path.append(accepted)
+        cur = accepted
+
+
+def accept_stochastic(parent, draft, cu_nodes, root_logits, node_logits, temperature: float, root_q, node_q,
+                      u_accept, u_final, max_depth: int):
+    """accept_stochastic_one per request; node arrays are global [T, ...],
+    parents request-local.  Returns (accept_len [B], accept_idx [B, max_depth]
+    (-1 padded), next_token [B])."""
+    cu = np.asarray(cu_nodes)
+    B = cu.shape[0] - 1
+    alen = np.zeros(B, np.int32)
+    aidx = np.full((B, max_depth), -1, np.int32)
+    nxt = np.zeros(B, np.int32)
+    for b in range(B):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        path, t = accept_stochastic_one(parent[lo:hi], draft[lo:hi], root_logits[b], node_logits[lo:hi],
+                                        temperature, root_q[b], node_q[lo:hi], u_accept[lo:hi],
+                                        float(u_final[b]), max_depth)
+        alen[b] = len(path)
+        aidx[b, :len(path)] = path
+        nxt[b] = t
+    return alen, aidx, nxt
+
+
+# ---------------------------------------------------------------------------
 # O-rollback by token table ([TSD] "KV Cache Rollback": unaccepted nodes are
 # discarded by "page table updates" in paged caches)
 # ---------------------------------------------------------------------------

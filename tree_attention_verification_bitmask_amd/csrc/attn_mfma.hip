@@ -1183,29 +1183,56 @@ __device__ __forceinline__ int tile_chunks(const KParams &p, const Req &rq, int 
     return (k_hi - k_lo + kChunk - 1) / kChunk;
 }
 
-// Group q = (b * hkv + g) * splits + s: its longest tile's chunk count.
-__device__ __forceinline__ int group_chunks(const KParams &p, int q) {
-    const int s = q % p.splits;
-    const int b = q / p.splits / p.hkv;
-    const Req rq = load_request(p, b);
+// Chunk count of group (s, request sizes rq): its longest tile's.
+__device__ __forceinline__ int group_chunks_of(const KParams &p, const Req &rq, int s) {
     int len = 0;
     for (int rt = 0; rt < p.row_tiles; ++rt) len = max(len, tile_chunks(p, rq, s, rt));
     return len;
 }
 
+// One workgroup.  Each thread takes groups tid, tid + kPlanThreads, ...; the
+// first kPlanCache of them keep their request sizes and lengths in registers
+// from the one round of loads at the start (so the second pass below loads
+// nothing), and the group (b, g = 0, s = 0) reports a bad request b.
+constexpr int kPlanCache = 4;
 __global__ void __launch_bounds__(kPlanThreads) attn_plan_kernel(KParams p, int ngroups, int nslots,
                                                                   int32_t *__restrict__ table) {
     __shared__ int cnt[kPlanBins];
     __shared__ int wsum[kPlanThreads / 64];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int R = p.row_tiles;
+    Req creq[kPlanCache];
+    int clen[kPlanCache];
+#pragma unroll
+    for (int c = 0; c < kPlanCache; ++c) {
+        const int q = tid + c * kPlanThreads;
+        clen[c] = 0;
+        if (q < ngroups) creq[c] = load_request(p, q / p.splits / p.hkv);
+    }
     for (int i = tid; i < kPlanBins; i += kPlanThreads) cnt[i] = 0;
-    for (int b = tid; b < p.batch; b += kPlanThreads)
-        if (!load_request(p, b).ok) report(p.err, TV_DEVERR_BAD_REQUEST, b);
     for (int i = tid; i < nslots; i += kPlanThreads) table[i] = -1;
     __syncthreads();
-    for (int q = tid; q < ngroups; q += kPlanThreads) {
-        const int len = group_chunks(p, q);
+#pragma unroll
+    for (int c = 0; c < kPlanCache; ++c) {
+        const int q = tid + c * kPlanThreads;
+        if (q < ngroups) {
+            const int s = q % p.splits, g = (q / p.splits) % p.hkv;
+            if (!creq[c].ok) {
+                if (s == 0 && g == 0) report(p.err, TV_DEVERR_BAD_REQUEST, q / p.splits / p.hkv);
+            } else {
+                clen[c] = group_chunks_of(p, creq[c], s);
+                if (clen[c] > 0) atomicAdd(&cnt[clen[c]], 1);
+            }
+        }
+    }
+    for (int q = tid + kPlanCache * kPlanThreads; q < ngroups; q += kPlanThreads) {
+        const int s = q % p.splits, g = (q / p.splits) % p.hkv;
+        const Req rq = load_request(p, q / p.splits / p.hkv);
+        if (!rq.ok) {
+            if (s == 0 && g == 0) report(p.err, TV_DEVERR_BAD_REQUEST, q / p.splits / p.hkv);
+            continue;
+        }
+        const int len = group_chunks_of(p, rq, s);
         if (len > 0) atomicAdd(&cnt[len], 1);
     }
     __syncthreads();
@@ -1237,13 +1264,10 @@ __global__ void __launch_bounds__(kPlanThreads) attn_plan_kernel(KParams p, int 
         run += v[e];
     }
     __syncthreads();
-    for (int q = tid; q < ngroups; q += kPlanThreads) {
-        const int len = group_chunks(p, q);
-        if (len <= 0) continue;
+    // Group q of length len > 0 with request sizes rq -> its tiles' slots.
+    auto place = [&](int q, int len, const Req &rq) {
         const int k = atomicAdd(&cnt[len], 1);  // rank of the group, longest first
         const int s = q % p.splits;
-        const int b = q / p.splits / p.hkv;
-        const Req rq = load_request(p, b);
         const int m = k / kXcds;  // the group's rank on its XCD
         const int base = m * kXcds * R + k % kXcds;
         // tile rt goes to slot i of the group, rotated by the slot's row of 4
@@ -1254,6 +1278,17 @@ __global__ void __launch_bounds__(kPlanThreads) attn_plan_kernel(KParams p, int 
             const int i = ((rt - rot) % R + R) % R;
             if (tile_chunks(p, rq, s, rt) > 0) table[base + kXcds * i] = q * R + rt;
         }
+    };
+#pragma unroll
+    for (int c = 0; c < kPlanCache; ++c) {
+        const int q = tid + c * kPlanThreads;
+        if (q < ngroups && clen[c] > 0) place(q, clen[c], creq[c]);
+    }
+    for (int q = tid + kPlanCache * kPlanThreads; q < ngroups; q += kPlanThreads) {
+        const Req rq = load_request(p, q / p.splits / p.hkv);
+        if (!rq.ok) continue;
+        const int len = group_chunks_of(p, rq, q % p.splits);
+        if (len > 0) place(q, len, rq);
     }
 }
 
