@@ -85,6 +85,7 @@ typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
 #define TV_DEVERR_BAD_LEDGER 5  /* chosen slot whose parent is unusable; index = b       */
 #define TV_DEVERR_LIMIT 6       /* a request above a per-request limit; index = b        */
 #define TV_DEVERR_BAD_SLOT 7    /* token-table entry outside [0, kv_rows); index = b     */
+#define TV_DEVERR_BAD_TOKEN 8   /* draft token >= vocab; index = global node             */
 
 /* Human-readable name of a tv_status value (static string). */
 const char *tv_status_string(int status);
@@ -312,6 +313,55 @@ tv_status tree_accept_greedy(const int32_t *parent, const int32_t *draft_tokens,
                              const int32_t *cu_nodes, int32_t batch, int32_t total_nodes,
                              int32_t max_depth, int32_t *accept_len, int32_t *accept_idx,
                              int32_t *next_token, int32_t *err, void *stream);
+
+/*
+ * tree_accept_stochastic -- the accepted path and next token at temperature
+ * T > 0 when the draft is stochastic.
+ *
+ * Defines: [TSD] "Verification and Acceptance Algorithms", section "Exact
+ * Sampling Equivalence": a candidate x that the drafter proposed with
+ * probability q(x) is accepted with probability min(1, p(x) / q(x)); after a
+ * rejection the replacement comes from (p - q)+ normalised, so that the
+ * emitted tokens follow the target's distribution exactly.
+ * Reading (the pages do not spell out several candidates at one node): at
+ * the current node v (first the implicit root) p = softmax(logits_v / T) and
+ * q_v is the distribution v's children were drawn from.  The children are
+ * tried in ascending index against the residual r (r = p at first): child c
+ * with token x is accepted iff u_accept[c] < min(1, r(x) / q_v(x)) (if
+ * q_v(x) = 0: iff r(x) > 0); a rejection replaces r by (r - q_v)+ / its sum
+ * (kept if that sum is 0).  An accepted child becomes the current node; the
+ * walk ends when no child is accepted, v has none, or max_depth nodes are
+ * accepted, and the next token is drawn from r by inverse transform with
+ * u_final[b] (the smallest index whose cumulative weight exceeds u times the
+ * total; if rounding leaves none, the last index with positive weight).
+ * Children with a negative draft token (dead leaves) are skipped.  Float64
+ * throughout; only the order of additions differs from a sequential sum.
+ *
+ * In:  parent, draft_tokens [T] (request-local parents, as tree_mask_build);
+ *      cu_nodes [B+1]; root_logits [B, vocab] and node_logits [T, vocab]
+ *      (fp32 or bf16: row b is the target at request b's root, row t at node
+ *      t; each row needs a finite maximum); root_q [B, vocab], node_q
+ *      [T, vocab] fp32 draft probabilities at the same places; u_accept [T],
+ *      u_final [B] float64 uniforms in [0, 1) (the call is deterministic in
+ *      them).  0 < temperature < inf; 1 <= vocab <= TV_MAX_VOCAB;
+ *      1 <= max_depth <= TV_MAX_DEPTH; N_b <= TV_MAX_NODES.  u arrays 8-byte
+ *      aligned, the rest naturally aligned.
+ * Out: accept_len [B], accept_idx [B, max_depth] (request-local, -1 padded),
+ *      next_token [B], as tree_accept_greedy.
+ * Workspace: tree_accept_stochastic_workspace_size(batch, total_nodes, vocab)
+ *      bytes (16 per row of logits plus 8 per logit of each request's
+ *      residual), 256-byte aligned; no contents required.
+ * err: BAD_REQUEST (cu_nodes outside [0, T], decreasing, or N_b above
+ *      TV_MAX_NODES), BAD_PARENT, BAD_TOKEN (a draft token >= vocab); such a
+ *      request gets accept_len 0, no path and next_token -1.
+ */
+size_t tree_accept_stochastic_workspace_size(int32_t batch, int32_t total_nodes, int32_t vocab);
+tv_status tree_accept_stochastic(const int32_t *parent, const int32_t *draft_tokens, const int32_t *cu_nodes,
+                                 int32_t batch, int32_t total_nodes, int32_t max_depth, const void *root_logits,
+                                 const void *node_logits, tv_dtype dtype, float temperature, const float *root_q,
+                                 const float *node_q, int32_t vocab, const double *u_accept, const double *u_final,
+                                 int32_t *accept_len, int32_t *accept_idx, int32_t *next_token, void *workspace,
+                                 size_t workspace_bytes, int32_t *err, void *stream);
 
 /*
  * kv_compact_path -- commit the accepted path's K/V, discard the rest.

@@ -411,3 +411,35 @@ def test_gdn_host_checks(L):
     assert com(D=65) == LIMIT
     assert com(cs=FAKE_ODD) == ALIGN
     assert com(B=0) == OK
+
+
+def test_accept_stochastic_host_checks(L):
+    B, T, V = 2, 10, 1000
+    need = L.tree_accept_stochastic_workspace_size(B, T, V)
+    assert need == ((12 * 16 + 255) // 256) * 256 + B * V * 8   # row stats, then one residual per request
+    assert L.tree_accept_stochastic_workspace_size(-1, T, V) == 0
+    assert L.tree_accept_stochastic_workspace_size(B, T, 0) == 0
+
+    def st(parent=FAKE, draft=FAKE, cu=FAKE, B=B, T=T, D=8, rl=FAKE, nl=FAKE, dt=0, temp=1.0, rq=FAKE, nq=FAKE,
+           V=V, ua=FAKE, uf=FAKE, alen=FAKE, aidx=FAKE, nxt=FAKE, ws=FAKE, wsb=need):
+        return L.tree_accept_stochastic(parent, draft, cu, B, T, D, rl, nl, dt, temp, rq, nq, V, ua, uf, alen, aidx,
+                                        nxt, ws, wsb, None, None)
+    assert st(B=-1) == SHAPE
+    assert st(D=0) == SHAPE
+    assert st(V=0) == SHAPE
+    for bad_t in (0.0, -1.0, float("inf"), float("nan")):
+        assert st(temp=bad_t) == SHAPE
+    assert st(D=65) == LIMIT
+    assert st(V=16777217) == LIMIT
+    assert st(dt=4) == DTYPE
+    assert st(rq=None) == NULL
+    assert st(uf=None) == NULL
+    assert st(nxt=None) == NULL
+    assert st(nl=None) == NULL
+    assert st(ua=None) == NULL
+    assert st(ua=FAKE_ODD) == ALIGN                         # float64 uniforms
+    assert st(rl=C.c_void_p(0x10002)) == ALIGN              # fp32 logits
+    assert st(ws=None) == WS
+    assert st(wsb=need - 1) == WS
+    assert st(ws=C.c_void_p(0x10080)) == ALIGN
+    assert st(B=0, T=0, ws=None, wsb=0) == OK

@@ -1,0 +1,169 @@
+"""tree_accept_stochastic on the GPU against the oracle, through the C ABI.
+
+The accepted path, its length and the next token are integers decided in
+float64 on both sides (only the order of additions differs), so they must
+match the oracle exactly.  Inputs: random forests, each node's children drawn
+from that node's draft distribution (so acceptances and rejections both
+occur), independent target logits, seeded uniforms; vocabularies from 40 (many
+rejections per node) to 151936 (the Qwen3 vocabulary); fp32 and bf16 logits.
+Also: a point-mass target gives tree_accept_greedy's walk, max_depth cuts the
+walk, and bad parents, tokens and request ranges are reported per request.
+"""
+import numpy as np
+import pytest
+
+from oracle import tree_verify_oracle as O
+from tests.gpu_util import announce
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tree_attention_verification_bitmask_amd import binding
+    binding.lib()   # raises if the HIP library is missing: no fallback
+    return binding
+
+
+def B():
+    from tree_attention_verification_bitmask_amd import binding
+    return binding
+
+
+def _round_bf16(x):
+    f = np.asarray(x, np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    return (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32).view(np.float32)
+
+
+def make_case(seed, batch, nodes, V, dead=0.05, spread=3.0, q_noise=1.0, logit_dtype="f32"):
+    """Random forests; each node's children drawn from its q; target logits
+    independent of q."""
+    rng = np.random.default_rng(seed)
+    sizes = rng.integers(nodes[0], nodes[1] + 1, batch)
+    cu = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    T = int(cu[-1])
+    parent = np.empty(T, np.int32)
+    for b in range(batch):
+        lo = int(cu[b])
+        for i in range(int(sizes[b])):
+            parent[lo + i] = -1 if i == 0 else int(rng.integers(-1, i))
+    root_logits = rng.normal(0, spread, (batch, V)).astype(np.float32)
+    node_logits = rng.normal(0, spread, (T, V)).astype(np.float32)
+    if logit_dtype == "bf16":
+        root_logits, node_logits = _round_bf16(root_logits), _round_bf16(node_logits)
+    # draft distributions: the target's logits plus noise (a drafter that
+    # roughly agrees with the target), so candidates are often but not always
+    # accepted
+    def qdist(logits):
+        z = logits.astype(np.float64) + rng.normal(0, q_noise, logits.shape)
+        z = np.exp(z - z.max(axis=1, keepdims=True))
+        return (z / z.sum(axis=1, keepdims=True)).astype(np.float32)
+    root_q, node_q = qdist(root_logits), qdist(node_logits)
+    draft = np.empty(T, np.int32)
+    for b in range(batch):
+        lo = int(cu[b])
+        for i in range(int(sizes[b])):
+            p = int(parent[lo + i])
+            q = root_q[b] if p < 0 else node_q[lo + p]
+            q64 = q.astype(np.float64)
+            draft[lo + i] = int(rng.choice(V, p=q64 / q64.sum()))
+    draft[rng.random(T) < dead] = -1
+    u_accept = rng.random(T)
+    u_final = rng.random(batch)
+    return dict(parent=parent, draft=draft, cu=cu, root_logits=root_logits, node_logits=node_logits,
+                root_q=root_q, node_q=node_q, u_accept=u_accept, u_final=u_final)
+
+
+def run_gpu(c, temperature, max_depth, logit_dtype="f32"):
+    i32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.int32)).cuda()
+    f64 = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float64)).cuda()
+    ldt = torch.bfloat16 if logit_dtype == "bf16" else torch.float32
+    lg = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda().to(ldt).contiguous()
+    f32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
+    alen, aidx, nxt, err = B().tree_accept_stochastic(
+        i32(c["parent"]), i32(c["draft"]), i32(c["cu"]), lg(c["root_logits"]), lg(c["node_logits"]), temperature,
+        f32(c["root_q"]), f32(c["node_q"]), f64(c["u_accept"]), f64(c["u_final"]), max_depth)
+    torch.cuda.synchronize()
+    return alen.cpu().numpy(), aidx.cpu().numpy(), nxt.cpu().numpy(), int(err.item())
+
+
+def run_oracle(c, temperature, max_depth):
+    return O.accept_stochastic(c["parent"], c["draft"], c["cu"], c["root_logits"].astype(np.float64),
+                               c["node_logits"].astype(np.float64), temperature, c["root_q"].astype(np.float64),
+                               c["node_q"].astype(np.float64), c["u_accept"], c["u_final"], max_depth)
+
+
+CASES = [  # seed, batch, nodes, vocab, temperature, max_depth, logits
+    (0, 8, (10, 40), 40, 1.0, 16, "f32"),
+    (1, 16, (1, 64), 257, 0.7, 8, "f32"),
+    (2, 4, (50, 128), 4096, 1.3, 16, "f32"),
+    (3, 8, (30, 90), 4096, 1.0, 4, "bf16"),
+    (4, 2, (64, 128), 151936, 1.0, 16, "f32"),
+    (5, 3, (20, 60), 151936, 0.8, 16, "bf16"),
+]
+
+
+@pytest.mark.parametrize("seed,batch,nodes,V,temp,D,ldt", CASES)
+def test_stochastic_walk_matches_oracle(seed, batch, nodes, V, temp, D, ldt):
+    announce(f"stochastic accept seed {seed} B {batch} V {V} T {temp} D {D} {ldt}")
+    c = make_case(seed, batch, nodes, V, logit_dtype=ldt)
+    alen, aidx, nxt, err = run_gpu(c, temp, D, ldt)
+    ralen, raidx, rnxt = run_oracle(c, temp, D)
+    assert err == 0
+    assert np.array_equal(alen, ralen), (alen, ralen)
+    assert np.array_equal(aidx, raidx)
+    assert np.array_equal(nxt, rnxt), (nxt, rnxt)
+
+
+def test_stochastic_walk_exercises_both_outcomes():
+    """The random cases above accept and reject: check the inputs do both
+    (on the oracle, so the parity tests are not vacuous)."""
+    c = make_case(0, 8, (10, 40), 40)
+    alen, _, _ = run_oracle(c, 1.0, 16)
+    assert alen.max() >= 2 and (alen < np.diff(c["cu"])).any()
+
+
+def test_point_mass_target_gives_greedy_walk():
+    announce("stochastic accept: point-mass target")
+    rng = np.random.default_rng(9)
+    c = make_case(9, 6, (5, 50), 300)
+    T = c["draft"].shape[0]
+    bstar = rng.integers(0, 300, 6)
+    nstar = rng.integers(0, 300, T)
+    c["root_logits"][np.arange(6), bstar] = 3000.0
+    c["node_logits"][np.arange(T), nstar] = 3000.0
+    # drafts often equal to the parent's choice
+    owner = np.searchsorted(c["cu"], np.arange(T), side="right") - 1
+    want = np.where(c["parent"] < 0, bstar[owner], nstar[np.maximum(c["parent"] + c["cu"][owner], 0)])
+    c["draft"] = np.where(rng.random(T) < 0.7, want, c["draft"]).astype(np.int32)
+    alen, aidx, nxt, err = run_gpu(c, 1.0, 16)
+    galen, gaidx, gnxt = O.accept_greedy(c["parent"], c["draft"], nstar.astype(np.int32), bstar.astype(np.int32),
+                                         c["cu"], 16)
+    assert err == 0
+    assert np.array_equal(alen, galen) and np.array_equal(aidx, gaidx) and np.array_equal(nxt, gnxt)
+    assert galen.max() >= 2
+
+
+def test_errors_reported_per_request():
+    announce("stochastic accept: errors")
+    c = make_case(11, 4, (6, 20), 100, dead=0.0)
+    lo1, lo2 = int(c["cu"][1]), int(c["cu"][2])
+    c["parent"][lo1 + 3] = 5            # request 1: a parent after its child
+    c["draft"][lo2 + 1] = 100           # request 2: a token outside the vocabulary
+    alen, aidx, nxt, err = run_gpu(c, 1.0, 16)
+    assert err == max((O.ERR_BAD_PARENT << 24) | (lo1 + 3), (B().DEVERR_BAD_TOKEN << 24) | (lo2 + 1))
+    for b in (1, 2):
+        assert alen[b] == 0 and nxt[b] == -1 and (aidx[b] == -1).all()
+    # the good requests are walked as the oracle walks them
+    for b in (0, 3):
+        lo, hi = int(c["cu"][b]), int(c["cu"][b + 1])
+        path, t = O.accept_stochastic_one(c["parent"][lo:hi], c["draft"][lo:hi], c["root_logits"][b].astype(np.float64),
+                                          c["node_logits"][lo:hi].astype(np.float64), 1.0,
+                                          c["root_q"][b].astype(np.float64), c["node_q"][lo:hi].astype(np.float64),
+                                          c["u_accept"][lo:hi], float(c["u_final"][b]), 16)
+        assert alen[b] == len(path) and list(aidx[b, :len(path)]) == path and nxt[b] == t

@@ -21,6 +21,7 @@ TV_MAX_NODES, TV_MAX_DEPTH, TV_MAX_LEDGER, TV_MAX_VOCAB = 1024, 64, 8192, 167772
 DEVERR_BAD_PARENT, DEVERR_TOO_DEEP, DEVERR_BAD_REQUEST, DEVERR_BAD_PATH, DEVERR_BAD_LEDGER = 1, 2, 3, 4, 5
 DEVERR_LIMIT = 6
 DEVERR_BAD_SLOT = 7
+DEVERR_BAD_TOKEN = 8
 TV_GDN_HEAD_DIM, TV_GDN_MAX_NODES, TV_GDN_MAX_TABLE = 128, 256, 4096
 
 
@@ -80,6 +81,11 @@ def lib() -> C.CDLL:
     L.tree_target_sample_workspace_size.restype = sz
     L.tree_target_sample.argtypes = [vp, i32, i32, C.c_int, f32, vp, vp, vp, sz, vp]
     L.tree_target_sample.restype = C.c_int
+    L.tree_accept_stochastic_workspace_size.argtypes = [i32, i32, i32]
+    L.tree_accept_stochastic_workspace_size.restype = sz
+    L.tree_accept_stochastic.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, C.c_int, f32, vp, vp, i32, vp, vp,
+                                         vp, vp, vp, vp, sz, vp, vp]
+    L.tree_accept_stochastic.restype = C.c_int
     L.tree_rope_apply.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32, C.c_int, vp, vp]
     L.tree_rope_apply.restype = C.c_int
     L.kv_rollback_token_table.argtypes = [vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp]
@@ -449,6 +455,40 @@ def tree_target_sample(logits, temperature: float, u, token=None, workspace=None
         _ptr(logits), rows, vocab, code, float(temperature), _ptr(u), _ptr(token), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return token
+
+
+def tree_accept_stochastic(parent, draft_tokens, cu_nodes, root_logits, node_logits, temperature: float, root_q,
+                           node_q, u_accept, u_final, max_depth: int, err=None, workspace=None, stream=None):
+    """The stochastic tree walk: root_logits [B, V] / node_logits [T, V]
+    (float32 or bfloat16), root_q [B, V] / node_q [T, V] float32 draft
+    probabilities, u_accept [T] / u_final [B] float64 uniforms ->
+    (accept_len [B], accept_idx [B, max_depth], next_token [B], err)."""
+    import torch
+    B, V = root_logits.shape
+    T = int(parent.numel())
+    code = _dtype_code(root_logits)
+    dev = root_logits.device
+    for t, n in ((parent, "parent"), (draft_tokens, "draft_tokens"), (cu_nodes, "cu_nodes")):
+        _need(t, n, torch.int32)
+    _need(root_logits, "root_logits", None, B * V)
+    _need(node_logits, "node_logits", root_logits.dtype, T * V)
+    _need(root_q, "root_q", torch.float32, B * V)
+    _need(node_q, "node_q", torch.float32, T * V)
+    _need(u_accept, "u_accept", torch.float64, T)
+    _need(u_final, "u_final", torch.float64, B)
+    alen = torch.empty(B, dtype=torch.int32, device=dev)
+    aidx = torch.empty((B, max_depth), dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev) if err is None else err
+    ws_bytes = int(lib().tree_accept_stochastic_workspace_size(B, T, V))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _check("tree_accept_stochastic", lib().tree_accept_stochastic(
+        _ptr(parent), _ptr(draft_tokens), _ptr(cu_nodes), B, T, max_depth, _ptr(root_logits), _ptr(node_logits),
+        code, float(temperature), _ptr(root_q), _ptr(node_q), V, _ptr(u_accept), _ptr(u_final), _ptr(alen),
+        _ptr(aidx), _ptr(nxt), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(err),
+        _stream(stream)))
+    return alen, aidx, nxt, err
 
 
 def tree_rope_apply(q, k_cache, pos_ids, cu_nodes, kv_start, prefix_len, base: float = 1.0e6, err=None,

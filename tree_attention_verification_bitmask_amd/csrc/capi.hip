@@ -359,6 +359,42 @@ tv_status tree_accept_greedy(const int32_t *parent, const int32_t *draft_tokens,
                                                   accept_idx, next_token, err, (hipStream_t)stream));
 }
 
+size_t tree_accept_stochastic_workspace_size(int32_t batch, int32_t total_nodes, int32_t vocab) {
+    if (check_batch(batch, total_nodes) != TV_OK || vocab < 1 || vocab > TV_MAX_VOCAB) return 0;
+    return tv::accept_stochastic_workspace(batch, total_nodes, vocab);
+}
+
+tv_status tree_accept_stochastic(const int32_t *parent, const int32_t *draft_tokens, const int32_t *cu_nodes,
+                                 int32_t batch, int32_t total_nodes, int32_t max_depth, const void *root_logits,
+                                 const void *node_logits, tv_dtype dtype, float temperature, const float *root_q,
+                                 const float *node_q, int32_t vocab, const double *u_accept, const double *u_final,
+                                 int32_t *accept_len, int32_t *accept_idx, int32_t *next_token, void *workspace,
+                                 size_t workspace_bytes, int32_t *err, void *stream) {
+    tv_status st = check_batch(batch, total_nodes);
+    if (st != TV_OK) return st;
+    if (max_depth < 1 || vocab < 1) return TV_ERR_SHAPE;
+    if (!(temperature > 0.f) || !(temperature < INFINITY)) return TV_ERR_SHAPE;
+    if (max_depth > TV_MAX_DEPTH || vocab > TV_MAX_VOCAB) return TV_ERR_LIMIT;
+    if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_DTYPE;
+    if (!cu_nodes || !root_logits || !root_q || !u_final || !accept_len || !accept_idx || !next_token)
+        return TV_ERR_NULL;
+    if (total_nodes > 0 && (!parent || !draft_tokens || !node_logits || !node_q || !u_accept)) return TV_ERR_NULL;
+    const size_t es = dtype == TV_F32 ? 4 : 2;
+    if (!aligned(root_logits, es) || !aligned(node_logits, es) || !aligned(root_q, 4) || !aligned(node_q, 4) ||
+        !aligned(u_accept, 8) || !aligned(u_final, 8))
+        return TV_ERR_ALIGN;
+    const size_t need = tv::accept_stochastic_workspace(batch, total_nodes, vocab);
+    if (batch > 0) {
+        if (!workspace || workspace_bytes < need) return TV_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return TV_ERR_ALIGN;
+    }
+    if (batch == 0) return TV_OK;
+    return launch_status(tv::launch_accept_stochastic(
+        parent, draft_tokens, cu_nodes, batch, total_nodes, max_depth, root_logits, node_logits, dtype,
+        1.0 / (double)temperature, root_q, node_q, vocab, u_accept, u_final, accept_len, accept_idx, next_token,
+        workspace, err, (hipStream_t)stream));
+}
+
 tv_status kv_compact_path(void *k_cache, void *v_cache, const int32_t *cu_nodes,
                           const int32_t *kv_start, const int32_t *prefix_len,
                           const int32_t *accept_len, const int32_t *accept_idx, int32_t batch,

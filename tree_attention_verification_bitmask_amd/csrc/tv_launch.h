@@ -43,6 +43,15 @@ int64_t target_sample_blocks(int rows, int vocab);
 hipError_t launch_target_sample(const void *logits, int rows, int vocab, tv_dtype dtype, double inv_t,
                                 const double *u, int32_t *token, void *workspace, hipStream_t stream);
 
+// tree_accept_stochastic: workspace bytes and the launch (stats, then walk).
+size_t accept_stochastic_workspace(int batch, int total_nodes, int vocab);
+hipError_t launch_accept_stochastic(const int32_t *parent, const int32_t *draft, const int32_t *cu_nodes, int batch,
+                                    int total_nodes, int max_depth, const void *root_logits,
+                                    const void *node_logits, tv_dtype dtype, double inv_t, const float *root_q,
+                                    const float *node_q, int vocab, const double *u_accept, const double *u_final,
+                                    int32_t *accept_len, int32_t *accept_idx, int32_t *next_token, void *workspace,
+                                    int32_t *err, hipStream_t stream);
+
 // The tree part of RoPE inside tree_attn_verify: (cos, sin) of every node's
 // angles into cs [T, d/2] (float2) and the tree's K rows rotated in place
 // (contiguous rows from kv_start, or through the token table when non-null).
