@@ -133,9 +133,9 @@ def ingest_traffic(workload: str, fetch_dir: str, write_dir: str, calib_mib: int
         f"{calib_mib}`; run from /tmp on the GPU box:\n\n"
         "```\n"
         "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -o p -- python3 $REPO/bench.py "
-        f"--workload {workload} --steps 5 --warmup 2 --no-cpu-baseline --calib-copy-mib {calib_mib}\n"
+        f"--workload {workload} --secondary none --steps 5 --warmup 2 --no-cpu-baseline --calib-copy-mib {calib_mib}\n"
         "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/write -o p -- python3 $REPO/bench.py "
-        f"--workload {workload} --steps 5 --warmup 2 --no-cpu-baseline --calib-copy-mib {calib_mib}\n"
+        f"--workload {workload} --secondary none --steps 5 --warmup 2 --no-cpu-baseline --calib-copy-mib {calib_mib}\n"
         f"python3 $REPO/bench.py --workload {workload} --ingest-traffic OUT/fetch OUT/write\n"
         "```\n\n"
         "A call of tree_attn_verify is attn_fwd_kernel plus attn_combine_kernel (and,\n"
@@ -245,6 +245,10 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--waves", type=int, default=0,
                     help="tuning: plan override for tree_attn_verify, waves per workgroup (4 or 8; 0 = library)")
+    ap.add_argument("--paged", action="store_true",
+                    help="attention variant: K/V through a token table over a permuted pool of cache rows")
+    ap.add_argument("--rope-base", type=float, default=0.0,
+                    help="attention variant: RoPE inside the call at this base (0 = off)")
     ap.add_argument("--splits", type=int, default=0,
                     help="tuning: plan override for tree_attn_verify, key-axis slices (0 = library)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -272,6 +276,8 @@ def main(argv=None):
                     help="time tree_target_sample (the target's sampled choice per node, T > 0) on the "
                          "--argmax-rows x --argmax-vocab logits instead of the pass")
     ap.add_argument("--sample-temperature", type=float, default=1.0)
+    ap.add_argument("--stochastic", action="store_true",
+                    help="time tree_accept_stochastic instead (c3's tree, the Qwen3 vocabulary, fp32 logits)")
     ap.add_argument("--rope", action="store_true",
                     help="time tree_rope_apply and kv_rollback_token_table on the workload instead of the pass")
     ap.add_argument("--gdn", action="store_true",
@@ -303,6 +309,8 @@ def main(argv=None):
         return bench_argmax(args, torch, BND, L, dev)
     if args.sample:
         return bench_sample(args, torch, BND, L, dev)
+    if args.stochastic:
+        return bench_stochastic(args, torch, BND, L, dev)
     if args.rope:
         return bench_rope(args, torch, BND, L, dev)
     if args.gdn:
@@ -381,8 +389,36 @@ def time_pass(args, torch, BND, L, dev, wl, steps: int, warmup: int) -> dict:
     newlen = torch.empty(B, dtype=torch.int32, device=dev)
     err = torch.zeros(4, dtype=torch.int32, device=dev)
     ov = BND._override(args.splits, BND.TV_ORDER_AUTO, args.waves)
+    # variants of the attention call: K/V through a token table over a
+    # permuted pool (1.5x the rows), and RoPE inside the call
+    pools, tables = [], []
+    if args.paged:
+        rng = np.random.default_rng(1234)
+        rows = sets[0][1].shape[0]
+        pool = rows * 3 // 2
+        lens = (wl.prefix_len.astype(np.int64) + np.diff(wl.cu_nodes)).astype(np.int64)
+        stride = int(lens.max())
+        for (q, k, v) in sets:
+            slot_of_row = rng.permutation(pool)[:rows]
+            idx = torch.from_numpy(slot_of_row).to(dev)
+            kp = torch.zeros((pool,) + tuple(k.shape[1:]), dtype=k.dtype, device=dev)
+            vp = torch.zeros_like(kp)
+            kp[idx] = k
+            vp[idx] = v
+            tab = np.zeros((B, stride), np.int32)
+            for b in range(B):
+                k0s = int(wl.kv_start[b])
+                tab[b, :lens[b]] = slot_of_row[k0s:k0s + lens[b]]
+            pools.append((kp, vp))
+            tables.append(i32(tab))
+    inputs = [BND._inputs(None, 0.0, None)] * R
+    if args.paged or args.rope_base > 0:
+        inputs = [BND.AttnInputs(int(pos.data_ptr()) if args.rope_base > 0 else None,
+                                 int(tables[r].data_ptr()) if args.paged else None,
+                                 int(tables[r].shape[1]) if args.paged else 0, float(args.rope_base))
+                  for r in range(R)]
     ws_bytes = BND.tree_attn_verify_workspace_size(B, T, wl.max_nodes, wl.max_prefix, wl.hq, wl.hkv, wl.d, code,
-                                                   args.splits, BND.TV_ORDER_AUTO, args.waves)
+                                                   args.splits, BND.TV_ORDER_AUTO, args.waves, inputs[0])
     plan = BND.tree_attn_verify_plan(B, T, wl.max_nodes, wl.max_prefix, wl.hq, wl.hkv, wl.d, code,
                                      args.splits, BND.TV_ORDER_AUTO, args.waves)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
@@ -395,9 +431,10 @@ def time_pass(args, torch, BND, L, dev, wl, steps: int, warmup: int) -> dict:
     mask_args = (P_(parent), P_(cu), P_(P), B, T, wl.max_nodes, wl.max_depth, P_(anc), P_(level), P_(pos),
                  C_void(err.data_ptr()), sp)
     attn_args = []
-    for (q, k, v), o in zip(sets, outs):
-        attn_args.append((P_(q), P_(k), P_(v), P_(cu), P_(ks), P_(P), P_(anc), B, T, wl.max_nodes, wl.max_prefix,
-                          k.shape[0], wl.hq, wl.hkv, wl.d, float(wl.scale), code, P_(o), P_(ws), ws.numel(),
+    for r, ((q, k, v), o) in enumerate(zip(sets, outs)):
+        ka, va = pools[r] if args.paged else (k, v)
+        attn_args.append((P_(q), P_(ka), P_(va), P_(cu), P_(ks), P_(P), P_(anc), B, T, wl.max_nodes, wl.max_prefix,
+                          ka.shape[0], wl.hq, wl.hkv, wl.d, float(wl.scale), code, P_(o), P_(ws), ws.numel(),
                           C_void(err.data_ptr() + 4), sp))
     acc_args = (P_(parent), P_(draft), P_(target), P_(root), P_(cu), B, T, wl.max_depth, P_(alen), P_(aidx),
                 P_(nxt), C_void(err.data_ptr() + 8), sp)
@@ -412,11 +449,12 @@ def time_pass(args, torch, BND, L, dev, wl, steps: int, warmup: int) -> dict:
         st = L.tree_mask_build(*mask_args)
         if ev is not None:
             ev[0].record(stream)
-        if ov is None:
+        if ov is None and inputs[r] is None:
             st |= L.tree_attn_verify(*attn_args[r])
         else:
-            a = attn_args[r]   # (..., scale, dtype, out, workspace, bytes, err, stream): no optional inputs
-            st |= L.tree_attn_verify_ex(*a[:17], None, *a[17:-1], ctypes.byref(ov), a[-1])
+            a = attn_args[r]   # (..., scale, dtype, out, workspace, bytes, err, stream)
+            st |= L.tree_attn_verify_ex(*a[:17], ctypes.byref(inputs[r]) if inputs[r] is not None else None,
+                                        *a[17:-1], ctypes.byref(ov) if ov is not None else None, a[-1])
         if ev is not None:
             ev[1].record(stream)
         if args.separate_commit:
@@ -512,7 +550,8 @@ def time_pass(args, torch, BND, L, dev, wl, steps: int, warmup: int) -> dict:
                    "cache": "warm" if args.warm else "cold",
                    "commit": "two launches" if args.separate_commit else "one launch",
                    "workspace_bytes": ws_bytes, "plan": plan, "host_enqueue_ms": t_host_enq * 1e3,
-                   "spin_ahead_ms": spin_ms},
+                   "spin_ahead_ms": spin_ms,
+                   "attention_inputs": {"token_table": bool(args.paged), "rope_base": float(args.rope_base)}},
         "roofline": roof,
     }
     return line
@@ -758,6 +797,106 @@ def bench_sample(args, torch, BND, L, dev):
         dt = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": n / dt, "unit": "nodes/s", "cores": 1, "kind": "oracle",
                                 "sample": f"target_sample on rows 0..{n - 1} of the same logits ({dt:.2f} s)"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_stochastic(args, torch, BND, L, dev):
+    """One step = one tree_accept_stochastic call on c3's tree (one request,
+    128 nodes) over the Qwen3 vocabulary (151936): target logits fp32
+    [1 + 128, V], draft probabilities fp32 [1 + 128, V] (the target's logits
+    plus noise, so candidates are often but not always accepted), each child's
+    token drawn from its parent's q, seeded uniforms; rotated copies keep the
+    Infinity Cache cold.  value = verification steps (requests) per second.
+    The roofline counts the logits read once (the statistics pass); the walk's
+    reads (a few elements per candidate, two passes over q and the residual
+    per rejection, one for the final draw) depend on the data and come on
+    top."""
+    wl = W.make_workload("c3", seed=args.seed)
+    V = args.argmax_vocab
+    T = wl.total_nodes
+    rng = np.random.default_rng(args.seed)
+    rl = rng.normal(0, 3, (1, V)).astype(np.float32)
+    nl = rng.normal(0, 3, (T, V)).astype(np.float32)
+
+    def qd(x):
+        z = x.astype(np.float64) + rng.normal(0, 1.0, x.shape)
+        z = np.exp(z - z.max(axis=1, keepdims=True))
+        return (z / z.sum(axis=1, keepdims=True)).astype(np.float32)
+    rq, nq = qd(rl), qd(nl)
+    draft = np.empty(T, np.int32)
+    for i in range(T):
+        pa = int(wl.parent[i])
+        q = (rq[0] if pa < 0 else nq[pa]).astype(np.float64)
+        draft[i] = int(rng.choice(V, p=q / q.sum()))
+    ua, uf = rng.random(T), rng.random(1)
+    set_bytes = 2 * (1 + T) * V * 4
+    R = max(2, math.ceil(COLD_BYTES / set_bytes))
+    t32 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    sets = [(t32(rl), t32(nl), t32(rq), t32(nq)) for _ in range(R)]
+    parent, dr, cu = t32(wl.parent.astype(np.int32)), t32(draft), t32(wl.cu_nodes.astype(np.int32))
+    u_a, u_f = t32(ua), t32(uf)
+    D = wl.max_depth
+    alen = torch.empty(1, dtype=torch.int32, device=dev)
+    aidx = torch.empty((1, D), dtype=torch.int32, device=dev)
+    nxt = torch.empty(1, dtype=torch.int32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws_bytes = int(L.tree_accept_stochastic_workspace_size(1, T, V))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = C_void(stream.cuda_stream)
+    P_ = lambda t: C_void(t.data_ptr())
+    temp = 1.0
+    call_args = [(P_(parent), P_(dr), P_(cu), 1, T, D, P_(a), P_(b), BND.TV_F32, temp, P_(c), P_(d), V, P_(u_a),
+                  P_(u_f), P_(alen), P_(aidx), P_(nxt), P_(ws), ws_bytes, P_(err), sp) for (a, b, c, d) in sets]
+    for i in range(args.warmup):
+        if L.tree_accept_stochastic(*call_args[i % R]):
+            raise RuntimeError("tree_accept_stochastic rejected its arguments")
+    torch.cuda.synchronize()
+    if int(err.item()) != 0:
+        raise RuntimeError(f"device error {int(err.item()):#x}")
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1 << 24)
+    start.record(stream)
+    for i in range(K):
+        evs[i][0].record(stream)
+        L.tree_accept_stochastic(*call_args[(args.warmup + i) % R])
+        evs[i][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    call_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    us = float(call_ms.mean() * 1e3)
+    byts = (1 + T) * V * 4
+    roof = {"bound": "hbm", "achieved": byts / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "traffic": None, "traffic_detail": "not measured for this kernel",
+            "kernel": "tree_accept_stochastic", "avg_us": us,
+            "p10_us": float(np.percentile(call_ms, 10) * 1e3), "p90_us": float(np.percentile(call_ms, 90) * 1e3),
+            "alg_bytes": byts, "accept_len": int(alen.item())}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    line = {
+        "metric": "stochastic verification steps per second (tree_accept_stochastic)",
+        "value": 1.0 / (us * 1e-6),
+        "unit": "requests/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": start.elapsed_time(end) / K,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32->f64",
+        "data": "synthetic",
+        "config": {"workload": f"c3 tree ({T} nodes), vocab {V}, fp32 logits and draft probabilities, T {temp}",
+                   "seed": args.seed, "cold_cache_sets": R},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import tree_verify_oracle as O
+        t0 = time.perf_counter()
+        n = 0
+        while n < 3 and time.perf_counter() - t0 < args.cpu_budget:
+            O.accept_stochastic(wl.parent, draft, wl.cu_nodes, rl.astype(np.float64), nl.astype(np.float64), temp,
+                                rq.astype(np.float64), nq.astype(np.float64), ua, uf, D)
+            n += 1
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": n / dt, "unit": "requests/s", "cores": 1, "kind": "oracle",
+                                "sample": f"{n} oracle walks of the same request ({dt:.2f} s)"}
     print(json.dumps(line), flush=True)
     return 0
 
