@@ -349,8 +349,8 @@ tv_status tree_accept_greedy(const int32_t *parent, const int32_t *draft_tokens,
  * Out: accept_len [B], accept_idx [B, max_depth] (request-local, -1 padded),
  *      next_token [B], as tree_accept_greedy.
  * Workspace: tree_accept_stochastic_workspace_size(batch, total_nodes, vocab)
- *      bytes (16 per row of logits plus 8 per logit of each request's
- *      residual), 256-byte aligned; no contents required.
+ *      bytes (16 per 2048 logits of every row, then 8 per logit of each
+ *      request's residual), 256-byte aligned; no contents required.
  * err: BAD_REQUEST (cu_nodes outside [0, T], decreasing, or N_b above
  *      TV_MAX_NODES), BAD_PARENT, BAD_TOKEN (a draft token >= vocab); such a
  *      request gets accept_len 0, no path and next_token -1.

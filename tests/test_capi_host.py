@@ -416,7 +416,8 @@ def test_gdn_host_checks(L):
 def test_accept_stochastic_host_checks(L):
     B, T, V = 2, 10, 1000
     need = L.tree_accept_stochastic_workspace_size(B, T, V)
-    assert need == ((12 * 16 + 255) // 256) * 256 + B * V * 8   # row stats, then one residual per request
+    assert need == ((12 * 16 + 255) // 256) * 256 + B * V * 8   # chunk stats (1 chunk), one residual per request
+    assert L.tree_accept_stochastic_workspace_size(1, 2, 4097) == ((3 * 3 * 16 + 255) // 256) * 256 + 4097 * 8
     assert L.tree_accept_stochastic_workspace_size(-1, T, V) == 0
     assert L.tree_accept_stochastic_workspace_size(B, T, 0) == 0
 

@@ -11,16 +11,22 @@
 // index, each against the residual left by the rejections before it.
 //
 // Two launches:
-//  * stats: one workgroup per row (roots, then nodes) writes M = max y and
-//    Z = sum exp(y - M), y = logit * (1/T), float64.  p(x) = exp(y_x - M) / Z.
-//  * walk: one workgroup of 1024 threads per request.  A candidate's test
-//    reads p(x) and q(x) only; a rejection costs two passes over the
-//    vocabulary (the residual's sum, then the residual itself, float64 in the
-//    workspace); the final draw one pass: each thread sums a contiguous range
-//    of weights in index order, a block scan gives the range starts, and the
-//    range holding u * total is scanned again element by element.
-// All arithmetic is float64, the precision of the acceptance decisions and of
-// the draw; only the order of additions differs from a sequential sum.
+//  * chunk statistics: one wavefront per 2048-logit chunk of every row
+//    (roots, then nodes), four per workgroup, writes the chunk's maximum m_c
+//    of y = logit * (1/T) and s_c = sum exp(y - m_c), float64: every logit is
+//    read once, by the whole GPU.
+//  * walk: one workgroup of 1024 threads per request.  At each node it
+//    merges that row's chunk statistics into M = max y and Z = sum exp(y - M)
+//    (p(x) = exp(y_x - M) / Z).  A candidate's test reads p(x) and q(x) only.
+//    The first rejection at a node writes the residual (p - q)+ to the
+//    workspace and sums it in one pass; a later one takes two passes without
+//    exponentials (the sum, then the residual).  The final draw: each thread
+//    sums a contiguous range of weights in index order, a block scan gives
+//    the range starts, and the range holding u * total is scanned again.
+// All arithmetic is float64 (exp by the table-driven exp_nonpos), the
+// precision of the acceptance decisions and of the draw; only the order of
+// additions differs from a sequential sum.
+#include "exp64.h"
 #include "tv_device.h"
 #include "tv_launch.h"
 
@@ -29,7 +35,8 @@
 namespace tv {
 namespace {
 
-constexpr int kStatThreads = 256;
+constexpr int kStatWaves = 4;
+constexpr int kStatChunk = 2048;  // logits per chunk statistic
 constexpr int kWalkThreads = 1024;
 constexpr int kWalkWaves = kWalkThreads / 64;
 
@@ -80,22 +87,37 @@ __device__ __forceinline__ double block_max64(double x, double *red) {
     return t;
 }
 
+// Chunk statistics: wave gw takes chunk gw % nchunks of row gw / nchunks.
 template <typename T>
-__global__ void __launch_bounds__(kStatThreads) stoch_stats_kernel(const T *__restrict__ root_logits,
-                                                                   const T *__restrict__ node_logits, int batch,
-                                                                   int vocab, double inv_t,
-                                                                   double2 *__restrict__ stats) {
-    __shared__ double red[kStatThreads / 64];
-    const int r = blockIdx.x;
+__global__ void __launch_bounds__(64 * kStatWaves) stoch_chunk_kernel(const T *__restrict__ root_logits,
+                                                                      const T *__restrict__ node_logits, int batch,
+                                                                      int rows, int vocab, int nchunks, double inv_t,
+                                                                      ExpConst ek, double2 *__restrict__ cst) {
+    __shared__ double etab[kExpTable];
+    exp_table_fill(etab);
+    __syncthreads();
+    const int64_t gw = (int64_t)blockIdx.x * kStatWaves + (threadIdx.x >> 6);
+    if (gw >= (int64_t)rows * nchunks) return;
+    const int lane = threadIdx.x & 63;
+    const int r = (int)(gw / nchunks), c = (int)(gw - (int64_t)r * nchunks);
     const T *row = r < batch ? root_logits + (int64_t)r * vocab : node_logits + (int64_t)(r - batch) * vocab;
+    const int i0 = c * kStatChunk, i1 = min(vocab, i0 + kStatChunk);
+    double y[kStatChunk / 64];
     double m = -INFINITY;
-    for (int i = threadIdx.x; i < vocab; i += kStatThreads) m = fmax(m, ld64(row, i) * inv_t);
-    m = block_max64<kStatThreads / 64>(m, red);
-    double s = 0.0;
-    if (m > -INFINITY)
-        for (int i = threadIdx.x; i < vocab; i += kStatThreads) s += exp(ld64(row, i) * inv_t - m);
-    s = block_sum64<kStatThreads / 64>(s, red);
-    if (threadIdx.x == 0) stats[r] = make_double2(m, s);
+#pragma unroll
+    for (int e = 0; e < kStatChunk / 64; ++e) {
+        const int i = i0 + e * 64 + lane;
+        y[e] = i < i1 ? ld64(row, i) * inv_t : -INFINITY;
+        m = fmax(m, y[e]);
+    }
+    m = wave_max64(m);
+    double sum = 0.0;
+    if (m > -INFINITY) {
+#pragma unroll
+        for (int e = 0; e < kStatChunk / 64; ++e) sum += exp_nonpos(y[e] - m, etab, ek);
+    }
+    sum = wave_sum64(sum);
+    if (lane == 0) cst[gw] = make_double2(m, sum);
 }
 
 template <typename T>
@@ -103,10 +125,12 @@ __global__ void __launch_bounds__(kWalkThreads) stoch_walk_kernel(
     const int32_t *__restrict__ parent, const int32_t *__restrict__ draft, const int32_t *__restrict__ cu_nodes,
     int batch, int total_nodes, int max_depth, const T *__restrict__ root_logits, const T *__restrict__ node_logits,
     int vocab, double inv_t, const float *__restrict__ root_q, const float *__restrict__ node_q,
-    const double *__restrict__ u_accept, const double *__restrict__ u_final, const double2 *__restrict__ stats,
-    double *__restrict__ res_all, int32_t *__restrict__ accept_len, int32_t *__restrict__ accept_idx,
-    int32_t *__restrict__ next_token, int32_t *__restrict__ err) {
+    const double *__restrict__ u_accept, const double *__restrict__ u_final, const double2 *__restrict__ cst,
+    int nchunks, ExpConst ek, double *__restrict__ res_all, int32_t *__restrict__ accept_len,
+    int32_t *__restrict__ accept_idx, int32_t *__restrict__ next_token, int32_t *__restrict__ err) {
     __shared__ int kids[TV_MAX_NODES];
+    __shared__ double etab[kExpTable];
+    exp_table_fill(etab);  // (visible after the barrier of the checks below)
     __shared__ int wcount[kWalkWaves];
     __shared__ double red[kWalkWaves];
     __shared__ int sel[2];
@@ -153,13 +177,25 @@ __global__ void __launch_bounds__(kWalkThreads) stoch_walk_kernel(
     const T *lrow = nullptr;
     const float *qrow = nullptr;
     // r(v): the current residual (normalised)
-    auto r_at = [&](int v) { return implicit ? exp(ld64(lrow, v) * inv_t - M) / Z : res[v] / S; };
+    auto p_at = [&](int v) { return exp_nonpos(ld64(lrow, v) * inv_t - M, etab, ek) / Z; };
+    auto r_at = [&](int v) { return implicit ? p_at(v) : res[v] / S; };
     for (;;) {
         const int row = cur < 0 ? b : batch + lo + cur;
         lrow = cur < 0 ? root_logits + (int64_t)b * vocab : node_logits + (int64_t)(lo + cur) * vocab;
         qrow = cur < 0 ? root_q + (int64_t)b * vocab : node_q + (int64_t)(lo + cur) * vocab;
-        M = stats[row].x;
-        Z = stats[row].y;
+        // M and Z of the row from its chunk statistics (chunk order)
+        {
+            const double2 *rc = cst + (int64_t)row * nchunks;
+            double mloc = -INFINITY;
+            for (int c = tid; c < nchunks; c += kWalkThreads) mloc = fmax(mloc, rc[c].x);
+            M = block_max64<kWalkWaves>(mloc, red);
+            double part = 0.0;
+            for (int c = tid; c < nchunks; c += kWalkThreads) {
+                const double2 cs = rc[c];
+                if (cs.x > -INFINITY) part += cs.y * exp_nonpos(cs.x - M, etab, ek);
+            }
+            Z = block_sum64<kWalkWaves>(part, red);
+        }
         implicit = true;
         // children of cur in ascending index (none once max_depth are accepted)
         const bool kid = L < max_depth && tid < n && parent[lo + tid] == cur;
@@ -187,14 +223,31 @@ __global__ void __launch_bounds__(kWalkThreads) stoch_walk_kernel(
                 break;
             }
             // rejected: r <- (r - q)+ / sum (r - q)+ (kept when that sum is 0)
-            double s1 = 0.0;
-            for (int v = tid; v < vocab; v += kWalkThreads) s1 += fmax(r_at(v) - (double)qrow[v], 0.0);
-            s1 = block_sum64<kWalkWaves>(s1, red);
-            if (s1 > 0.0) {
-                for (int v = tid; v < vocab; v += kWalkThreads) res[v] = fmax(r_at(v) - (double)qrow[v], 0.0);
-                implicit = false;
-                S = s1;
-                __syncthreads();
+            if (implicit) {
+                // from p: one pass writes (p - q)+ and sums it; if the sum is
+                // 0, r stays p (implicit) and the buffer is not read
+                double s1 = 0.0;
+                for (int v = tid; v < vocab; v += kWalkThreads) {
+                    const double d = fmax(p_at(v) - (double)qrow[v], 0.0);
+                    res[v] = d;
+                    s1 += d;
+                }
+                s1 = block_sum64<kWalkWaves>(s1, red);
+                if (s1 > 0.0) {
+                    implicit = false;
+                    S = s1;
+                }
+            } else {
+                // from the stored residual: the sum first (the residual must
+                // survive a zero sum), then the update in place
+                double s1 = 0.0;
+                for (int v = tid; v < vocab; v += kWalkThreads) s1 += fmax(res[v] / S - (double)qrow[v], 0.0);
+                s1 = block_sum64<kWalkWaves>(s1, red);
+                if (s1 > 0.0) {
+                    for (int v = tid; v < vocab; v += kWalkThreads) res[v] = fmax(res[v] / S - (double)qrow[v], 0.0);
+                    S = s1;
+                    __syncthreads();
+                }
             }
         }
         if (acc < 0) break;
@@ -205,11 +258,14 @@ __global__ void __launch_bounds__(kWalkThreads) stoch_walk_kernel(
     }
 
     // the next token: inverse transform over the residual's weights
-    auto w_at = [&](int v) { return implicit ? exp(ld64(lrow, v) * inv_t - M) : res[v]; };
+    auto w_at = [&](int v) { return implicit ? exp_nonpos(ld64(lrow, v) * inv_t - M, etab, ek) : res[v]; };
     const int per = (vocab + kWalkThreads - 1) / kWalkThreads;
     const int v0 = min(vocab, tid * per), v1 = min(vocab, v0 + per);
     double local = 0.0;
     int last = -1;  // the range's last index with a positive weight
+    // (unrolled: the range's loads are independent, so several are in flight
+    // at once instead of one memory round trip per element)
+#pragma unroll 8
     for (int v = v0; v < v1; ++v) {
         const double w = w_at(v);
         local += w;
@@ -243,6 +299,7 @@ __global__ void __launch_bounds__(kWalkThreads) stoch_walk_kernel(
     if (local > 0.0 && start <= thr && thr < start + local) {
         double c = start;
         int pick = last;
+#pragma unroll 8
         for (int v = v0; v < v1; ++v) {
             c += w_at(v);
             if (c > thr) {
@@ -265,7 +322,8 @@ __global__ void __launch_bounds__(kWalkThreads) stoch_walk_kernel(
 }  // namespace
 
 size_t accept_stochastic_workspace(int batch, int total_nodes, int vocab) {
-    const size_t stats = (size_t)(batch + total_nodes) * sizeof(double2);
+    const size_t nchunks = ((size_t)vocab + kStatChunk - 1) / kStatChunk;
+    const size_t stats = (size_t)(batch + total_nodes) * nchunks * sizeof(double2);
     return ((stats + 255) & ~(size_t)255) + (size_t)batch * vocab * sizeof(double);
 }
 
@@ -276,24 +334,29 @@ hipError_t launch_accept_stochastic(const int32_t *parent, const int32_t *draft,
                                     int32_t *accept_len, int32_t *accept_idx, int32_t *next_token, void *workspace,
                                     int32_t *err, hipStream_t stream) {
     if (batch == 0) return hipSuccess;
-    double2 *stats = (double2 *)workspace;
-    const size_t soff = ((size_t)(batch + total_nodes) * sizeof(double2) + 255) & ~(size_t)255;
-    double *res = (double *)((char *)workspace + soff);
+    const int nchunks = (vocab + kStatChunk - 1) / kStatChunk;
     const int rows = batch + total_nodes;
+    double2 *cst = (double2 *)workspace;
+    const size_t soff = ((size_t)rows * nchunks * sizeof(double2) + 255) & ~(size_t)255;
+    double *res = (double *)((char *)workspace + soff);
+    const ExpConst ek = exp_const();
+    const unsigned blocks = (unsigned)(((int64_t)rows * nchunks + kStatWaves - 1) / kStatWaves);
     if (dtype == TV_BF16) {
-        hipLaunchKernelGGL(stoch_stats_kernel<uint16_t>, dim3(rows), dim3(kStatThreads), 0, stream,
-                           (const uint16_t *)root_logits, (const uint16_t *)node_logits, batch, vocab, inv_t, stats);
+        hipLaunchKernelGGL(stoch_chunk_kernel<uint16_t>, dim3(blocks), dim3(64 * kStatWaves), 0, stream,
+                           (const uint16_t *)root_logits, (const uint16_t *)node_logits, batch, rows, vocab, nchunks,
+                           inv_t, ek, cst);
         hipLaunchKernelGGL(stoch_walk_kernel<uint16_t>, dim3(batch), dim3(kWalkThreads), 0, stream, parent, draft,
                            cu_nodes, batch, total_nodes, max_depth, (const uint16_t *)root_logits,
-                           (const uint16_t *)node_logits, vocab, inv_t, root_q, node_q, u_accept, u_final, stats, res,
-                           accept_len, accept_idx, next_token, err);
+                           (const uint16_t *)node_logits, vocab, inv_t, root_q, node_q, u_accept, u_final, cst,
+                           nchunks, ek, res, accept_len, accept_idx, next_token, err);
     } else {
-        hipLaunchKernelGGL(stoch_stats_kernel<float>, dim3(rows), dim3(kStatThreads), 0, stream,
-                           (const float *)root_logits, (const float *)node_logits, batch, vocab, inv_t, stats);
+        hipLaunchKernelGGL(stoch_chunk_kernel<float>, dim3(blocks), dim3(64 * kStatWaves), 0, stream,
+                           (const float *)root_logits, (const float *)node_logits, batch, rows, vocab, nchunks,
+                           inv_t, ek, cst);
         hipLaunchKernelGGL(stoch_walk_kernel<float>, dim3(batch), dim3(kWalkThreads), 0, stream, parent, draft,
                            cu_nodes, batch, total_nodes, max_depth, (const float *)root_logits,
-                           (const float *)node_logits, vocab, inv_t, root_q, node_q, u_accept, u_final, stats, res,
-                           accept_len, accept_idx, next_token, err);
+                           (const float *)node_logits, vocab, inv_t, root_q, node_q, u_accept, u_final, cst, nchunks,
+                           ek, res, accept_len, accept_idx, next_token, err);
     }
     return hipGetLastError();
 }
