@@ -133,7 +133,7 @@ __global__ void __launch_bounds__(kWalkThreads) stoch_walk_kernel(
     exp_table_fill(etab);  // (visible after the barrier of the checks below)
     __shared__ int wcount[kWalkWaves];
     __shared__ double red[kWalkWaves];
-    __shared__ int sel[2];
+    __shared__ int sel[3];
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     int32_t *idx_out = accept_idx + (int64_t)b * max_depth;
@@ -177,8 +177,11 @@ __global__ void __launch_bounds__(kWalkThreads) stoch_walk_kernel(
     const T *lrow = nullptr;
     const float *qrow = nullptr;
     // r(v): the current residual (normalised)
-    auto p_at = [&](int v) { return exp_nonpos(ld64(lrow, v) * inv_t - M, etab, ek) / Z; };
-    auto r_at = [&](int v) { return implicit ? p_at(v) : res[v] / S; };
+    // (normalised by multiplying with 1/Z and 1/S: a float64 division costs
+    // as much as the exponential, and these passes are float64-bound on one CU)
+    double iZ = 1.0, iS = 1.0;
+    auto p_at = [&](int v) { return exp_nonpos(ld64(lrow, v) * inv_t - M, etab, ek) * iZ; };
+    auto r_at = [&](int v) { return implicit ? p_at(v) : res[v] * iS; };
     for (;;) {
         const int row = cur < 0 ? b : batch + lo + cur;
         lrow = cur < 0 ? root_logits + (int64_t)b * vocab : node_logits + (int64_t)(lo + cur) * vocab;
@@ -195,6 +198,7 @@ __global__ void __launch_bounds__(kWalkThreads) stoch_walk_kernel(
                 if (cs.x > -INFINITY) part += cs.y * exp_nonpos(cs.x - M, etab, ek);
             }
             Z = block_sum64<kWalkWaves>(part, red);
+            iZ = 1.0 / Z;
         }
         implicit = true;
         // children of cur in ascending index (none once max_depth are accepted)
@@ -227,6 +231,7 @@ __global__ void __launch_bounds__(kWalkThreads) stoch_walk_kernel(
                 // from p: one pass writes (p - q)+ and sums it; if the sum is
                 // 0, r stays p (implicit) and the buffer is not read
                 double s1 = 0.0;
+#pragma unroll 8
                 for (int v = tid; v < vocab; v += kWalkThreads) {
                     const double d = fmax(p_at(v) - (double)qrow[v], 0.0);
                     res[v] = d;
@@ -236,16 +241,20 @@ __global__ void __launch_bounds__(kWalkThreads) stoch_walk_kernel(
                 if (s1 > 0.0) {
                     implicit = false;
                     S = s1;
+                    iS = 1.0 / S;
                 }
             } else {
                 // from the stored residual: the sum first (the residual must
                 // survive a zero sum), then the update in place
                 double s1 = 0.0;
-                for (int v = tid; v < vocab; v += kWalkThreads) s1 += fmax(res[v] / S - (double)qrow[v], 0.0);
+#pragma unroll 8
+                for (int v = tid; v < vocab; v += kWalkThreads) s1 += fmax(res[v] * iS - (double)qrow[v], 0.0);
                 s1 = block_sum64<kWalkWaves>(s1, red);
                 if (s1 > 0.0) {
-                    for (int v = tid; v < vocab; v += kWalkThreads) res[v] = fmax(res[v] / S - (double)qrow[v], 0.0);
+#pragma unroll 8
+                    for (int v = tid; v < vocab; v += kWalkThreads) res[v] = fmax(res[v] * iS - (double)qrow[v], 0.0);
                     S = s1;
+                    iS = 1.0 / S;
                     __syncthreads();
                 }
             }
@@ -263,8 +272,9 @@ __global__ void __launch_bounds__(kWalkThreads) stoch_walk_kernel(
     const int v0 = min(vocab, tid * per), v1 = min(vocab, v0 + per);
     double local = 0.0;
     int last = -1;  // the range's last index with a positive weight
-    // (unrolled: the range's loads are independent, so several are in flight
-    // at once instead of one memory round trip per element)
+    // (this and the passes above are unrolled: their loads are independent,
+    // so several are in flight at once instead of one memory round trip per
+    // element)
 #pragma unroll 8
     for (int v = v0; v < v1; ++v) {
         const double w = w_at(v);
@@ -290,32 +300,61 @@ __global__ void __launch_bounds__(kWalkThreads) stoch_walk_kernel(
     const double start = base + incl - local;
     const double thr = u_final[b] * total;
     if (tid == 0) {
-        sel[0] = INT_MAX;
-        sel[1] = -1;
+        sel[0] = INT_MAX;  // the chosen index
+        sel[1] = -1;       // the last index with a positive weight
+        sel[2] = INT_MAX;  // the thread whose range holds thr
     }
     __syncthreads();
     // the range whose span holds thr (one, unless rounding makes two adjacent
-    // spans overlap by an ulp: then the smaller index wins)
-    if (local > 0.0 && start <= thr && thr < start + local) {
-        double c = start;
-        int pick = last;
-#pragma unroll 8
-        for (int v = v0; v < v1; ++v) {
-            c += w_at(v);
-            if (c > thr) {
-                pick = v;
-                break;
-            }
-        }
-        atomicMin(&sel[0], pick);
-    }
+    // spans overlap by an ulp: then the earlier range wins)
+    if (local > 0.0 && start <= thr && thr < start + local) atomicMin(&sel[2], tid);
     // the last index with a positive weight, for a draw that rounding pushed
     // past the total
     if (last >= 0) atomicMax(&sel[1], last);
     __syncthreads();
+    const int owner = sel[2];  // uniform
+    if (owner != INT_MAX) {
+        // That range scanned by the whole block (one weight per thread, an
+        // inclusive block scan added to the range's start): the first index
+        // whose running sum exceeds thr, else the range's last positive one.
+        __shared__ double owner_start;
+        __shared__ int owner_last;
+        if (tid == owner) {
+            owner_start = start;
+            owner_last = last;
+        }
+        __syncthreads();
+        const int r0 = min(vocab, owner * per), r1 = min(vocab, r0 + per);
+        double run = owner_start;  // uniform: the running sum before the tile
+        for (int t0 = r0; t0 < r1; t0 += kWalkThreads) {
+            const bool in = t0 + tid < r1;
+            const double w = in ? w_at(t0 + tid) : 0.0;
+            double inc = w;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const double o = __shfl_up(inc, off, 64);
+                if (lane >= off) inc += o;
+            }
+            __syncthreads();
+            if (lane == 63) red[wv] = inc;
+            __syncthreads();
+            double before_w = 0.0, tile = 0.0;
+#pragma unroll
+            for (int w2 = 0; w2 < kWalkWaves; ++w2) {
+                before_w += w2 < wv ? red[w2] : 0.0;
+                tile += red[w2];
+            }
+            if (in && run + (before_w + inc) > thr) atomicMin(&sel[0], t0 + tid);
+            __syncthreads();
+            if (sel[0] != INT_MAX) break;  // uniform
+            run += tile;
+        }
+        if (tid == 0 && sel[0] == INT_MAX) sel[0] = owner_last;
+    }
+    __syncthreads();
     if (tid == 0) {
         accept_len[b] = L;
-        next_token[b] = sel[0] != INT_MAX ? sel[0] : (sel[1] >= 0 ? sel[1] : 0);
+        next_token[b] = owner != INT_MAX ? sel[0] : (sel[1] >= 0 ? sel[1] : 0);
     }
 }
 
