@@ -251,6 +251,8 @@ def main(argv=None):
                     help="attention variant: RoPE inside the call at this base (0 = off)")
     ap.add_argument("--splits", type=int, default=0,
                     help="tuning: plan override for tree_attn_verify, key-axis slices (0 = library)")
+    ap.add_argument("--order", choices=("auto", "static", "planned", "balanced"), default="auto",
+                    help="tuning: plan override for tree_attn_verify, batch task order (auto = library)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (counter calibration)")
@@ -388,7 +390,9 @@ def time_pass(args, torch, BND, L, dev, wl, steps: int, warmup: int) -> dict:
     nxt = torch.empty(B, dtype=torch.int32, device=dev)
     newlen = torch.empty(B, dtype=torch.int32, device=dev)
     err = torch.zeros(4, dtype=torch.int32, device=dev)
-    ov = BND._override(args.splits, BND.TV_ORDER_AUTO, args.waves)
+    order = {"auto": BND.TV_ORDER_AUTO, "static": BND.TV_ORDER_STATIC, "planned": BND.TV_ORDER_PLANNED,
+             "balanced": BND.TV_ORDER_BALANCED}[args.order]
+    ov = BND._override(args.splits, order, args.waves)
     # variants of the attention call: K/V through a token table over a
     # permuted pool (1.5x the rows), and RoPE inside the call
     pools, tables = [], []
@@ -418,9 +422,9 @@ def time_pass(args, torch, BND, L, dev, wl, steps: int, warmup: int) -> dict:
                                  int(tables[r].shape[1]) if args.paged else 0, float(args.rope_base))
                   for r in range(R)]
     ws_bytes = BND.tree_attn_verify_workspace_size(B, T, wl.max_nodes, wl.max_prefix, wl.hq, wl.hkv, wl.d, code,
-                                                   args.splits, BND.TV_ORDER_AUTO, args.waves, inputs[0])
+                                                   args.splits, order, args.waves, inputs[0])
     plan = BND.tree_attn_verify_plan(B, T, wl.max_nodes, wl.max_prefix, wl.hq, wl.hkv, wl.d, code,
-                                     args.splits, BND.TV_ORDER_AUTO, args.waves)
+                                     args.splits, order, args.waves)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sp = C_void(stream.cuda_stream)

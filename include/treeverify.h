@@ -209,14 +209,20 @@ typedef struct {
  * count and order computes the same sums, rounded differently).
  *   splits: key-axis slices per row tile, 0 = the library's choice (clamped
  *           to [1, number of 32-key chunks]);
- *   order:  batches only: TV_ORDER_AUTO (the library's choice), TV_ORDER_STATIC
- *           (workgroups take tasks in a fixed order) or TV_ORDER_PLANNED (a
+ *   order:  batches only: TV_ORDER_AUTO (the library's choice: BALANCED
+ *           when it applies and no splits are given), TV_ORDER_STATIC
+ *           (workgroups take tasks in a fixed order), TV_ORDER_PLANNED (a
  *           planner launch orders them longest first, when the plan is small
- *           enough for it);
+ *           enough for it) or TV_ORDER_BALANCED (a planner launch gives each
+ *           of 256 persistent workgroups an equal share of the batch's key
+ *           axes, cut into a few pieces at request boundaries; batches of at
+ *           most 1024 requests with at most 8 row tiles per request and KV
+ *           head, else the call falls back to the other orders; splits is
+ *           then ignored);
  *   waves:  wavefronts per workgroup of the matrix-core kernel (32 query
  *           rows each), 0 = the library's choice, else 4 or 8.
  */
-enum { TV_ORDER_AUTO = 0, TV_ORDER_STATIC = 1, TV_ORDER_PLANNED = 2 };
+enum { TV_ORDER_AUTO = 0, TV_ORDER_STATIC = 1, TV_ORDER_PLANNED = 2, TV_ORDER_BALANCED = 3 };
 typedef struct {
     int32_t splits;
     int32_t order;
@@ -253,7 +259,8 @@ tv_status tree_attn_verify_ex(const void *q, void *k_cache, const void *v_cache,
  *   [0] 1 = matrix-core kernel, 0 = vector kernel (fp32, or too few rows)
  *   [1] query rows per workgroup tile   [2] row tiles per (request, KV head)
  *   [3] key-axis slices                 [4] keys per slice
- *   [5] 1 = planned (longest-first) task order for a batch
+ *       (both 0 for the balanced order: its pieces vary in length)
+ *   [5] 1 = planned (longest-first) task order for a batch, 2 = balanced
  *   [6] chunks copied ahead of use      [7] workspace bytes without
  *       tv_attn_inputs (saturated to INT32_MAX)
  * Returns the same host-side status the call itself would for these sizes.

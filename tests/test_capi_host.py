@@ -118,10 +118,22 @@ def test_attn_plan_is_a_function_of_its_arguments(L, monkeypatch):
     p3 = BND.tree_attn_verify_plan(*sizes, splits=3)
     assert p3["splits"] == 3 and p3["keys_per_split"] * 3 >= 4096 + 128
     assert BND.tree_attn_verify_workspace_size(*sizes, splits=3) == p3["workspace_bytes"] < ws
-    # batches: planned order by default, static on request
+    # batches: balanced order by default, the others on request; fixed
+    # splits keep the sliced orders
     bsz = (8, 634, 128, 7275, 32, 8, 128, BND.TV_BF16)
-    assert BND.tree_attn_verify_plan(*bsz)["planned"] == 1
+    bal = BND.tree_attn_verify_plan(*bsz)
+    assert bal["planned"] == 2 and bal["splits"] == 0 and bal["keys_per_split"] == 0
+    assert BND.tree_attn_verify_plan(*bsz, order=BND.TV_ORDER_BALANCED) == bal
+    assert BND.tree_attn_verify_plan(*bsz, order=BND.TV_ORDER_PLANNED)["planned"] == 1
     assert BND.tree_attn_verify_plan(*bsz, order=BND.TV_ORDER_STATIC)["planned"] == 0
+    assert BND.tree_attn_verify_plan(*bsz, splits=4)["planned"] == 1
+    # beyond the balanced planner (more than 1024 requests, or more than 8
+    # row tiles per request and KV head): the longest-first order
+    assert BND.tree_attn_verify_plan(1025, 1025, 1, 64, 32, 1, 128, BND.TV_BF16)["planned"] != 2
+    assert BND.tree_attn_verify_plan(2, 2048, 1024, 64, 32, 8, 128, BND.TV_BF16,
+                                     order=BND.TV_ORDER_BALANCED)["planned"] == 1
+    # one request: the balanced order does not apply
+    assert BND.tree_attn_verify_plan(*sizes, order=BND.TV_ORDER_BALANCED) == base
 
 
 def test_attn_override_checked(L):
@@ -131,7 +143,7 @@ def test_attn_override_checked(L):
     assert L.tree_attn_verify_plan(*args, C.byref(ov), info) == OK
     assert L.tree_attn_verify_plan(*args, C.byref(ov), None) == NULL
     assert L.tree_attn_verify_plan(*args, None, info) == OK
-    bads = (BND.PlanOverride(-1, 0), BND.PlanOverride(0, 3), BND.PlanOverride(0, 0, 0, (C.c_int32 * 5)(1)),
+    bads = (BND.PlanOverride(-1, 0), BND.PlanOverride(0, 4), BND.PlanOverride(0, 0, 0, (C.c_int32 * 5)(1)),
             BND.PlanOverride(0, 0, 5), BND.PlanOverride(0, 0, 2))
     for bad in bads:
         assert L.tree_attn_verify_plan(*args, C.byref(bad), info) == SHAPE

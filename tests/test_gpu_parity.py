@@ -291,6 +291,140 @@ def test_attn_static_order_for_batches(case):
                       what=f"{case} static order")
 
 
+@pytest.mark.parametrize("case", ["c5", "batch_4_tiles", "batch_3_tiles", "batch_2_kv_heads"])
+def test_attn_planned_order_for_batches(case):
+    """Batches in the longest-first order (a planner launch sorts fixed
+    slices; the balanced order is the default): the same results."""
+    announce(f"attn planned batch order {case}")
+    if case == "c5":
+        wl = W.make_workload("c5", seed=2)
+    else:
+        parents, prefixes, hq, hkv, d, dtype = EDGE[case]
+        wl = W.make_from_trees(parents, prefixes, hq=hq, hkv=hkv, d=d, dtype=dtype, seed=4, values="qwen")
+    plan = B().tree_attn_verify_plan(wl.batch, wl.total_nodes, wl.max_nodes, wl.max_prefix, wl.hq, wl.hkv,
+                                     wl.d, B().TV_BF16, order=B().TV_ORDER_PLANNED)
+    assert plan["mfma"] == 1 and plan["planned"] == 1
+    out = run_attn(wl, order=B().TV_ORDER_PLANNED)
+    rows = sample_rows(wl, 200, 6)
+    assert_attn_close(np.stack([out[t, h] for t, h in rows]), *oracle_attn(wl, rows=rows), wl.dtype,
+                      what=f"{case} planned order")
+
+
+BALANCED = {
+    # name: (parents, prefixes, hq, hkv, d)
+    # the widest groups the balanced order takes: 8 row tiles per KV head
+    "wide_8_tiles": ([W.random_tree(np.random.default_rng(40), 512, 16),
+                      W.random_tree(np.random.default_rng(41), 100, 16),
+                      W.random_tree(np.random.default_rng(42), 300, 16)], [100, 2000, 50], 32, 8, 128),
+    # every width from 1 to 4 in one batch, and an empty request
+    "widths_1_to_4": ([W.random_tree(np.random.default_rng(43 + i), n, 16) for i, n in enumerate((30, 100, 170, 250))]
+                      + [np.zeros(0, np.int32)], [900, 40, 2500, 300, 10], 32, 8, 128),
+    # many short requests: lanes that cross several groups
+    "many_short": ([W.random_tree(np.random.default_rng(50 + i), 8 + (5 * i) % 57, 16) for i in range(40)],
+                   [(97 * i) % 400 for i in range(40)], 32, 8, 128),
+}
+
+
+def _balanced_tables(wl, plan, ws):
+    """The balanced order's plan as the device wrote it into the workspace:
+    the partial O and (m, l) slots, then {first, count} per workgroup (256),
+    the pieces {tile, first chunk, end chunk, partial slot or -1}, and
+    {first partial, count} per (request, KV head), each table at the next
+    256-byte boundary (the layout attn_mfma.hip gives the balanced plan)."""
+    up = lambda x: (x + 255) & ~255
+    R, TR, nq = plan["row_tiles"], plan["rows_per_tile"], wl.batch * wl.hkv
+    slots = (256 + nq) * R
+    rows = slots * TR
+    wg_off = up(up(rows * wl.d * 2) + rows * 8)
+    pc_off = up(wg_off + 256 * 8)
+    gr_off = up(pc_off + slots * 16)
+    assert gr_off + nq * 8 == plan["workspace_bytes"]
+    h = ws.cpu().numpy()
+    wg = h[wg_off:wg_off + 256 * 8].view(np.int32).reshape(256, 2)
+    pcs = h[pc_off:pc_off + slots * 16].view(np.int32).reshape(slots, 4)
+    grp = h[gr_off:gr_off + nq * 8].view(np.int32).reshape(nq, 2)
+    return wg, pcs, grp, slots
+
+
+@pytest.mark.parametrize("case", ["c5"] + list(BALANCED) + ["batch_4_tiles", "many_requests", "batch_2_kv_heads"])
+def test_attn_balanced_order(case):
+    """The balanced order (the default for batches), read back from the
+    workspace: every key chunk of every row tile is taken by exactly one
+    piece; a group (request, KV head) is either one piece that writes the
+    output or C pieces in the partial slots the merge reads; the row tiles of
+    one key range run as one lane on one XCD; and the lanes of a width hold
+    equal chunk counts (within one).  Then the output against the oracle."""
+    announce(f"attn balanced order {case}")
+    if case == "c5":
+        wl = W.make_workload("c5", seed=3)
+    elif case in BALANCED:
+        parents, prefixes, hq, hkv, d = BALANCED[case]
+        wl = W.make_from_trees(parents, prefixes, hq=hq, hkv=hkv, d=d, dtype="bf16", seed=5, values="qwen")
+    else:
+        parents, prefixes, hq, hkv, d, dtype = EDGE[case]
+        wl = W.make_from_trees(parents, prefixes, hq=hq, hkv=hkv, d=d, dtype=dtype, seed=5, values="qwen")
+    plan = B().tree_attn_verify_plan(wl.batch, wl.total_nodes, wl.max_nodes, wl.max_prefix, wl.hq, wl.hkv,
+                                     wl.d, B().TV_BF16)
+    assert plan["mfma"] == 1 and plan["planned"] == 2
+    ws = torch.full((plan["workspace_bytes"],), 0xA5, dtype=torch.uint8, device="cuda")  # garbage on entry
+    d = dev_workload(wl)
+    out = run_attn(wl, d, workspace=ws)
+    wg, pcs, grp, slots = _balanced_tables(wl, plan, ws)
+    R, TR, G, hkv = plan["row_tiles"], plan["rows_per_tile"], wl.hq // wl.hkv, wl.hkv
+    N = np.diff(wl.cu_nodes).astype(int)
+    P = np.asarray(wl.prefix_len).astype(int)
+    width = [-(-int(n) * G // TR) for n in N]
+    length = [-(-(int(P[b]) + int(N[b])) // 32) for b in range(wl.batch)]
+    seen = {}
+    lanes = {}
+    per_wg = {}
+    for w in range(256):
+        f, n = int(wg[w, 0]), int(wg[w, 1])
+        assert 0 <= f and n >= 0 and f + n <= slots
+        if n == 0:
+            continue
+        ws_ = set()
+        for e in range(f, f + n):
+            tile, c0, c1, ps = (int(v) for v in pcs[e])
+            q, rt = divmod(tile, R)
+            b, g = divmod(q, hkv)
+            assert 0 <= b < wl.batch and rt < width[b] and 0 <= c0 < c1 <= length[b], (w, e, pcs[e])
+            ws_.add(width[b])
+            F, C = (int(v) for v in grp[q])
+            if C == 1:
+                assert ps == -1 and (c0, c1) == (0, length[b])
+            else:
+                assert C > 1 and ps >= 0 and ps % R == rt and F <= ps // R < F + C and ps < slots
+            for ch in range(c0, c1):
+                assert (b, g, rt, ch) not in seen
+                seen[(b, g, rt, ch)] = ps
+            lanes.setdefault((q, c0, c1), []).append((rt, w))
+        assert len(ws_) == 1  # one width per workgroup
+        per_wg[w] = (ws_.pop(), sum(int(pcs[e, 2] - pcs[e, 1]) for e in range(f, f + n)))
+    want = {(b, g, rt, ch) for b in range(wl.batch) for g in range(hkv) for rt in range(width[b])
+            for ch in range(length[b])}
+    assert set(seen) == want
+    # the pieces of one group: distinct partial slots per row tile
+    for (b, g, rt), pss in itertools.groupby(sorted((k[:3], v) for k, v in seen.items()), key=lambda kv: kv[0]):
+        slots_used = {v for _, v in pss}
+        F, C = (int(v) for v in grp[b * hkv + g])
+        assert len(slots_used) == C
+    # a key range's row tiles: one workgroup each, all on one XCD when every
+    # width is a power of two (the lanes, widest first, then never straddle
+    # the 32 workgroups of an XCD)
+    pow2 = all(w & (w - 1) == 0 for w in width)
+    for (q, c0, c1), tw in lanes.items():
+        b = q // hkv
+        assert sorted(rt for rt, _ in tw) == list(range(width[b]))
+        assert len({w % 8 for _, w in tw}) == 1 or not pow2
+    for c in {v[0] for v in per_wg.values()}:
+        loads = [v[1] for v in per_wg.values() if v[0] == c]
+        assert max(loads) - min(loads) <= 1, (c, min(loads), max(loads))
+    rows = sample_rows(wl, 250, 7)
+    assert_attn_close(np.stack([out[t, h] for t, h in rows]), *oracle_attn(wl, rows=rows), wl.dtype,
+                      what=f"{case} balanced order")
+
+
 def test_attn_largest_tree():
     """1024 nodes (4096 rows per KV head, 16 mask words) over a short prefix."""
     announce("attn 1024-node tree")
@@ -352,10 +486,12 @@ def test_attn_device_error_for_inconsistent_request():
     assert int(err.item()) == (O.ERR_BAD_REQUEST << 24) | 0
 
 
-def test_attn_device_error_in_batch():
-    """A batch (planned task order) where one request's prefix_len exceeds
-    max_prefix: that request is reported and skipped, the others are computed."""
-    announce("attn device error word in a batch")
+@pytest.mark.parametrize("order", [0, 2])
+def test_attn_device_error_in_batch(order):
+    """A batch (balanced order, the default, and the longest-first order)
+    where one request's prefix_len exceeds max_prefix: that request is
+    reported and skipped, the others are computed."""
+    announce(f"attn device error word in a batch, order {order}")
     wl = W.make_workload("c5", seed=0)
     bad = int(np.argmax(wl.prefix_len))
     maxp = int(np.sort(wl.prefix_len)[-2])
@@ -363,7 +499,8 @@ def test_attn_device_error_in_batch():
     d = dev_workload(wl)
     anc, _, _, _ = B().tree_mask_build(d["parent"], d["cu"], d["P"], wl.max_nodes, wl.max_depth)
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    out = B().tree_attn_verify(d["q"], d["k"], d["v"], d["cu"], d["ks"], d["P"], anc, wl.max_nodes, maxp, err=err)
+    out = B().tree_attn_verify(d["q"], d["k"], d["v"], d["cu"], d["ks"], d["P"], anc, wl.max_nodes, maxp, err=err,
+                               order=order)
     torch.cuda.synchronize()
     assert int(err.item()) == (O.ERR_BAD_REQUEST << 24) | bad
     lo, hi = int(wl.cu_nodes[bad]), int(wl.cu_nodes[bad + 1])

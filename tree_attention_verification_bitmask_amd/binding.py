@@ -171,7 +171,7 @@ def tree_mask_build(parent, cu_nodes, prefix_len, max_nodes: int, max_depth: int
     return anc, level, pos, err
 
 
-TV_ORDER_AUTO, TV_ORDER_STATIC, TV_ORDER_PLANNED = 0, 1, 2
+TV_ORDER_AUTO, TV_ORDER_STATIC, TV_ORDER_PLANNED, TV_ORDER_BALANCED = 0, 1, 2, 3
 
 
 class PlanOverride(C.Structure):

@@ -245,6 +245,13 @@ struct KParams {
     int64_t tstride;
     int kvr32;               // min(kv_rows, INT32_MAX): bound of a table entry
     const float2 *rope_cs;   // (cos, sin) [T, D/2] to rotate q at load (or null)
+    // balanced order (attn_bal_plan_kernel), else null: each workgroup's
+    // {first piece, count}; the pieces {tile, first chunk, end chunk, partial
+    // slot or -1}; each (request, KV head)'s {first partial, count}
+    const int2 *bal_wg;
+    const int4 *bal_piece;
+    const int2 *bal_group;
+    int bal_slots;  // entries of bal_piece, and partial slots (the bound every index is checked against)
 };
 
 // Sizes of request b, with all four reads issued before any test: a chain of
@@ -347,28 +354,61 @@ __device__ __forceinline__ bool decode_task(const KParams &p, int wid, Task *t) 
     return true;
 }
 
+// One piece of work for a workgroup: row tile rt of (request b, KV head g)
+// over the keys [k_lo, k_lo + k_span), clipped to the keys the tile's nodes
+// can see.  The result goes to the output (pslot < 0) or, normalised by its
+// own sum, to partial slot pslot with its (m, l) for the merge kernel.
+struct Piece {
+    int b, g, rt, k_lo, k_span;
+    int64_t pslot;
+    bool report_bad;     // the piece that reports an invalid request b
+    bool empty_partial;  // a piece with no visible key still writes its partial (an empty one)
+};
+
+// The partial of a piece that sees no key of the tile: (m, l) = (-inf, 0) and
+// zero O for every row, so a merge that reads it adds nothing.
+template <int D, int NW, int RB>
+__device__ __forceinline__ void store_empty_partial(const KParams &p, int64_t pslot) {
+    constexpr int DB = D / 32;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int64_t unit = pslot * (NW * RB) + wave * RB + rb;
+        uint2 *po = p.ws_o + unit * (DB * 4 * 64) + lane;
+#pragma unroll
+        for (int i = 0; i < DB * 4; ++i)
+            __hip_atomic_store(reinterpret_cast<uint64_t *>(po + i * 64), 0ull, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        if (lane < 32) {
+            const uint64_t w = (uint64_t)__float_as_uint(-INFINITY);
+            __hip_atomic_store(reinterpret_cast<uint64_t *>(p.ws_ml + unit * 32 + lane), w, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
 // NW = waves per workgroup; RB = 32-row blocks per wave (two blocks share
 // every K and V operand read from LDS, halving LDS and L2 traffic per
 // product); AH = copy look-ahead in chunks (AH for long slices, fewer for
-// short ones); PAGED: K/V rows through the token table.
+// short ones); PAGED: K/V rows through the token table.  `smem` is the
+// workgroup's LDS (K/V rings, then the ancestor rows); every wave of the
+// workgroup runs the piece (the waves without rows keep the copy schedule).
 template <int D, int NW, int RB, int AH, bool PAGED>
-__global__ void __launch_bounds__(64 * NW, 1) attn_fwd_kernel(KParams p) {
+__device__ __attribute__((always_inline)) inline void attn_piece(const KParams &p, unsigned char *smem,
+                                                                 const Piece &pc, int tid) {
     using Gm = Geo<D, NW, RB>;
     constexpr int KS = Gm::kKS, DB = Gm::kDB, PW = Gm::kDmaPerWave, TR = Gm::kTileRows;
     constexpr uint32_t kHalf = Gm::kHalf;
     constexpr int BP = kBarrierPeriod;
     static_assert(AH >= BP + 1 && AH + BP <= 7, "ring safety");
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[Gm::kRingBytes + kAncBytes];
-
-    Task tk;
-    if (!decode_task(p, blockIdx.x, &tk)) return;
-    const int b = tk.b, g = tk.g, s = tk.s, rt = tk.rt;
+    const int b = pc.b, g = pc.g, rt = pc.rt;
 
     const Req rq = load_request(p, b);
     const int lo = rq.lo, n_nodes = rq.n, P = rq.P;
     const int64_t ks = rq.ks;
     if (!rq.ok) {
-        if (g == 0 && rt == 0 && s == 0 && threadIdx.x == 0) report(p.err, TV_DEVERR_BAD_REQUEST, b);
+        if (pc.report_bad && threadIdx.x == 0) report(p.err, TV_DEVERR_BAD_REQUEST, b);
         return;
     }
     const int G = p.hq / p.hkv;
@@ -379,14 +419,16 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_kernel(KParams p) {
     const int node_first = row0 / G;
     const int node_last = (row_end - 1) / G;
     const int key_end = P + node_last + 1;  // tree keys past the tile's last node are never visible
-    const int k_lo = s * p.keys_per_split;
-    if (k_lo >= key_end) return;
-    const int k_hi = min(k_lo + p.keys_per_split, key_end);
+    const int k_lo = pc.k_lo;
+    if (k_lo >= key_end) {
+        if (pc.empty_partial && pc.pslot >= 0) store_empty_partial<D, NW, RB>(p, pc.pslot);
+        return;
+    }
+    const int k_hi = min(k_lo + pc.k_span, key_end);
     const int n = (k_hi - k_lo + kChunk - 1) / kChunk;  // chunks of the slice (>= 1)
     // chunks i < c_mask lie wholly in the prefix and below k_hi: no mask
     const int c_mask = max(0, (min(P, k_hi) - k_lo) / kChunk);
 
-    const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lane = tid & 63;
     const int col = lane & 31;  // query row within the wave's 32
@@ -978,7 +1020,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_kernel(KParams p) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const float lr = halves_sum(l_run[rb]);
-        if (p.splits == 1) {
+        if (pc.pslot < 0) {
             if (!row_ok[rb]) continue;
             const float inv = 1.f / lr;
             uint16_t *orow = p.out + (((int64_t)lo + node[rb]) * p.hq + head[rb]) * D;
@@ -995,15 +1037,14 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_kernel(KParams p) {
             // Partial of this slice for one 32-row group: O / l rounded to
             // bf16 (a convex combination of V rows, so bf16 keeps its range)
             // plus the fp32 (m, l).  Lane-native layout
-            // [tile][split][row group][DB*4 x 4 bf16][64 lanes].  A row that
+            // [slot][row group][DB*4 x 4 bf16][64 lanes].  A row that
             // sees no key of the slice has l = 0 and stores zeros.  The
             // stores are relaxed atomics at agent scope, which write through
             // this XCD's L2: the merge kernel reads them from another XCD
             // anyway, and the end of this kernel then has no dirty partials
             // left to write back (measured: 1.5 us less per call at 240
             // workgroups).
-            const int tile = (b * p.hkv + g) * p.row_tiles + rt;
-            const int64_t unit = ((int64_t)tile * p.splits + s) * (NW * RB) + wave * RB + rb;
+            const int64_t unit = pc.pslot * (NW * RB) + wave * RB + rb;
             uint2 *po = p.ws_o + unit * (DB * 4 * 64) + lane;
             const float inv = lr > 0.f ? 1.f / lr : 0.f;
 #pragma unroll
@@ -1023,6 +1064,62 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_fwd_kernel(KParams p) {
                                    __HIP_MEMORY_SCOPE_AGENT);
             }
         }
+    }
+}
+
+
+// One workgroup per task of the static or planned order (decode_task).
+template <int D, int NW, int RB, int AH, bool PAGED>
+__global__ void __launch_bounds__(64 * NW, 1) attn_fwd_kernel(KParams p) {
+    using Gm = Geo<D, NW, RB>;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[Gm::kRingBytes + kAncBytes];
+    Task tk;
+    if (!decode_task(p, blockIdx.x, &tk)) return;
+    Piece pc;
+    pc.b = tk.b;
+    pc.g = tk.g;
+    pc.rt = tk.rt;
+    pc.k_lo = tk.s * p.keys_per_split;
+    pc.k_span = p.keys_per_split;
+    pc.pslot = p.splits == 1 ? -1 : ((int64_t)(tk.b * p.hkv + tk.g) * p.row_tiles + tk.rt) * p.splits + tk.s;
+    pc.report_bad = tk.g == 0 && tk.rt == 0 && tk.s == 0;
+    pc.empty_partial = false;  // (the merge skips the slices past a tile's keys)
+    attn_piece<D, NW, RB, AH, PAGED>(p, smem, pc, threadIdx.x);
+}
+
+// Balanced order: a fixed grid of kBalWgs workgroups (one per CU), each
+// running its own list of pieces one after the other (attn_bal_plan_kernel).
+// Between two pieces a barrier lets every wave finish its LDS reads of the
+// previous piece before the rings are refilled; no copy is in flight then
+// (each wave waits for all of its copies before the last chunk is read).
+constexpr int kBalWgs = 256;
+template <int D, int NW, int RB, int AH, bool PAGED>
+__global__ void __launch_bounds__(64 * NW, 1) attn_fwd_bal_kernel(KParams p) {
+    using Gm = Geo<D, NW, RB>;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[Gm::kRingBytes + kAncBytes];
+    const int2 range = p.bal_wg[blockIdx.x];
+    // (every entry is checked against the tables' bounds before use)
+    if (range.x < 0 || range.y < 0 || range.y > p.bal_slots - range.x) return;
+    for (int i = 0; i < range.y; ++i) {
+        if (i > 0) __syncthreads();
+        const int4 e = p.bal_piece[range.x + i];
+        if (e.x < 0 || e.x >= p.batch * p.hkv * p.row_tiles || e.y < 0 || e.z <= e.y || e.w >= p.bal_slots) continue;
+        const int q = e.x / p.row_tiles;
+        Piece pc;
+        pc.rt = e.x - q * p.row_tiles;
+        pc.g = q % p.hkv;
+        pc.b = q / p.hkv;
+        pc.k_lo = e.y * kChunk;
+        pc.k_span = (e.z - e.y) * kChunk;
+        pc.pslot = e.w;
+        pc.report_bad = false;  // (the planner reports invalid requests)
+        pc.empty_partial = true;
+        // (the thread id made opaque: what the piece derives from it is
+        // formed inside each piece, not hoisted out of this loop and kept
+        // live through every piece)
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        attn_piece<D, NW, RB, AH, PAGED>(p, smem, pc, tid);
     }
 }
 
@@ -1061,17 +1158,28 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
     // two memory round trips overlap.  Slices the request does not have were never written and
     // hold arbitrary bits; they are skipped by branches below, never scaled by
     // zero (0 * NaN would poison the sum).
-    const int64_t base = (int64_t)tile * p.splits;
+    // Balanced order: the tile's pieces are the partial slots
+    // (first + i) * row_tiles + rt, i < count; a tile of one piece was
+    // written whole by its piece.
+    int64_t base = (int64_t)tile * p.splits, step = 1;
+    int nbal = 0;
+    if (p.bal_group) {
+        const int2 gi = p.bal_group[tile / p.row_tiles];
+        if (gi.y <= 1 || gi.x < 0 || (int64_t)(gi.x + gi.y) * p.row_tiles > p.bal_slots) return;
+        base = (int64_t)gi.x * p.row_tiles + rt;
+        step = p.row_tiles;
+        nbal = gi.y;
+    }
     const float2 *ml = p.ws_ml + (base * nw + rg) * 32 + col;
     const uint2 *po = p.ws_o + (base * nw + rg) * (DB * 4 * 64) + (db * 4 + i4b) * 64 + lane;
-    const int64_t kMlStride = (int64_t)nw * 32;                   // per slice
-    const int64_t kOStride = (int64_t)nw * DB * 4 * 64;           // per slice
+    const int64_t kMlStride = step * nw * 32;                   // per slice
+    const int64_t kOStride = step * nw * DB * 4 * 64;           // per slice
     float2 m_l[kBatch];
     uint2 o[kBatch][I4W];
     // (one request: every tile has nearly all slices, so the early loads are
     // nearly all used; in a ragged batch short requests have few slices, and
     // the loads wait for the sizes instead)
-    const int nb0 = p.batch == 1 ? min(kBatch, p.splits) : 0;  // wave-uniform
+    const int nb0 = (p.batch == 1 && !p.bal_group) ? min(kBatch, p.splits) : 0;  // wave-uniform
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
         m_l[u] = u < nb0 ? ml[u * kMlStride] : make_float2(-INFINITY, 0.f);
@@ -1088,7 +1196,7 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
     if (row0 + rg * 32 >= rows_b) return;  // (wave-uniform) no rows in this group
     const int row_end = min(rows_b, row0 + p.tile_rows);
     const int key_end = P + (row_end - 1) / G + 1;
-    const int nsplit = min(p.splits, (key_end + p.keys_per_split - 1) / p.keys_per_split);
+    const int nsplit = p.bal_group ? nbal : min(p.splits, (key_end + p.keys_per_split - 1) / p.keys_per_split);
     const int r = row0 + rg * 32 + col;
 
     float M = -INFINITY, L = 0.f;
@@ -1292,6 +1400,304 @@ __global__ void __launch_bounds__(kPlanThreads) attn_plan_kernel(KParams p, int 
     }
 }
 
+
+// Balanced plan for batches (TV_ORDER_BALANCED).  The work of a group
+// (request b, KV head g) is its R_b row tiles (R_b = ceil(N_b G / tile rows))
+// over L_b chunks (the last tile's keys; the others see a few less).  The
+// R_b tiles of one key range read the same K/V, so they run together on R_b
+// workgroups of one XCD, a "lane" of width R_b.  Groups of equal width form a
+// class; class c gets x_c lanes of width c, with x_c proportional to its
+// chunks W_c, so that every lane has W_c / x_c chunks, the same for every
+// class, and the lanes fill the kBalWgs workgroups.  Lane i of class c takes
+// the chunks [i W_c / x_c, (i + 1) W_c / x_c) of the class's groups laid end
+// to end (requests in order, KV heads within a request): one piece per group
+// the range meets, usually one or two.  A group cut into several pieces has
+// partials (C pieces in partial slots F .. F + C - 1, each times R_max plus the
+// row tile); a group left whole writes its output directly.  Piece numbers
+// F = (pieces before class c) + i + rank of the group in its class are unique:
+// along a class both the lane and the group rank only grow, one of them at
+// every cut.  Workgroup ids: lane l of the kBalWgs is id (l / 32) + 8 (l % 32)
+// (32 consecutive lanes per XCD, so a lane's tiles share that XCD's L2).
+// One thread per request (batch <= kBalThreads), then one per lane.
+constexpr int kBalThreads = 1024;
+constexpr int kBalMaxWidth = 8;  // row tiles per group the balanced plan takes
+constexpr int kBalMaxChunks = 1 << 22;  // chunks of all groups together (32-bit plan arithmetic)
+constexpr int kBalWaves = kBalThreads / 64;
+
+__device__ __forceinline__ int bal_wg_of_lane(int l) { return (l >> 5) + 8 * (l & 31); }
+
+// n / d for 0 <= n < 2^31, d > 0 and a quotient below 2^22, from the float
+// reciprocal of d (relative error 2^-23, so the estimate is off by at most
+// one) and one correction each way.
+__device__ __forceinline__ int bal_div(int n, int d, float inv_d) {
+    int q = (int)((float)n * inv_d);
+    if ((q + 1) * d <= n) ++q;
+    else if (q * d > n) --q;
+    return q;
+}
+
+// Lane of class position x (0 <= x < W): the largest i with i W / lanes <= x.
+// (W <= kBalMaxChunks and lanes <= kBalWgs: every product fits 31 bits.)
+__device__ __forceinline__ int bal_lane_of(int x, int W, float inv_W, int lanes) {
+    return bal_div((x + 1) * lanes - 1, W, inv_W);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within each row of
+// 16 lanes, then the row totals broadcast to the rows after them (DPP moves,
+// no LDS round trip).
+__device__ __forceinline__ int bal_wave_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false); // row_bcast:15 -> rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false); // row_bcast:31 -> rows 2, 3
+    return x;
+}
+
+__global__ void __launch_bounds__(kBalThreads) attn_bal_plan_kernel(KParams p, int2 *__restrict__ wg,
+                                                                     int4 *__restrict__ piece,
+                                                                     int2 *__restrict__ grp) {
+    constexpr int NC = kBalMaxWidth + 1;  // classes 1 .. kBalMaxWidth (0: no work)
+    __shared__ int s_cls[kBalThreads], s_len[kBalThreads];
+    __shared__ int s_rank[kBalThreads], s_off[kBalThreads];  // by request: rank and first chunk in its class
+    __shared__ int s_plen[kBalThreads], s_porder[kBalThreads], s_first[kBalThreads];  // by class position
+    __shared__ int s_wcnt[kBalWaves][NC];
+    __shared__ int s_wsum[kBalWaves][NC];
+    __shared__ int s_cnt[NC], s_W[NC], s_x[NC], s_cstart[NC], s_sbase[NC], s_lane0[NC], s_pbase[NC];
+    __shared__ int s_nlanes;
+    __shared__ int s_wtot[kBalWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int R = p.row_tiles, hkv = p.hkv, G = p.hq / p.hkv;
+
+    // (1) each request's class (row tiles) and length (chunks of its last
+    // tile); within the wave, the requests of its class before it (ballot)
+    // and their chunks (prefix sum)
+    const int b = tid;
+    int cls = 0, len = 0;
+    if (b < p.batch) {
+        const Req rq = load_request(p, b);
+        if (!rq.ok) {
+            report(p.err, TV_DEVERR_BAD_REQUEST, b);
+        } else if (rq.n > 0) {
+            cls = (rq.n * G + p.tile_rows - 1) / p.tile_rows;
+            len = (rq.P + rq.n + kChunk - 1) / kChunk;
+        }
+    }
+    for (int i = tid; i < kBalWgs; i += kBalThreads) wg[i] = make_int2(0, 0);
+    const uint64_t below = (1ull << lane) - 1ull;
+    int rank_b = 0, off_b = 0;
+#pragma unroll
+    for (int c = 1; c < NC; ++c) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(cls == c);
+        int incl = 0;
+        if (m != 0) {  // (wave-uniform)
+            const int xv = cls == c ? len : 0;
+            incl = bal_wave_scan(xv);
+            if (cls == c) {
+                rank_b = __builtin_popcountll(m & below);
+                off_b = incl - xv;
+            }
+        }
+        if (lane == 63) {
+            s_wcnt[wv][c] = __builtin_popcountll(m);
+            s_wsum[wv][c] = incl;
+        }
+    }
+    __syncthreads();
+    // (2) across waves: the class totals, and each request's rank and first
+    // chunk in its class
+    if (tid > 0 && tid < NC) {
+        int cnt = 0, sum = 0;
+#pragma unroll
+        for (int w = 0; w < kBalWaves; ++w) {
+            cnt += s_wcnt[w][tid];
+            sum += s_wsum[w][tid];
+        }
+        s_cnt[tid] = cnt;
+        s_W[tid] = sum * hkv;  // chunks of the class: every KV head of each request
+    }
+    if (cls > 0) {
+#pragma unroll
+        for (int w = 0; w < kBalWaves - 1; ++w)
+            if (w < wv) {
+                rank_b += s_wcnt[w][cls];
+                off_b += s_wsum[w][cls];
+            }
+    }
+    s_cls[tid] = cls;
+    s_len[tid] = len;
+    s_rank[tid] = rank_b;
+    s_off[tid] = off_b * hkv;  // the request's groups start here in its class
+    __syncthreads();
+    // (3) wave 0: lanes per class (the floor of each class's share, at least
+    // one, then one more for each class whose remainder is at least a half
+    // while lanes are left), laid out widest class first.  Meanwhile the
+    // requests take their positions in class order.
+    if (wv == 0) {
+        int W[NC], x[NC];
+        float frac[NC];
+        int wtot = 0, used = 0;
+#pragma unroll
+        for (int c = 1; c < NC; ++c) {
+            W[c] = s_W[c];
+            wtot += W[c] * c;
+        }
+        const float share = (float)kBalWgs / (float)max(wtot, 1);
+#pragma unroll
+        for (int c = 1; c < NC; ++c) {
+            x[c] = 0;
+            frac[c] = 0.f;
+            if (W[c] > 0) {
+                const float y = (float)W[c] * share;
+                int xi = (int)y;
+                frac[c] = y - (float)xi;
+                xi = max(1, min(xi, W[c]));
+                x[c] = xi;
+                used += xi * c;
+            }
+        }
+        // (the floor of one lane per class may overshoot: 8 classes of
+        // widths 1 .. 8 need 36 workgroups, so this ends)
+        while (used > kBalWgs) {
+            int best = 0, bx = 0;
+#pragma unroll
+            for (int c = 1; c < NC; ++c)
+                if (x[c] > 1 && x[c] * c > bx) {
+                    best = c;
+                    bx = x[c] * c;
+                }
+#pragma unroll
+            for (int c = 1; c < NC; ++c)
+                if (c == best) --x[c];
+            used -= best;
+        }
+#pragma unroll
+        for (int c = NC - 1; c >= 1; --c)
+            if (frac[c] >= 0.5f && c <= kBalWgs - used && x[c] > 0 && x[c] < W[c]) {
+                ++x[c];
+                used += c;
+            }
+        if (lane == 0) {
+            int l0 = 0, sb = 0, pb = 0;
+#pragma unroll
+            for (int c = NC - 1; c >= 1; --c) {
+                s_x[c] = x[c];
+                s_lane0[c] = l0;
+                s_sbase[c] = sb;
+                s_pbase[c] = pb;
+                l0 += x[c] * c;
+                sb += x[c];
+                pb += x[c] + s_cnt[c] * hkv;
+            }
+            s_nlanes = sb;
+        }
+    }
+    if (cls > 0) {
+        int cst = 0;
+#pragma unroll
+        for (int c = 1; c < NC; ++c)
+            if (c < cls) cst += s_cnt[c];
+        s_porder[cst + rank_b] = b;
+        s_plen[cst + rank_b] = len;
+        s_first[cst + rank_b] = off_b * hkv;
+    }
+    if (tid > 0 && tid < NC) {
+        int cst = 0;
+#pragma unroll
+        for (int c = 1; c < NC; ++c)
+            if (c < tid) cst += s_cnt[c];
+        s_cstart[tid] = cst;
+    }
+    __syncthreads();
+    // (4) each group's pieces, for the merge: one thread per group
+    for (int q = tid; q < p.batch * hkv; q += kBalThreads) {
+        const int rb = q / hkv, g = q - rb * hkv;
+        const int c = s_cls[rb];
+        int2 gi = make_int2(0, 0);
+        if (c > 0) {
+            const int Wc = s_W[c], xc = s_x[c];
+            const int lb = s_len[rb];
+            const int o = s_off[rb] + g * lb;
+            const float inv = 1.f / (float)Wc;
+            const int i0 = bal_lane_of(o, Wc, inv, xc);
+            const int i1 = bal_lane_of(o + lb - 1, Wc, inv, xc);
+            gi = make_int2(s_pbase[c] + i0 + s_rank[rb] * hkv + g, i1 - i0 + 1);
+        }
+        grp[q] = gi;
+    }
+    // (5) one thread per lane: its pieces, counted, then written after a scan
+    // of the counts (times the lane's width) gives each lane its entries
+    const int nl = s_nlanes;
+    int c = 0, i = 0, count = 0, pos0 = 0, A = 0, E = 0, Wc = 1, xc = 1, cs0 = 0, ncls = 0, pb0 = 0, l00 = 0;
+    if (tid < nl) {
+#pragma unroll
+        for (int cc = 1; cc < NC; ++cc) {
+            const int xcc = s_x[cc], sb = s_sbase[cc];
+            if (xcc > 0 && tid >= sb && tid < sb + xcc) c = cc;
+        }
+        Wc = s_W[c];
+        xc = s_x[c];
+        i = tid - s_sbase[c];
+        cs0 = s_cstart[c];
+        pb0 = s_pbase[c];
+        l00 = s_lane0[c];
+        ncls = s_cnt[c];
+        const float inv_x = 1.f / (float)xc;
+        A = bal_div(i * Wc, xc, inv_x);
+        E = bal_div((i + 1) * Wc, xc, inv_x);
+        // the request holding chunk A: the last position whose first chunk <= A
+        int lo = cs0, hi = cs0 + ncls - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_first[mid] <= A) lo = mid;
+            else hi = mid - 1;
+        }
+        pos0 = lo;
+        // count the groups [A, E) meets
+        int pos = pos0, xx = A;
+        while (xx < E) {
+            const int lb = s_plen[pos];
+            const int gstart = s_first[pos];
+            const int g = bal_div(xx - gstart, lb, 1.f / (float)lb);
+            const int gend = gstart + (g + 1) * lb;
+            xx = min(E, gend);
+            ++count;
+            if (g + 1 == hkv && xx == gend) ++pos;
+        }
+    }
+    // entries of the lanes before this one: a scan of count * width
+    const int v = tid < nl ? count * c : 0;
+    const int incl = bal_wave_scan(v);
+    if (lane == 63) s_wtot[wv] = incl;
+    __syncthreads();
+    if (tid < nl) {
+        int ebase = incl - v;
+        for (int w = 0; w < wv; ++w) ebase += s_wtot[w];
+        for (int rt = 0; rt < c; ++rt) wg[bal_wg_of_lane(l00 + i * c + rt)] = make_int2(ebase + rt * count, count);
+        const float inv_W = 1.f / (float)Wc;
+        int pos = pos0, j = 0, xx = A;
+        while (xx < E) {
+            const int lb = s_plen[pos];
+            const int gstart = s_first[pos];
+            const int g = bal_div(xx - gstart, lb, 1.f / (float)lb);
+            const int o = gstart + g * lb;
+            const int gend = o + lb;
+            const int xe = min(E, gend);
+            const int i0 = bal_lane_of(o, Wc, inv_W, xc);
+            const int i1 = bal_lane_of(gend - 1, Wc, inv_W, xc);
+            // the group's rank in its class: requests before it times hkv, plus g
+            const int pi = pb0 + i + (pos - cs0) * hkv + g;
+            const int q = s_porder[pos] * hkv + g;
+            for (int rt = 0; rt < c; ++rt)
+                piece[ebase + rt * count + j] = make_int4(q * R + rt, xx - o, xe - o, i1 > i0 ? pi * R + rt : -1);
+            xx = xe;
+            ++j;
+            if (g + 1 == hkv && xx == gend) ++pos;
+        }
+    }
+}
+
 }  // namespace
 
 MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefix, int hq, int hkv,
@@ -1326,6 +1732,30 @@ MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefi
     // tests) may fix the slice count or the batch order instead.
     const long planned = (long)batch * hkv * plan.row_tiles;  // tasks per slice
     const int order = ov ? ov->order : TV_ORDER_AUTO;
+    // Batches: the balanced order (equal shares of the key axis per
+    // workgroup, see attn_bal_plan_kernel) unless the override fixes the
+    // slices or another order, or the batch is beyond its planner.
+    const bool bal_fits = batch <= kBalThreads && plan.row_tiles <= kBalMaxWidth &&
+                          (long)batch * hkv * chunks <= kBalMaxChunks &&
+                          ((long)kBalWgs + (long)batch * hkv) * plan.row_tiles <= INT32_MAX;
+    if (batch > 1 && bal_fits &&
+        (order == TV_ORDER_BALANCED || (order == TV_ORDER_AUTO && !(ov && ov->splits > 0)))) {
+        plan.balanced = true;
+        plan.splits = 0;
+        plan.keys_per_split = 0;
+        const size_t slots = ((size_t)kBalWgs + (size_t)batch * hkv) * plan.row_tiles;
+        const size_t rows = slots * plan.rows_per_tile;
+        auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+        size_t off = up(rows * head_dim * sizeof(uint16_t));  // partial O
+        off = up(off + rows * sizeof(float2));                 // partial (m, l)
+        plan.bal_wg_off = off;
+        off = up(off + (size_t)kBalWgs * sizeof(int2));
+        plan.bal_piece_off = off;
+        off = up(off + slots * sizeof(int4));
+        plan.bal_group_off = off;
+        plan.ws_bytes = off + (size_t)batch * hkv * sizeof(int2);
+        return plan;
+    }
     const bool can_plan = batch > 1 && order != TV_ORDER_STATIC;
     const long target = batch == 1 ? 256 : (can_plan ? 1024 : 640);
     int splits = (int)((target + base_tasks - 1) / base_tasks);
@@ -1357,6 +1787,7 @@ MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefi
 }
 
 int attn_mfma_lookahead(const MfmaPlan &plan) {
+    if (plan.balanced) return kAhead;
     return plan.keys_per_split / kChunk <= kShortSlice ? kAheadShort : kAhead;
 }
 
@@ -1370,6 +1801,15 @@ void launch_fwd_t(const KParams &p, const MfmaPlan &plan, long grid, hipStream_t
 }
 template <int D, int NW, int RB>
 void launch_fwd(const KParams &p, const MfmaPlan &plan, long grid, hipStream_t stream) {
+    if (plan.balanced) {
+        if (p.table)
+            hipLaunchKernelGGL((attn_fwd_bal_kernel<D, NW, RB, kAhead, true>), dim3(kBalWgs), dim3(64 * NW), 0,
+                               stream, p);
+        else
+            hipLaunchKernelGGL((attn_fwd_bal_kernel<D, NW, RB, kAhead, false>), dim3(kBalWgs), dim3(64 * NW), 0,
+                               stream, p);
+        return;
+    }
     if (p.table) launch_fwd_t<D, NW, RB, true>(p, plan, grid, stream);
     else launch_fwd_t<D, NW, RB, false>(p, plan, grid, stream);
 }
@@ -1407,7 +1847,25 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *works
     p.ws_o = nullptr;
     p.ws_ml = nullptr;
     p.task_table = nullptr;
-    if (plan.splits > 1) {
+    p.bal_wg = nullptr;
+    p.bal_piece = nullptr;
+    p.bal_group = nullptr;
+    p.bal_slots = 0;
+    if (plan.balanced) {
+        const size_t rows = ((size_t)kBalWgs + (size_t)a.batch * a.hkv) * plan.row_tiles * plan.rows_per_tile;
+        const size_t off = (rows * a.head_dim * sizeof(uint16_t) + 255) & ~(size_t)255;
+        char *ws = (char *)workspace;
+        p.ws_o = (uint2 *)ws;
+        p.ws_ml = (float2 *)(ws + off);
+        int2 *wg = (int2 *)(ws + plan.bal_wg_off);
+        int4 *piece = (int4 *)(ws + plan.bal_piece_off);
+        int2 *grp = (int2 *)(ws + plan.bal_group_off);
+        p.bal_slots = (int)(((size_t)kBalWgs + (size_t)a.batch * a.hkv) * plan.row_tiles);
+        hipLaunchKernelGGL(attn_bal_plan_kernel, dim3(1), dim3(kBalThreads), 0, stream, p, wg, piece, grp);
+        p.bal_wg = wg;
+        p.bal_piece = piece;
+        p.bal_group = grp;
+    } else if (plan.splits > 1) {
         const size_t rows = (size_t)a.batch * a.hkv * plan.row_tiles * plan.splits * plan.rows_per_tile;
         size_t off = rows * a.head_dim * sizeof(uint16_t);
         off = (off + 255) & ~(size_t)255;
@@ -1426,22 +1884,24 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *works
     }
     const long tiles = (long)a.batch * a.hkv * plan.row_tiles;
     // few slices: one merge wave covers all four float4 slots of its channels
-    const bool wide = plan.splits <= 8;
+    // (the balanced order cuts a group into a few pieces)
+    const bool wide = plan.balanced || plan.splits <= 8;
+    const bool merge = plan.balanced || plan.splits > 1;
     const long cwaves = tiles * (plan.rows_per_tile / 32) * (a.head_dim / 32) * (wide ? 1 : 4);
     const long cblocks = (cwaves + kCombineWaves - 1) / kCombineWaves;
     if (a.head_dim == 128) {
         if (plan.waves == 8) launch_fwd<128, 8, 1>(p, plan, grid, stream);
         else launch_fwd<128, 4, 1>(p, plan, grid, stream);
-        if (plan.splits > 1 && wide)
+        if (merge && wide)
             hipLaunchKernelGGL((attn_combine_kernel<128, 4>), dim3(cblocks), dim3(64 * kCombineWaves), 0, stream, p);
-        else if (plan.splits > 1)
+        else if (merge)
             hipLaunchKernelGGL((attn_combine_kernel<128, 1>), dim3(cblocks), dim3(64 * kCombineWaves), 0, stream, p);
     } else {
         if (plan.waves == 8) launch_fwd<64, 8, 1>(p, plan, grid, stream);
         else launch_fwd<64, 4, 1>(p, plan, grid, stream);
-        if (plan.splits > 1 && wide)
+        if (merge && wide)
             hipLaunchKernelGGL((attn_combine_kernel<64, 4>), dim3(cblocks), dim3(64 * kCombineWaves), 0, stream, p);
-        else if (plan.splits > 1)
+        else if (merge)
             hipLaunchKernelGGL((attn_combine_kernel<64, 1>), dim3(cblocks), dim3(64 * kCombineWaves), 0, stream, p);
     }
     return hipGetLastError();

@@ -59,7 +59,7 @@ bool override_ok(const tv_attn_plan_override *ov) {
     if (!ov) return true;
     for (int i = 0; i < 5; ++i)
         if (ov->reserved[i] != 0) return false;
-    return ov->splits >= 0 && ov->order >= TV_ORDER_AUTO && ov->order <= TV_ORDER_PLANNED &&
+    return ov->splits >= 0 && ov->order >= TV_ORDER_AUTO && ov->order <= TV_ORDER_BALANCED &&
            (ov->waves == 0 || ov->waves == 4 || ov->waves == 8);
 }
 
@@ -277,7 +277,7 @@ tv_status tree_attn_verify_plan(int32_t batch, int32_t total_nodes, int32_t max_
     info[2] = plan.use ? plan.row_tiles : 0;
     info[3] = plan.use ? plan.splits : 0;
     info[4] = plan.use ? plan.keys_per_split : 0;
-    info[5] = plan.use && plan.table ? 1 : 0;
+    info[5] = plan.use ? (plan.balanced ? 2 : plan.table ? 1 : 0) : 0;
     info[6] = plan.use ? tv::attn_mfma_lookahead(plan) : 0;
     info[7] = plan.use ? (int32_t)(plan.ws_bytes > (size_t)INT32_MAX ? INT32_MAX : plan.ws_bytes) : 0;
     return TV_OK;

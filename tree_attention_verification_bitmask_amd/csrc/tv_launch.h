@@ -114,6 +114,8 @@ struct MfmaPlan {
     bool table = false;     // batches: workgroups take their task from a planned table
     int table_slots = 0;    // workgroups launched on the table path
     size_t table_off = 0;   // byte offset of the table in the workspace
+    bool balanced = false;  // batches: equal key-axis shares per workgroup, persistent workgroups
+    size_t bal_wg_off = 0, bal_piece_off = 0, bal_group_off = 0;  // byte offsets of its tables
     size_t ws_bytes = 0;
 };
 // ov may be null (the library's own plan).
