@@ -352,8 +352,12 @@ def test_attn_balanced_order(case):
     workspace: every key chunk of every row tile is taken by exactly one
     piece; a group (request, KV head) is either one piece that writes the
     output or C pieces in the partial slots the merge reads; the row tiles of
-    one key range run as one lane on one XCD; and the lanes of a width hold
-    equal chunk counts (within one).  Then the output against the oracle."""
+    one key range run as one lane on one XCD; and the lanes of a width carry
+    equal loads, counting each chunk as one position and each piece that
+    starts a group as four more (its prologue); a lane may hold part of a
+    group's four without its first chunk, so the count is exact to within
+    four each way, and the lanes' loads differ by at most 2 * 4 + 1.  Then
+    the output against the oracle."""
     announce(f"attn balanced order {case}")
     if case == "c5":
         wl = W.make_workload("c5", seed=3)
@@ -400,7 +404,7 @@ def test_attn_balanced_order(case):
                 seen[(b, g, rt, ch)] = ps
             lanes.setdefault((q, c0, c1), []).append((rt, w))
         assert len(ws_) == 1  # one width per workgroup
-        per_wg[w] = (ws_.pop(), sum(int(pcs[e, 2] - pcs[e, 1]) for e in range(f, f + n)))
+        per_wg[w] = (ws_.pop(), sum(int(pcs[e, 2] - pcs[e, 1]) + 4 * (int(pcs[e, 1]) == 0) for e in range(f, f + n)))
     want = {(b, g, rt, ch) for b in range(wl.batch) for g in range(hkv) for rt in range(width[b])
             for ch in range(length[b])}
     assert set(seen) == want
@@ -419,7 +423,7 @@ def test_attn_balanced_order(case):
         assert len({w % 8 for _, w in tw}) == 1 or not pow2
     for c in {v[0] for v in per_wg.values()}:
         loads = [v[1] for v in per_wg.values() if v[0] == c]
-        assert max(loads) - min(loads) <= 1, (c, min(loads), max(loads))
+        assert max(loads) - min(loads) <= 9, (c, min(loads), max(loads))
     rows = sample_rows(wl, 250, 7)
     assert_attn_close(np.stack([out[t, h] for t, h in rows]), *oracle_attn(wl, rows=rows), wl.dtype,
                       what=f"{case} balanced order")

@@ -1177,9 +1177,10 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
     float2 m_l[kBatch];
     uint2 o[kBatch][I4W];
     // (one request: every tile has nearly all slices, so the early loads are
-    // nearly all used; in a ragged batch short requests have few slices, and
-    // the loads wait for the sizes instead)
-    const int nb0 = (p.batch == 1 && !p.bal_group) ? min(kBatch, p.splits) : 0;  // wave-uniform
+    // nearly all used; the balanced order knows the tile's piece count from
+    // its group record; in a ragged batch in the other orders short requests
+    // have few slices, and the loads wait for the sizes instead)
+    const int nb0 = p.bal_group ? min(kBatch, nbal) : (p.batch == 1 ? min(kBatch, p.splits) : 0);  // wave-uniform
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
         m_l[u] = u < nb0 ? ml[u * kMlStride] : make_float2(-INFINITY, 0.f);
@@ -1406,22 +1407,29 @@ __global__ void __launch_bounds__(kPlanThreads) attn_plan_kernel(KParams p, int 
 // over L_b chunks (the last tile's keys; the others see a few less).  The
 // R_b tiles of one key range read the same K/V, so they run together on R_b
 // workgroups of one XCD, a "lane" of width R_b.  Groups of equal width form a
-// class; class c gets x_c lanes of width c, with x_c proportional to its
-// chunks W_c, so that every lane has W_c / x_c chunks, the same for every
-// class, and the lanes fill the kBalWgs workgroups.  Lane i of class c takes
-// the chunks [i W_c / x_c, (i + 1) W_c / x_c) of the class's groups laid end
-// to end (requests in order, KV heads within a request): one piece per group
-// the range meets, usually one or two.  A group cut into several pieces has
-// partials (C pieces in partial slots F .. F + C - 1, each times R_max plus the
-// row tile); a group left whole writes its output directly.  Piece numbers
-// F = (pieces before class c) + i + rank of the group in its class are unique:
-// along a class both the lane and the group rank only grow, one of them at
-// every cut.  Workgroup ids: lane l of the kBalWgs is id (l / 32) + 8 (l % 32)
+// class; laid end to end (requests in order, KV heads within a request), each
+// group takes kBalPieceCost positions (its piece's prologue) and then one
+// position per chunk.  Class c gets x_c lanes of width c, x_c in proportion to
+// its positions W_c, so that every lane has W_c / x_c positions, the same for
+// every class, and the lanes fill the kBalWgs workgroups.  Lane i of class c
+// takes the chunks whose positions lie in [i W_c / x_c, (i + 1) W_c / x_c):
+// one piece per group with such chunks, usually one or two.  A group cut into
+// several pieces has partials (C pieces in partial slots F .. F + C - 1, each
+// times R_max plus the row tile); a group left whole writes its output
+// directly.  Piece numbers F = (pieces before class c) + i + rank of the group
+// in its class are unique: along a class both the lane and the group rank
+// only grow, one of them at every cut.  A lane holds at least one position,
+// so the lanes between a group's first and last chunk all hold some of its
+// chunks.  Workgroup ids: lane l of the kBalWgs is id (l / 32) + 8 (l % 32)
 // (32 consecutive lanes per XCD, so a lane's tiles share that XCD's L2).
 // One thread per request (batch <= kBalThreads), then one per lane.
 constexpr int kBalThreads = 1024;
 constexpr int kBalMaxWidth = 8;  // row tiles per group the balanced plan takes
-constexpr int kBalMaxChunks = 1 << 22;  // chunks of all groups together (32-bit plan arithmetic)
+constexpr int kBalMaxChunks = 1 << 22;  // positions of all groups together (32-bit plan arithmetic)
+// Each group's range opens with this many positions that hold no chunk: the
+// cost of a piece's prologue (about 5 us, four chunks of a full tile), so a
+// lane that starts a second piece takes that many fewer chunks.
+constexpr int kBalPieceCost = 4;
 constexpr int kBalWaves = kBalThreads / 64;
 
 __device__ __forceinline__ int bal_wg_of_lane(int l) { return (l >> 5) + 8 * (l & 31); }
@@ -1484,6 +1492,7 @@ __global__ void __launch_bounds__(kBalThreads) attn_bal_plan_kernel(KParams p, i
             len = (rq.P + rq.n + kChunk - 1) / kChunk;
         }
     }
+    const int span = cls > 0 ? len + kBalPieceCost : 0;  // positions of each of its groups
     for (int i = tid; i < kBalWgs; i += kBalThreads) wg[i] = make_int2(0, 0);
     const uint64_t below = (1ull << lane) - 1ull;
     int rank_b = 0, off_b = 0;
@@ -1492,7 +1501,7 @@ __global__ void __launch_bounds__(kBalThreads) attn_bal_plan_kernel(KParams p, i
         const uint64_t m = __builtin_amdgcn_ballot_w64(cls == c);
         int incl = 0;
         if (m != 0) {  // (wave-uniform)
-            const int xv = cls == c ? len : 0;
+            const int xv = cls == c ? span : 0;
             incl = bal_wave_scan(xv);
             if (cls == c) {
                 rank_b = __builtin_popcountll(m & below);
@@ -1515,7 +1524,7 @@ __global__ void __launch_bounds__(kBalThreads) attn_bal_plan_kernel(KParams p, i
             sum += s_wsum[w][tid];
         }
         s_cnt[tid] = cnt;
-        s_W[tid] = sum * hkv;  // chunks of the class: every KV head of each request
+        s_W[tid] = sum * hkv;  // positions of the class: every KV head of each request
     }
     if (cls > 0) {
 #pragma unroll
@@ -1618,7 +1627,7 @@ __global__ void __launch_bounds__(kBalThreads) attn_bal_plan_kernel(KParams p, i
         if (c > 0) {
             const int Wc = s_W[c], xc = s_x[c];
             const int lb = s_len[rb];
-            const int o = s_off[rb] + g * lb;
+            const int o = s_off[rb] + g * (lb + kBalPieceCost) + kBalPieceCost;  // the group's first chunk
             const float inv = 1.f / (float)Wc;
             const int i0 = bal_lane_of(o, Wc, inv, xc);
             const int i1 = bal_lane_of(o + lb - 1, Wc, inv, xc);
@@ -1657,12 +1666,15 @@ __global__ void __launch_bounds__(kBalThreads) attn_bal_plan_kernel(KParams p, i
         // count the groups [A, E) meets
         int pos = pos0, xx = A;
         while (xx < E) {
-            const int lb = s_plen[pos];
+            const int lb = s_plen[pos] + kBalPieceCost;
             const int gstart = s_first[pos];
             const int g = bal_div(xx - gstart, lb, 1.f / (float)lb);
-            const int gend = gstart + (g + 1) * lb;
-            xx = min(E, gend);
-            ++count;
+            const int o = gstart + g * lb;
+            const int gend = o + lb;
+            const int xe = min(E, gend);
+            // chunks whose position lies in [xx, xe)
+            count += max(xx - o - kBalPieceCost, 0) < xe - o - kBalPieceCost;
+            xx = xe;
             if (g + 1 == hkv && xx == gend) ++pos;
         }
     }
@@ -1678,21 +1690,25 @@ __global__ void __launch_bounds__(kBalThreads) attn_bal_plan_kernel(KParams p, i
         const float inv_W = 1.f / (float)Wc;
         int pos = pos0, j = 0, xx = A;
         while (xx < E) {
-            const int lb = s_plen[pos];
+            const int len_g = s_plen[pos];
+            const int lb = len_g + kBalPieceCost;
             const int gstart = s_first[pos];
             const int g = bal_div(xx - gstart, lb, 1.f / (float)lb);
-            const int o = gstart + g * lb;
+            const int o = gstart + g * lb;  // the group's positions: kBalPieceCost, then its chunks
             const int gend = o + lb;
             const int xe = min(E, gend);
-            const int i0 = bal_lane_of(o, Wc, inv_W, xc);
-            const int i1 = bal_lane_of(gend - 1, Wc, inv_W, xc);
-            // the group's rank in its class: requests before it times hkv, plus g
-            const int pi = pb0 + i + (pos - cs0) * hkv + g;
-            const int q = s_porder[pos] * hkv + g;
-            for (int rt = 0; rt < c; ++rt)
-                piece[ebase + rt * count + j] = make_int4(q * R + rt, xx - o, xe - o, i1 > i0 ? pi * R + rt : -1);
+            const int c0 = max(xx - o - kBalPieceCost, 0), c1 = xe - o - kBalPieceCost;
+            if (c0 < c1) {
+                const int i0 = bal_lane_of(o + kBalPieceCost, Wc, inv_W, xc);
+                const int i1 = bal_lane_of(gend - 1, Wc, inv_W, xc);
+                // the group's rank in its class: requests before it times hkv, plus g
+                const int pi = pb0 + i + (pos - cs0) * hkv + g;
+                const int q = s_porder[pos] * hkv + g;
+                for (int rt = 0; rt < c; ++rt)
+                    piece[ebase + rt * count + j] = make_int4(q * R + rt, c0, c1, i1 > i0 ? pi * R + rt : -1);
+                ++j;
+            }
             xx = xe;
-            ++j;
             if (g + 1 == hkv && xx == gend) ++pos;
         }
     }
@@ -1736,7 +1752,7 @@ MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefi
     // workgroup, see attn_bal_plan_kernel) unless the override fixes the
     // slices or another order, or the batch is beyond its planner.
     const bool bal_fits = batch <= kBalThreads && plan.row_tiles <= kBalMaxWidth &&
-                          (long)batch * hkv * chunks <= kBalMaxChunks &&
+                          (long)batch * hkv * (chunks + kBalPieceCost) <= kBalMaxChunks &&
                           ((long)kBalWgs + (long)batch * hkv) * plan.row_tiles <= INT32_MAX;
     if (batch > 1 && bal_fits &&
         (order == TV_ORDER_BALANCED || (order == TV_ORDER_AUTO && !(ov && ov->splits > 0)))) {
