@@ -49,6 +49,7 @@ import ctypes
 import csv
 import glob
 import hashlib
+import re
 import json
 import math
 import os
@@ -68,7 +69,10 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3
 METRIC = "verified tree-tokens/sec per GPU; % of HBM-BW / bf16-MFMA roofline"
 COLD_BYTES = 512 << 20
 ATTN_SOURCES = ("tree_attention_verification_bitmask_amd/csrc/attn_mfma.hip",)
-ATTN_KERNELS = ("attn_fwd_kernel", "attn_combine_kernel", "attn_plan_kernel")
+# the main kernel of a call (one of them runs per call), then the others a
+# call may run: the merge and the batch planners
+ATTN_MAIN_KERNELS = ("attn_fwd_kernel", "attn_fwd_bal_kernel")
+ATTN_KERNELS = ATTN_MAIN_KERNELS + ("attn_combine_kernel", "attn_plan_kernel", "attn_bal_plan_kernel")
 
 
 def attn_source_hash() -> str:
@@ -107,10 +111,13 @@ def ingest_traffic(workload: str, fetch_dir: str, write_dir: str, calib_mib: int
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _counter_rows(d) if r["Counter_Name"] == counter]
-        per_kernel = {k: [float(r["Counter_Value"]) for r in rows if k in r["Kernel_Name"]] for k in ATTN_KERNELS}
-        calls = len(per_kernel[ATTN_KERNELS[0]])
+        # (names matched as whole identifiers: attn_fwd_kernel is not a part of
+        # attn_fwd_bal_kernel, nor attn_plan_kernel of attn_bal_plan_kernel)
+        per_kernel = {k: [float(r["Counter_Value"]) for r in rows if re.search(r"\b" + k + r"\b", r["Kernel_Name"])]
+                      for k in ATTN_KERNELS}
+        calls = sum(len(per_kernel[k]) for k in ATTN_MAIN_KERNELS)
         if calls == 0:
-            raise RuntimeError(f"{counter}: no {ATTN_KERNELS[0]} dispatches in {d}")
+            raise RuntimeError(f"{counter}: no {' / '.join(ATTN_MAIN_KERNELS)} dispatches in {d}")
         # average KiB per call: the main kernel every call, the combine when it ran
         kib = sum(sum(v) for v in per_kernel.values()) / calls
         # the calibration copy is by far the largest copy in the trace; the
@@ -138,9 +145,10 @@ def ingest_traffic(workload: str, fetch_dir: str, write_dir: str, calib_mib: int
         f"--workload {workload} --secondary none --steps 5 --warmup 2 --no-cpu-baseline --calib-copy-mib {calib_mib}\n"
         f"python3 $REPO/bench.py --workload {workload} --ingest-traffic OUT/fetch OUT/write\n"
         "```\n\n"
-        "A call of tree_attn_verify is attn_fwd_kernel plus attn_combine_kernel (and,\n"
-        "for batches, the attn_plan_kernel that orders the tasks before them); the\n"
-        "figures are their per-call sums averaged over the calls in the trace.  Each\n"
+        "A call of tree_attn_verify is attn_fwd_kernel plus attn_combine_kernel, or for\n"
+        "batches attn_bal_plan_kernel, attn_fwd_bal_kernel and attn_combine_kernel (the\n"
+        "longest-first order: attn_plan_kernel first); the figures are their per-call\n"
+        "sums averaged over the calls in the trace.  Each\n"
         f"counter is scaled by {calib_mib} MiB over what it read for the calibration copy.\n\n"
         "| counter | KiB per call (raw) | calibration copy (KiB raw) | scale | bytes per call |\n"
         "|---|---|---|---|---|\n"
