@@ -322,6 +322,9 @@ BALANCED = {
     # many short requests: lanes that cross several groups
     "many_short": ([W.random_tree(np.random.default_rng(50 + i), 8 + (5 * i) % 57, 16) for i in range(40)],
                    [(97 * i) % 400 for i in range(40)], 32, 8, 128),
+    # 100 requests: lanes across many short groups, ranks across the planner's waves
+    "requests_100": ([W.random_tree(np.random.default_rng(100 + i), 8 + (7 * i) % 90, 16) for i in range(100)],
+                     [(131 * i) % 900 for i in range(100)], 32, 8, 128),
 }
 
 

@@ -1434,8 +1434,8 @@ constexpr int kBalWaves = kBalThreads / 64;
 
 __device__ __forceinline__ int bal_wg_of_lane(int l) { return (l >> 5) + 8 * (l & 31); }
 
-// n / d for 0 <= n < 2^31, d > 0 and a quotient below 2^22, from the float
-// reciprocal of d (relative error 2^-23, so the estimate is off by at most
+// n / d for 0 <= n < 2^31, d > 0 and a quotient of at most 2^22, from the
+// hardware reciprocal of d (within one ulp, so the estimate is off by at most
 // one) and one correction each way.
 __device__ __forceinline__ int bal_div(int n, int d, float inv_d) {
     int q = (int)((float)n * inv_d);
@@ -1628,7 +1628,7 @@ __global__ void __launch_bounds__(kBalThreads) attn_bal_plan_kernel(KParams p, i
             const int Wc = s_W[c], xc = s_x[c];
             const int lb = s_len[rb];
             const int o = s_off[rb] + g * (lb + kBalPieceCost) + kBalPieceCost;  // the group's first chunk
-            const float inv = 1.f / (float)Wc;
+            const float inv = __builtin_amdgcn_rcpf((float)Wc);
             const int i0 = bal_lane_of(o, Wc, inv, xc);
             const int i1 = bal_lane_of(o + lb - 1, Wc, inv, xc);
             gi = make_int2(s_pbase[c] + i0 + s_rank[rb] * hkv + g, i1 - i0 + 1);
@@ -1652,7 +1652,7 @@ __global__ void __launch_bounds__(kBalThreads) attn_bal_plan_kernel(KParams p, i
         pb0 = s_pbase[c];
         l00 = s_lane0[c];
         ncls = s_cnt[c];
-        const float inv_x = 1.f / (float)xc;
+        const float inv_x = __builtin_amdgcn_rcpf((float)xc);
         A = bal_div(i * Wc, xc, inv_x);
         E = bal_div((i + 1) * Wc, xc, inv_x);
         // the request holding chunk A: the last position whose first chunk <= A
@@ -1668,7 +1668,7 @@ __global__ void __launch_bounds__(kBalThreads) attn_bal_plan_kernel(KParams p, i
         while (xx < E) {
             const int lb = s_plen[pos] + kBalPieceCost;
             const int gstart = s_first[pos];
-            const int g = bal_div(xx - gstart, lb, 1.f / (float)lb);
+            const int g = bal_div(xx - gstart, lb, __builtin_amdgcn_rcpf((float)lb));
             const int o = gstart + g * lb;
             const int gend = o + lb;
             const int xe = min(E, gend);
@@ -1687,13 +1687,13 @@ __global__ void __launch_bounds__(kBalThreads) attn_bal_plan_kernel(KParams p, i
         int ebase = incl - v;
         for (int w = 0; w < wv; ++w) ebase += s_wtot[w];
         for (int rt = 0; rt < c; ++rt) wg[bal_wg_of_lane(l00 + i * c + rt)] = make_int2(ebase + rt * count, count);
-        const float inv_W = 1.f / (float)Wc;
+        const float inv_W = __builtin_amdgcn_rcpf((float)Wc);
         int pos = pos0, j = 0, xx = A;
         while (xx < E) {
             const int len_g = s_plen[pos];
             const int lb = len_g + kBalPieceCost;
             const int gstart = s_first[pos];
-            const int g = bal_div(xx - gstart, lb, 1.f / (float)lb);
+            const int g = bal_div(xx - gstart, lb, __builtin_amdgcn_rcpf((float)lb));
             const int o = gstart + g * lb;  // the group's positions: kBalPieceCost, then its chunks
             const int gend = o + lb;
             const int xe = min(E, gend);
