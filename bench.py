@@ -350,11 +350,16 @@ def main(argv=None):
     # on this GPU (read + write bytes over time), measured after the timed
     # regions.  (Skipped in counter runs: the traffic calibration takes the
     # largest copy in the trace as its reference.)
+    # And the matrix rate a plain bf16 GEMM reaches on it (the library's,
+    # under the same clock and power limits as the attention kernel).
     copy_gbs = hbm_copy_probe(torch, dev) if args.calib_copy_mib == 0 else None
+    gemm_tflops = mfma_gemm_probe(torch, dev) if args.calib_copy_mib == 0 else None
     for ln in [line, *lines.values()]:
         roof = ln["roofline"]
         roof["hbm_copy_probe_gbs"] = copy_gbs
         roof["frac_of_copy_probe"] = roof["achieved_gbs"] / copy_gbs if copy_gbs else None
+        roof["gemm_probe_tflops"] = gemm_tflops
+        roof["frac_of_gemm_probe"] = roof["achieved_tflops"] / gemm_tflops if gemm_tflops else None
     if lines:
         line["per_config"] = {
             name: {"workload": ln["config"]["workload"], "value": ln["value"], "unit": ln["unit"],
@@ -734,6 +739,26 @@ def hbm_copy_probe(torch, dev, mib: int = 512, reps: int = 10) -> float:
     ms = a.elapsed_time(b) / reps
     del src, dst
     return 2 * n * 4 / (ms * 1e-3) / 1e9
+
+
+def mfma_gemm_probe(torch, dev, n: int = 8192, reps: int = 10) -> float:
+    """TFLOP/s of an n x n x n bf16 matrix product (torch.matmul on contiguous
+    2-D operands, fp32 accumulation in the library), averaged over `reps`
+    products timed with HIP events: the matrix rate this GPU sustains."""
+    a = torch.randn((n, n), dtype=torch.float32, device=dev).to(torch.bfloat16).contiguous()
+    b = torch.randn((n, n), dtype=torch.float32, device=dev).to(torch.bfloat16).contiguous()
+    for _ in range(3):
+        c = torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
 
 
 def bench_sample(args, torch, BND, L, dev):

@@ -200,9 +200,10 @@ typedef struct {
  * Plan overrides for tree_attn_verify: tuning and tests only.
  *
  * tree_attn_verify picks its own plan (how many slices of the key axis each
- * query-row tile is cut into, and for batches whether a device-side planner
- * orders the tasks longest first) from the host sizes alone, so its workspace
- * size is a pure function of them.  The _ex variants below take an explicit
+ * query-row tile is cut into for one request; for batches, a device-side
+ * planner that gives every CU an equal share of the key axes, or orders fixed
+ * slices longest first) from the host sizes alone, so its workspace size is a
+ * pure function of them.  The _ex variants below take an explicit
  * override instead; a NULL override, or zero fields, give exactly the plain
  * calls' plan.  They exist so that tuning sweeps and the tests can reach every
  * plan the kernels support; the results are the same attention (each slice
