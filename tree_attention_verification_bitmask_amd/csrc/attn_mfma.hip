@@ -354,6 +354,18 @@ __device__ __forceinline__ bool decode_task(const KParams &p, int wid, Task *t) 
     return true;
 }
 
+// Rows per row tile for a request of rows_b query rows and tiles of at most TR
+// rows: the rows are spread evenly over its ceil(rows_b / TR) tiles, in whole
+// 32-row blocks, so the tiles of one key range carry equal work and keep in
+// step (sharing the K/V in their XCD's L2) instead of full tiles and a short
+// last one.
+__device__ __forceinline__ int tile_span(int rows_b, int TR) {
+    if (rows_b <= 0) return TR;
+    const int R = (rows_b + TR - 1) / TR;
+    const int per = (rows_b + R - 1) / R;
+    return (per + 31) & ~31;
+}
+
 // One piece of work for a workgroup: row tile rt of (request b, KV head g)
 // over the keys [k_lo, k_lo + k_span), clipped to the keys the tile's nodes
 // can see.  The result goes to the output (pslot < 0) or, normalised by its
@@ -413,9 +425,10 @@ __device__ __attribute__((always_inline)) inline void attn_piece(const KParams &
     }
     const int G = p.hq / p.hkv;
     const int rows_b = n_nodes * G;
-    const int row0 = rt * TR;
+    const int span = tile_span(rows_b, TR);
+    const int row0 = rt * span;
     if (row0 >= rows_b) return;
-    const int row_end = min(rows_b, row0 + TR);
+    const int row_end = min(rows_b, row0 + span);
     const int node_first = row0 / G;
     const int node_last = (row_end - 1) / G;
     const int key_end = P + node_last + 1;  // tree keys past the tile's last node are never visible
@@ -1193,9 +1206,10 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
     const int lo = rq.lo, n = rq.n, P = rq.P;
     const int G = p.hq / p.hkv;
     const int rows_b = n * G;
-    const int row0 = rt * p.tile_rows;
-    if (row0 + rg * 32 >= rows_b) return;  // (wave-uniform) no rows in this group
-    const int row_end = min(rows_b, row0 + p.tile_rows);
+    const int span = tile_span(rows_b, p.tile_rows);
+    const int row0 = rt * span;
+    const int row_end = min(rows_b, row0 + span);
+    if (row0 + rg * 32 >= row_end) return;  // (wave-uniform) no rows in this group
     const int key_end = P + (row_end - 1) / G + 1;
     const int nsplit = p.bal_group ? nbal : min(p.splits, (key_end + p.keys_per_split - 1) / p.keys_per_split);
     const int r = row0 + rg * 32 + col;
@@ -1282,9 +1296,10 @@ __device__ __forceinline__ int tile_chunks(const KParams &p, const Req &rq, int 
     if (!rq.ok) return 0;
     const int G = p.hq / p.hkv;
     const int rows_b = rq.n * G;
-    const int row0 = rt * p.tile_rows;
+    const int span = tile_span(rows_b, p.tile_rows);
+    const int row0 = rt * span;
     if (row0 >= rows_b) return 0;
-    const int row_end = min(rows_b, row0 + p.tile_rows);
+    const int row_end = min(rows_b, row0 + span);
     const int key_end = rq.P + (row_end - 1) / G + 1;
     const int k_lo = s * p.keys_per_split;
     if (k_lo >= key_end) return 0;
