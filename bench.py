@@ -845,10 +845,11 @@ def bench_stochastic(args, torch, BND, L, dev):
     plus noise, so candidates are often but not always accepted), each child's
     token drawn from its parent's q, seeded uniforms; rotated copies keep the
     Infinity Cache cold.  value = verification steps (requests) per second.
-    The roofline counts the logits read once (the statistics pass); the walk's
-    reads (a few elements per candidate, two passes over q and the residual
-    per rejection, one for the final draw) depend on the data and come on
-    top."""
+    The roofline counts the logits read once (the statistics pass); the
+    rejection passes re-read the logits and draft probabilities of every row
+    whose test was rejected (each node's tests are decided whether or not
+    the walk reaches it), and the draw re-reads one chunk; these depend on
+    the data and come on top."""
     wl = W.make_workload("c3", seed=args.seed)
     V = args.argmax_vocab
     T = wl.total_nodes

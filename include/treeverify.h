@@ -343,7 +343,12 @@ tv_status tree_accept_greedy(const int32_t *parent, const int32_t *draft_tokens,
  * u_final[b] (the smallest index whose cumulative weight exceeds u times the
  * total; if rounding leaves none, the last index with positive weight).
  * Children with a negative draft token (dead leaves) are skipped.  Float64
- * throughout; only the order of additions differs from a sequential sum.
+ * throughout.  The residual after rejections is formed in closed form: with
+ * r = (p - c q_v)+ / W (r = p: c = 0, W = 1), the next one is
+ * (p - (c + W) q_v)+ over its sum, which is the update above with the
+ * normalisations folded in; so every node's tests are decided at once, in
+ * parallel, and the walk follows them.  Only rounding differs from a
+ * sequential update.
  *
  * In:  parent, draft_tokens [T] (request-local parents, as tree_mask_build);
  *      cu_nodes [B+1]; root_logits [B, vocab] and node_logits [T, vocab]
@@ -357,11 +362,14 @@ tv_status tree_accept_greedy(const int32_t *parent, const int32_t *draft_tokens,
  * Out: accept_len [B], accept_idx [B, max_depth] (request-local, -1 padded),
  *      next_token [B], as tree_accept_greedy.
  * Workspace: tree_accept_stochastic_workspace_size(batch, total_nodes, vocab)
- *      bytes (16 per 2048 logits of every row, then 8 per logit of each
- *      request's residual), 256-byte aligned; no contents required.
+ *      bytes, 256-byte aligned, no contents required: over the B + T rows,
+ *      64 bytes per 2048 logits (chunk statistics and six slots of residual
+ *      chunk sums) and 332 bytes per row, plus 24 per node and 4 per request.
  * err: BAD_REQUEST (cu_nodes outside [0, T], decreasing, or N_b above
  *      TV_MAX_NODES), BAD_PARENT, BAD_TOKEN (a draft token >= vocab); such a
- *      request gets accept_len 0, no path and next_token -1.
+ *      request gets accept_len 0, no path and next_token -1.  When cu_nodes
+ *      decreases, the node ranges of other requests may overlap; their
+ *      results are then unspecified (indices stay in range).
  */
 size_t tree_accept_stochastic_workspace_size(int32_t batch, int32_t total_nodes, int32_t vocab);
 tv_status tree_accept_stochastic(const int32_t *parent, const int32_t *draft_tokens, const int32_t *cu_nodes,

@@ -427,9 +427,23 @@ def test_gdn_host_checks(L):
 
 def test_accept_stochastic_host_checks(L):
     B, T, V = 2, 10, 1000
+    def ws_size(B, T, V):
+        # ten 256-byte-aligned segments over B + T rows and 2048-logit
+        # chunks: chunk statistics (16 B), six slots of residual chunk sums
+        # (8 B each), then per row (M, Z) 16 B, four pass records of 64 B, the
+        # final residual 24 B, candidate range 8 B, decision 4 B, first
+        # candidate 24 B; a 24-byte record per candidate node and a 4-byte
+        # flag per request
+        nch, rows = -(-V // 2048), B + T
+        off = 0
+        for size in (rows * nch * 16, 6 * rows * nch * 8, rows * 16, 4 * rows * 64, rows * 24, rows * 8, rows * 4,
+                     rows * 24, T * 24, B * 4):
+            off = -(-off // 256) * 256 + size
+        return -(-off // 256) * 256
     need = L.tree_accept_stochastic_workspace_size(B, T, V)
-    assert need == ((12 * 16 + 255) // 256) * 256 + B * V * 8   # chunk stats (1 chunk), one residual per request
-    assert L.tree_accept_stochastic_workspace_size(1, 2, 4097) == ((3 * 3 * 16 + 255) // 256) * 256 + 4097 * 8
+    assert need == ws_size(B, T, V)
+    assert L.tree_accept_stochastic_workspace_size(1, 2, 4097) == ws_size(1, 2, 4097) == 3328
+    assert L.tree_accept_stochastic_workspace_size(1, 128, 151936) == ws_size(1, 128, 151936)
     assert L.tree_accept_stochastic_workspace_size(-1, T, V) == 0
     assert L.tree_accept_stochastic_workspace_size(B, T, 0) == 0
 

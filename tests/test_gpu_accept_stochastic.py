@@ -40,9 +40,10 @@ def _round_bf16(x):
     return (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32).view(np.float32)
 
 
-def make_case(seed, batch, nodes, V, dead=0.05, spread=3.0, q_noise=1.0, logit_dtype="f32"):
+def make_case(seed, batch, nodes, V, dead=0.05, spread=3.0, q_noise=1.0, logit_dtype="f32", root_kids=None):
     """Random forests; each node's children drawn from its q; target logits
-    independent of q."""
+    independent of q.  root_kids: the first root_kids nodes of each request
+    are the root's children and the others hang below them."""
     rng = np.random.default_rng(seed)
     sizes = rng.integers(nodes[0], nodes[1] + 1, batch)
     cu = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
@@ -51,7 +52,10 @@ def make_case(seed, batch, nodes, V, dead=0.05, spread=3.0, q_noise=1.0, logit_d
     for b in range(batch):
         lo = int(cu[b])
         for i in range(int(sizes[b])):
-            parent[lo + i] = -1 if i == 0 else int(rng.integers(-1, i))
+            if root_kids is not None:
+                parent[lo + i] = -1 if i < root_kids else int(rng.integers(0, i))
+            else:
+                parent[lo + i] = -1 if i == 0 else int(rng.integers(-1, i))
     root_logits = rng.normal(0, spread, (batch, V)).astype(np.float32)
     node_logits = rng.normal(0, spread, (T, V)).astype(np.float32)
     if logit_dtype == "bf16":
@@ -168,3 +172,52 @@ def test_errors_reported_per_request():
                                           c["root_q"][b].astype(np.float64), c["node_q"][lo:hi].astype(np.float64),
                                           c["u_accept"][lo:hi], float(c["u_final"][b]), 16)
         assert alen[b] == len(path) and list(aidx[b, :len(path)]) == path and nxt[b] == t
+
+
+def test_many_candidates_at_one_node():
+    """Roots with 40 children and a drafter far from the target, so that most
+    tests reject: tests past the fourth at a node take the per-row
+    continuation after the whole-GPU passes."""
+    announce("stochastic accept: 40 root children")
+    deep = 0
+    for seed, ldt in ((21, "f32"), (22, "bf16"), (23, "f32")):
+        c = make_case(seed, 3, (60, 90), 3000, q_noise=4.0, logit_dtype=ldt, root_kids=40)
+        alen, aidx, nxt, err = run_gpu(c, 1.0, 16, ldt)
+        ralen, raidx, rnxt = run_oracle(c, 1.0, 16)
+        assert err == 0
+        assert np.array_equal(alen, ralen) and np.array_equal(aidx, raidx) and np.array_equal(nxt, rnxt)
+        # how far down the root's candidate list each request went
+        for b in range(3):
+            lo, hi = int(c["cu"][b]), int(c["cu"][b + 1])
+            live = [i for i in range(hi - lo) if c["parent"][lo + i] == -1 and c["draft"][lo + i] >= 0]
+            tried = live.index(int(raidx[b, 0])) + 1 if ralen[b] > 0 else len(live)
+            deep += tried > 5
+    assert deep >= 2, "the cases should reach the continuation"
+
+
+def test_zero_residual_sum_keeps_r():
+    """Target and draft the same point mass, every candidate a token the
+    drafter gives probability 0: each test rejects, (r - q)+ sums to 0 so r
+    stays p, and the next token is the point mass (also past the fourth
+    candidate)."""
+    announce("stochastic accept: zero residual sum")
+    rng = np.random.default_rng(31)
+    V, B = 500, 4
+    c = make_case(31, B, (8, 12), V, dead=0.0, root_kids=7)
+    T = c["draft"].shape[0]
+    star_r = rng.integers(0, V, B)
+    star_n = rng.integers(0, V, T)
+    c["root_logits"][np.arange(B), star_r] = 3000.0
+    c["node_logits"][np.arange(T), star_n] = 3000.0
+    c["root_q"][:] = 0.0
+    c["root_q"][np.arange(B), star_r] = 1.0
+    c["node_q"][:] = 0.0
+    c["node_q"][np.arange(T), star_n] = 1.0
+    owner = np.searchsorted(c["cu"], np.arange(T), side="right") - 1
+    want = np.where(c["parent"] < 0, star_r[owner], star_n[np.maximum(c["parent"] + c["cu"][owner], 0)])
+    c["draft"] = ((want + 1 + rng.integers(0, V - 1, T)) % V).astype(np.int32)   # never the point mass
+    alen, aidx, nxt, err = run_gpu(c, 1.0, 16)
+    ralen, raidx, rnxt = run_oracle(c, 1.0, 16)
+    assert err == 0
+    assert (ralen == 0).all() and np.array_equal(rnxt, star_r)
+    assert np.array_equal(alen, ralen) and np.array_equal(aidx, raidx) and np.array_equal(nxt, rnxt)
