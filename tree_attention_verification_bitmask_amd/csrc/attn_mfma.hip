@@ -252,6 +252,10 @@ struct KParams {
     const int4 *bal_piece;
     const int2 *bal_group;
     int bal_slots;  // entries of bal_piece, and partial slots (the bound every index is checked against)
+    // 1: the static order with a multiple of 8 KV heads, where every slice of
+    // KV head g ran on XCD g mod 8; the merge then takes head g's tiles on
+    // that XCD too, so it reads the partials where they were written
+    int combine_xcd;
 };
 
 // Sizes of request b, with all four reads issued before any test: a chain of
@@ -1153,8 +1157,23 @@ __global__ void __launch_bounds__(64 * kCombineWaves) attn_combine_kernel(KParam
     constexpr int kBatch = I4W == 1 ? 16 : 8;        // slices per batch
     // (wave-uniform: the request's sizes then come by scalar loads, which
     // complete independently of the partials' vector loads)
-    const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * kCombineWaves + (threadIdx.x >> 6));
     const int nw = p.rgroups;  // 32-row groups per tile
+    int gw;
+    if (p.combine_xcd) {
+        // the waves of XCD x (workgroup ids x mod 8) take the tiles of KV
+        // heads g = x + 8 m, row tile fastest, then m, then the request
+        const int per_tile = kGroups * DB * nw;
+        const int x = blockIdx.x % kXcds;
+        const int wx = (blockIdx.x / kXcds) * kCombineWaves + (threadIdx.x >> 6);
+        const int tix = wx / per_tile;
+        const int m = (tix / p.row_tiles) % (p.hkv / kXcds);
+        const int bx = tix / (p.row_tiles * (p.hkv / kXcds));
+        if (bx >= p.batch) return;
+        gw = ((bx * p.hkv + x + kXcds * m) * p.row_tiles + tix % p.row_tiles) * per_tile + (wx - tix * per_tile);
+    } else {
+        gw = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
+    }
+    gw = __builtin_amdgcn_readfirstlane(gw);
     const int i4b = (gw % kGroups) * I4W;
     const int db = (gw / kGroups) % DB;
     const int rg = (gw / (kGroups * DB)) % nw;
@@ -1882,6 +1901,7 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *works
     p.bal_piece = nullptr;
     p.bal_group = nullptr;
     p.bal_slots = 0;
+    p.combine_xcd = (!plan.balanced && !plan.table && a.hkv % kXcds == 0) ? 1 : 0;
     if (plan.balanced) {
         const size_t rows = ((size_t)kBalWgs + (size_t)a.batch * a.hkv) * plan.row_tiles * plan.rows_per_tile;
         const size_t off = (rows * a.head_dim * sizeof(uint16_t) + 255) & ~(size_t)255;
@@ -1919,7 +1939,10 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *works
     const bool wide = plan.balanced || plan.splits <= 8;
     const bool merge = plan.balanced || plan.splits > 1;
     const long cwaves = tiles * (plan.rows_per_tile / 32) * (a.head_dim / 32) * (wide ? 1 : 4);
-    const long cblocks = (cwaves + kCombineWaves - 1) / kCombineWaves;
+    // XCD-aligned merge: each XCD's waves (tiles / 8 of them) in whole workgroups
+    const long cblocks = p.combine_xcd
+                             ? kXcds * ((cwaves / kXcds + kCombineWaves - 1) / kCombineWaves)
+                             : (cwaves + kCombineWaves - 1) / kCombineWaves;
     if (a.head_dim == 128) {
         if (plan.waves == 8) launch_fwd<128, 8, 1>(p, plan, grid, stream);
         else launch_fwd<128, 4, 1>(p, plan, grid, stream);
