@@ -109,7 +109,9 @@ CASES = [  # seed, batch, nodes, vocab, temperature, max_depth, logits
     (3, 8, (30, 90), 4096, 1.0, 4, "bf16"),
     (4, 2, (64, 128), 151936, 1.0, 16, "f32"),
     (5, 3, (20, 60), 151936, 0.8, 16, "bf16"),
-    (6, 2, (2, 4), 1500000, 1.0, 16, "f32"),     # draw ranges of 1465 logits: more than one block-wide tile
+    (6, 2, (2, 4), 1500000, 1.0, 16, "f32"),     # 733 chunks: more than one block-wide tile of chunk weights
+    (7, 3, (20, 40), 3001, 1.0, 16, "bf16"),     # rows not 16-byte aligned: the element-wise loads
+    (8, 64, (1, 24), 1000, 0.9, 8, "f32"),       # 64 requests, trees of 1 to 24 nodes
 ]
 
 
