@@ -260,14 +260,18 @@ __device__ __forceinline__ double chunk_resid_sum(const float x[kPerLane], const
 
 // The row's M = max y and Z = sum exp(y - M) from its chunk statistics, by
 // one wavefront: lane l takes chunks l, l + 64, ... in order, then a
-// butterfly, so every caller gets bit-identical values.
-__device__ __forceinline__ double2 row_mz(const double2 *st, int nchunks, int lane, const double *etab,
-                                          const ExpConst &ek) {
-    double m = -INFINITY;
-    for (int c = lane; c < nchunks; c += 64) m = fmax(m, st[c].x);
+// butterfly, so every wave of the row gets bit-identical values.  v0 and v1
+// are chunks lane and lane + 64, loaded by the caller ((-inf, 0) past the
+// row's chunks).
+__device__ __forceinline__ double2 row_mz(const double2 *st, int nchunks, int lane, double2 v0, double2 v1,
+                                          const double *etab, const ExpConst &ek) {
+    double m = fmax(v0.x, v1.x);
+    for (int c = lane + 128; c < nchunks; c += 64) m = fmax(m, st[c].x);
     m = wave_max64(m);
     double z = 0.0;
-    for (int c = lane; c < nchunks; c += 64) {
+    if (v0.x > -INFINITY) z += v0.y * exp_nonpos(v0.x - m, etab, ek);
+    if (v1.x > -INFINITY) z += v1.y * exp_nonpos(v1.x - m, etab, ek);
+    for (int c = lane + 128; c < nchunks; c += 64) {
         const double2 v = st[c];
         if (v.x > -INFINITY) z += v.y * exp_nonpos(v.x - m, etab, ek);
     }
@@ -476,28 +480,23 @@ __global__ void __launch_bounds__(64 * kPassWaves) stoch_pass_kernel(SArgs a, in
     const int row = (int)(blockIdx.x / groups);
     const int chunk = (int)(blockIdx.x - row * groups) * kPassWaves + (int)(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    exp_table_fill(etab);
-    __syncthreads();
-    if (chunk >= a.nchunks) return;  // (wave-uniform; after the only barrier)
     const bool writer = chunk == 0 && lane == 0;
     const int64_t slot_elems = (int64_t)a.rows * a.nchunks;
     const int64_t rc0 = (int64_t)row * a.nchunks;
     Rec *rec_out = a.rec + (int64_t)j * a.rows + row;  // level j + 1
     // everything the decision reads, loaded together
     const int2 kc = a.kc[row];
-    double c, W;
-    int lev;
+    double c = 0.0, W = 1.0;
+    int lev = 0;
     bool open;
     Cand cd;
-    double2 mz;
+    double2 mz = make_double2(0.0, 1.0);
+    double2 v0 = make_double2(-INFINITY, 0.0), v1 = v0;  // pass 0: chunk statistics lane, lane + 64
     if (j == 0) {
         cd = a.c0[row];
-        mz = row_mz(a.st + rc0, a.nchunks, lane, etab, a.ek);
+        if (lane < a.nchunks) v0 = a.st[rc0 + lane];
+        if (lane + 64 < a.nchunks) v1 = a.st[rc0 + lane + 64];
         open = kc.x > 0;
-        c = 0.0;
-        W = 1.0;
-        lev = 0;
-        if (open && writer) a.mz[row] = mz;
     } else {
         const Rec R = a.rec[(int64_t)(j - 1) * a.rows + row];
         mz = a.mz[row];
@@ -514,9 +513,18 @@ __global__ void __launch_bounds__(64 * kPassWaves) stoch_pass_kernel(SArgs a, in
             lev = j;
         }
     }
+    // a closed row's workgroup (its waves share the row) leaves before the
+    // exp table and the barrier
     if (!open) {
         if (writer) rec_out->status = kClosed;
         return;
+    }
+    exp_table_fill(etab);
+    __syncthreads();
+    if (chunk >= a.nchunks) return;  // (wave-uniform; after the only barrier)
+    if (j == 0) {
+        mz = row_mz(a.st + rc0, a.nchunks, lane, v0, v1, etab, a.ek);
+        if (writer) a.mz[row] = mz;
     }
     const double M = mz.x, iZ = 1.0 / mz.y;
     if (j >= kc.x) {  // every candidate rejected: the draw comes from this residual
