@@ -223,3 +223,16 @@ def test_zero_residual_sum_keeps_r():
     assert err == 0
     assert (ralen == 0).all() and np.array_equal(rnxt, star_r)
     assert np.array_equal(alen, ralen) and np.array_equal(aidx, raidx) and np.array_equal(nxt, rnxt)
+
+
+@pytest.mark.parametrize("nodes,D", [((0, 3), 1), ((0, 3), 16), ((0, 0), 4)])
+def test_empty_trees_and_depth_one(nodes, D):
+    """Requests with no nodes draw the next token from the root's p; a batch
+    with no nodes at all passes empty node arrays; max_depth 1 tests only
+    the root's children."""
+    announce(f"stochastic accept: nodes {nodes} D {D}")
+    c = make_case(41, 12, nodes, 500)
+    alen, aidx, nxt, err = run_gpu(c, 1.0, D)
+    ralen, raidx, rnxt = run_oracle(c, 1.0, D)
+    assert err == 0
+    assert np.array_equal(alen, ralen) and np.array_equal(aidx, raidx) and np.array_equal(nxt, rnxt)
