@@ -91,9 +91,12 @@ def test_attn_host_checks(L):
 
 
 def test_workspace_sizes(L):
-    # fp32 and tiny trees take the VALU path, which needs no workspace
+    # fp32 takes the vector kernel, which needs no workspace; a bf16 tree of
+    # 4 rows per KV head over a short prefix is one slice (no partials), over
+    # a long one it is cut into slices like any other
     assert L.tree_attn_verify_workspace_size(1, 16, 16, 128, 2, 1, 64, 0) == 0
-    assert L.tree_attn_verify_workspace_size(1, 4, 4, 128, 8, 8, 128, 1) == 0   # 4 rows per KV head
+    assert L.tree_attn_verify_workspace_size(1, 4, 4, 128, 8, 8, 128, 1) == 0
+    assert L.tree_attn_verify_workspace_size(1, 1, 1, 8192, 32, 8, 128, 1) > 0
     # bf16 Qwen3-shaped layers split the key axis: bf16 partials (256 B per
     # row and slice) and fp32 (m, l) per row and slice
     for B, T, n, P in ((1, 64, 64, 1024), (1, 128, 128, 4096), (1, 256, 256, 8192), (8, 1024, 128, 8192)):

@@ -195,7 +195,9 @@ EDGE = {
     "gqa_1": ([W.random_tree(np.random.default_rng(3), 64, 16)], [300], 8, 8, 128, "bf16"),
     "gqa_8": ([W.random_tree(np.random.default_rng(4), 50, 16)], [129], 64, 8, 128, "bf16"),
     "head_dim_64_bf16": ([W.random_tree(np.random.default_rng(5), 70, 16)], [200], 16, 4, 64, "bf16"),
-    "valu_bf16_small": ([W.random_tree(np.random.default_rng(6), 5, 16)], [90], 8, 8, 128, "bf16"),
+    "five_rows_bf16": ([W.random_tree(np.random.default_rng(6), 5, 16)], [90], 8, 8, 128, "bf16"),  # under 32 rows
+    "one_node_long_prefix": ([W.chain_tree(1)], [8191], 32, 8, 128, "bf16"),  # 4 rows, many slices
+    "chain_4_d64": ([W.chain_tree(4)], [3000], 16, 4, 64, "bf16"),
     "fp32_d128": ([W.random_tree(np.random.default_rng(7), 20, 16)], [65], 4, 2, 128, "f32"),
     "with_empty_request": ([W.random_tree(np.random.default_rng(8), 40, 16), np.zeros(0, np.int32),
                             W.random_tree(np.random.default_rng(9), 9, 16)], [100, 50, 0], 32, 8, 128, "bf16"),

@@ -5,8 +5,8 @@
 // Attention Mechanism": each node attends to the whole prefix and to the tree
 // nodes on its own root-to-node branch (parts 1 and 2).
 //
-// This path serves fp32 inputs and trees too small to fill an MFMA tile
-// (fewer than 32 node x GQA-head rows per KV head).  Keys are taken 64 at a
+// This path serves fp32 inputs (bf16 calls take the matrix-core kernel).
+// Keys are taken 64 at a
 // time, one per lane: the lane computes its key's logit against q (held in
 // LDS and read as a broadcast), the wave reduces max and sum (online
 // softmax), and then every lane accumulates its own output channels over the
