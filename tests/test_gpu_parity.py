@@ -199,6 +199,10 @@ EDGE = {
     "one_node_long_prefix": ([W.chain_tree(1)], [8191], 32, 8, 128, "bf16"),  # 4 rows, many slices
     "chain_4_d64": ([W.chain_tree(4)], [3000], 16, 4, 64, "bf16"),
     "fp32_d128": ([W.random_tree(np.random.default_rng(7), 20, 16)], [65], 4, 2, 128, "f32"),
+    # fp32 over long prefixes: the vector kernel's sixteen-wave form
+    "fp32_long_prefix_d128": ([W.random_tree(np.random.default_rng(12), 6, 16)], [5000], 8, 2, 128, "f32"),
+    "fp32_long_prefix_d64": ([W.chain_tree(3), W.random_tree(np.random.default_rng(13), 9, 16)], [4500, 37],
+                             4, 4, 64, "f32"),
     "with_empty_request": ([W.random_tree(np.random.default_rng(8), 40, 16), np.zeros(0, np.int32),
                             W.random_tree(np.random.default_rng(9), 9, 16)], [100, 50, 0], 32, 8, 128, "bf16"),
     "chain_64_deep": ([W.chain_tree(64)], [250], 32, 8, 128, "bf16"),
