@@ -257,7 +257,7 @@ tv_status tree_attn_verify_ex(const void *q, void *k_cache, const void *v_cache,
 /*
  * tree_attn_verify_plan -- the plan tree_attn_verify(_ex) would run for these
  * host sizes (pure host arithmetic; tuning and tests).  Writes info[0..7]:
- *   [0] 1 = matrix-core kernel, 0 = vector kernel (fp32, or too few rows)
+ *   [0] 1 = matrix-core kernel (bf16), 0 = vector kernel (fp32)
  *   [1] query rows per workgroup tile   [2] row tiles per (request, KV head)
  *   [3] key-axis slices                 [4] keys per slice
  *       (both 0 for the balanced order: its pieces vary in length)
