@@ -52,6 +52,23 @@ def mask(d, wl):
     return anc, pos
 
 
+# Workloads beside the named configs: bf16 trees of fewer than 32 rows per KV
+# head (the matrix-core kernel with one partly filled row block) and fp32
+# over a long prefix (the vector kernel's sixteen-wave form).
+EXTRA = {
+    "tiny_bf16": ([W.chain_tree(1), W.chain_tree(3), W.random_tree(np.random.default_rng(60), 5, 16)],
+                  [2000, 7000, 33], 32, 8, 128, "bf16"),
+    "fp32_long": ([W.random_tree(np.random.default_rng(61), 6, 16)], [5000], 8, 2, 128, "f32"),
+}
+
+
+def workload(name, seed):
+    if name in EXTRA:
+        parents, prefixes, hq, hkv, d, dtype = EXTRA[name]
+        return W.make_from_trees(parents, prefixes, hq=hq, hkv=hkv, d=d, dtype=dtype, seed=seed, values="qwen")
+    return W.make_workload(name, seed=seed)
+
+
 def paged_pool(wl, d, seed):
     """Scatter the cache rows into a pool 1.5x larger (random distinct slots,
     random values elsewhere) and build req_to_token [B, stride]: position p of
@@ -80,13 +97,13 @@ def paged_pool(wl, d, seed):
 
 PAGED_CASES = [("c1", 0, {}), ("c2", 1, {}), ("c3", 2, {}), ("c4", 0, {}), ("c5", 0, {}),
                ("c3", 3, dict(waves=8)), ("c2", 4, dict(waves=4, splits=1)),
-               ("c5", 1, dict(order=1)), ("c5", 2, dict(splits=3))]
+               ("c5", 1, dict(order=1)), ("c5", 2, dict(splits=3)), ("tiny_bf16", 0, {}), ("fp32_long", 0, {})]
 
 
 @pytest.mark.parametrize("name,seed,override", PAGED_CASES)
 def test_paged_equals_contiguous(name, seed, override):
     announce(f"paged {name} seed {seed} {override}")
-    wl = W.make_workload(name, seed=seed)
+    wl = workload(name, seed)
     d = dev_workload(wl)
     anc, _ = mask(d, wl)
     kp, vp, table, _ = paged_pool(wl, d, seed + 100)
@@ -110,7 +127,7 @@ def test_paged_matches_oracle(name, seed):
     """The oracle's attention over the rows the table names (gathered from
     the pool on the host)."""
     announce(f"paged vs oracle {name} seed {seed}")
-    wl = W.make_workload(name, seed=seed)
+    wl = workload(name, seed)
     d = dev_workload(wl)
     anc, _ = mask(d, wl)
     kp, vp, table, _ = paged_pool(wl, d, seed)
@@ -179,13 +196,14 @@ def round_like_cache(x, dtype):
 
 
 ROPE_CASES = [("c1", 0, 1e4, False), ("c2", 0, 1e6, False), ("c3", 1, 1e6, False), ("c5", 0, 1e6, False),
-              ("c2", 2, 1e6, True), ("c5", 3, 1e6, True), ("c1", 4, 1e4, True)]
+              ("c2", 2, 1e6, True), ("c5", 3, 1e6, True), ("c1", 4, 1e4, True), ("tiny_bf16", 1, 1e6, False),
+              ("tiny_bf16", 2, 1e6, True), ("fp32_long", 3, 1e4, True)]
 
 
 @pytest.mark.parametrize("name,seed,base,paged", ROPE_CASES)
 def test_rope_inside_attention(name, seed, base, paged):
     announce(f"rope inside attention {name} seed {seed} base {base} paged={paged}")
-    wl = W.make_workload(name, seed=seed)
+    wl = workload(name, seed)
     d = dev_workload(wl)
     anc, pos = mask(d, wl)
     q0 = d["q"].clone()

@@ -198,6 +198,9 @@ EDGE = {
     "five_rows_bf16": ([W.random_tree(np.random.default_rng(6), 5, 16)], [90], 8, 8, 128, "bf16"),  # under 32 rows
     "one_node_long_prefix": ([W.chain_tree(1)], [8191], 32, 8, 128, "bf16"),  # 4 rows, many slices
     "chain_4_d64": ([W.chain_tree(4)], [3000], 16, 4, 64, "bf16"),
+    "batch_tiny_trees": ([W.chain_tree(1), W.random_tree(np.random.default_rng(14), 3, 16), W.chain_tree(2),
+                          W.random_tree(np.random.default_rng(15), 6, 16), W.chain_tree(1)],
+                         [4000, 10, 2500, 600, 0], 32, 8, 128, "bf16"),
     "fp32_d128": ([W.random_tree(np.random.default_rng(7), 20, 16)], [65], 4, 2, 128, "f32"),
     # fp32 over long prefixes: the vector kernel's sixteen-wave form
     "fp32_long_prefix_d128": ([W.random_tree(np.random.default_rng(12), 6, 16)], [5000], 8, 2, 128, "f32"),
