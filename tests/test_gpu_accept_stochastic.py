@@ -236,3 +236,27 @@ def test_empty_trees_and_depth_one(nodes, D):
     ralen, raidx, rnxt = run_oracle(c, 1.0, D)
     assert err == 0
     assert np.array_equal(alen, ralen) and np.array_equal(aidx, raidx) and np.array_equal(nxt, rnxt)
+
+
+@pytest.mark.parametrize("case", range(20))
+def test_stochastic_random_shapes(case):
+    """Seeded random shapes: 1 to 9 requests of 0 to 85 nodes, vocabularies
+    from 2 to 40000 (chunk edges 2048 and 2049 included), temperatures 0.3 to
+    4, max_depth 1 to 64, drafters near and far from the target, and roots
+    with up to 11 children."""
+    rng = np.random.default_rng(5000 + case)
+    batch = int(rng.integers(1, 10))
+    lo_n = int(rng.choice([0, 1, 5]))
+    hi_n = lo_n + int(rng.choice([0, 3, 20, 80]))
+    V = int(rng.choice([2, 3, 17, 100, 1000, 2048, 2049, 5000, 40000]))
+    temp = float(rng.choice([0.3, 0.7, 1.0, 1.5, 4.0]))
+    D = int(rng.choice([1, 2, 4, 16, 64]))
+    ldt = "bf16" if rng.random() < 0.4 else "f32"
+    qn = float(rng.choice([0.3, 1.0, 4.0]))
+    rk = None if rng.random() < 0.7 else int(rng.integers(1, 12))
+    announce(f"stochastic random {case}: B {batch} nodes {lo_n}-{hi_n} V {V} T {temp} D {D} {ldt} root_kids {rk}")
+    c = make_case(10000 + case, batch, (lo_n, hi_n), V, q_noise=qn, logit_dtype=ldt, root_kids=rk)
+    alen, aidx, nxt, err = run_gpu(c, temp, D, ldt)
+    ralen, raidx, rnxt = run_oracle(c, temp, D)
+    assert err == 0
+    assert np.array_equal(alen, ralen) and np.array_equal(aidx, raidx) and np.array_equal(nxt, rnxt)
