@@ -73,3 +73,44 @@ def test_attn_random_shapes(case):
     if rows is not None:
         o = np.stack([o[t, h] for t, h in rows])
     assert_attn_close(o, ref, ref_abs, dtype, stated=True, what=f"random {case}")
+
+
+def random_fp32_case(rng):
+    """fp32 shapes for the vector kernel's tiles: GQA groups of 1 to 16 (tiles
+    of 1 to 8 query heads, several tiles per KV head when the group exceeds 8)
+    and trees of up to 160 nodes, so that tiles of 4, 2 and 1 nodes all occur,
+    with ragged last tiles."""
+    batch = int(rng.choice([1, 1, 2, 4]))
+    trees, prefixes = [], []
+    for _ in range(batch):
+        n = int(rng.integers(1, 161))
+        t = W.chain_tree(min(n, 64)) if rng.random() < 0.2 else W.random_tree(rng, n, 16)
+        trees.append(np.asarray(t, np.int32))
+        prefixes.append(int(rng.choice([0, 5, 130, 1100, 4100])))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 12, 16]))
+    d = int(rng.choice([64, 128]))
+    return trees, prefixes, hkv, G, d
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_attn_random_fp32_groups(case):
+    from tree_attention_verification_bitmask_amd import binding as B
+    trees, prefixes, hkv, G, d = random_fp32_case(np.random.default_rng(7500 + case))
+    announce(f"attn fp32 random {case}: nodes {[len(t) for t in trees]} P {prefixes} hkv {hkv} G {G} d {d}")
+    wl = W.make_from_trees(trees, prefixes, hq=hkv * G, hkv=hkv, d=d, dtype="f32", seed=case, values="qwen")
+    dv = dev_workload(wl)
+    anc, _, _, merr = B.tree_mask_build(dv["parent"], dv["cu"], dv["P"], wl.max_nodes, 64)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = B.tree_attn_verify(dv["q"], dv["k"], dv["v"], dv["cu"], dv["ks"], dv["P"], anc, wl.max_nodes,
+                             wl.max_prefix, err=err)
+    torch.cuda.synchronize()
+    assert int(merr.item()) == 0 and int(err.item()) == 0
+    rows = sample_rows(wl, 160, case) if wl.total_nodes * wl.hq > 2000 else None
+    ref = O.tree_attention(wl.q, wl.k, wl.v, wl.parent, wl.cu_nodes, wl.kv_start, wl.prefix_len, wl.scale, rows=rows)
+    ref_abs = O.tree_attention(wl.q, wl.k, np.abs(wl.v), wl.parent, wl.cu_nodes, wl.kv_start, wl.prefix_len,
+                               wl.scale, rows=rows)
+    o = to_np(out)
+    if rows is not None:
+        o = np.stack([o[t, h] for t, h in rows])
+    assert_attn_close(o, ref, ref_abs, "f32", stated=True, what=f"fp32 random {case}")
