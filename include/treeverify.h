@@ -209,7 +209,8 @@ typedef struct {
  * plan the kernels support; the results are the same attention (each slice
  * count and order computes the same sums, rounded differently).
  *   splits: key-axis slices per row tile, 0 = the library's choice (clamped
- *           to [1, number of 32-key chunks]);
+ *           to [1, number of 32-key chunks] for bf16, of 64-key chunks for
+ *           fp32);
  *   order:  batches only: TV_ORDER_AUTO (the library's choice: BALANCED
  *           when it applies and no splits are given), TV_ORDER_STATIC
  *           (workgroups take tasks in a fixed order), TV_ORDER_PLANNED (a
@@ -259,8 +260,10 @@ tv_status tree_attn_verify_ex(const void *q, void *k_cache, const void *v_cache,
  * host sizes (pure host arithmetic; tuning and tests).  Writes info[0..7]:
  *   [0] 1 = matrix-core kernel (bf16), 0 = vector kernel (fp32)
  *   [1] query rows per workgroup tile   [2] row tiles per (request, KV head)
+ *       (both 0 for the vector kernel)
  *   [3] key-axis slices                 [4] keys per slice
- *       (both 0 for the balanced order: its pieces vary in length)
+ *       (both 0 for the balanced order: its pieces vary in length; 1 and 0
+ *       for an unsliced vector-kernel call)
  *   [5] 1 = planned (longest-first) task order for a batch, 2 = balanced
  *   [6] chunks copied ahead of use      [7] workspace bytes without
  *       tv_attn_inputs (saturated to INT32_MAX)

@@ -54,7 +54,7 @@ def mask(d, wl):
 
 # Workloads beside the named configs: bf16 trees of fewer than 32 rows per KV
 # head (the matrix-core kernel with one partly filled row block) and fp32
-# over a long prefix (the vector kernel's sixteen-wave form).
+# over a long prefix (the vector kernel with the key axis cut into slices).
 EXTRA = {
     "tiny_bf16": ([W.chain_tree(1), W.chain_tree(3), W.random_tree(np.random.default_rng(60), 5, 16)],
                   [2000, 7000, 33], 32, 8, 128, "bf16"),

@@ -114,3 +114,32 @@ def test_attn_random_fp32_groups(case):
     if rows is not None:
         o = np.stack([o[t, h] for t, h in rows])
     assert_attn_close(o, ref, ref_abs, "f32", stated=True, what=f"fp32 random {case}")
+
+
+@pytest.mark.parametrize("splits", [2, 3, 7, 40, 1000])
+def test_attn_fp32_forced_slices(splits):
+    """The vector kernel's key-axis slices and their merge, at slice counts the
+    plan override fixes (1000 is clamped to the number of 64-key chunks):
+    two requests whose key axes end inside different slices, one of them
+    with no prefix, so that some slices hold no key a row sees."""
+    from tree_attention_verification_bitmask_amd import binding as B
+    trees = [W.random_tree(np.random.default_rng(81), 45, 16), W.chain_tree(20)]
+    wl = W.make_from_trees(trees, [700, 0], hq=12, hkv=4, d=64, dtype="f32", seed=splits, values="qwen")
+    plan = B.tree_attn_verify_plan(wl.batch, wl.total_nodes, wl.max_nodes, wl.max_prefix, wl.hq, wl.hkv, wl.d,
+                                   B.TV_F32, splits=splits)
+    announce(f"attn fp32 slices {splits}: plan {plan}")
+    span, S, kps = 700 + 45, plan["splits"], plan["keys_per_split"]
+    # whole 64-key chunks per slice, no empty slice past the longest key axis
+    assert plan["mfma"] == 0 and 1 < S <= min(splits, (span + 63) // 64) and kps % 64 == 0
+    assert (S - 1) * kps < span <= S * kps
+    dv = dev_workload(wl)
+    anc, _, _, merr = B.tree_mask_build(dv["parent"], dv["cu"], dv["P"], wl.max_nodes, 64)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = B.tree_attn_verify(dv["q"], dv["k"], dv["v"], dv["cu"], dv["ks"], dv["P"], anc, wl.max_nodes,
+                             wl.max_prefix, err=err, splits=splits)
+    torch.cuda.synchronize()
+    assert int(merr.item()) == 0 and int(err.item()) == 0
+    ref = O.tree_attention(wl.q, wl.k, wl.v, wl.parent, wl.cu_nodes, wl.kv_start, wl.prefix_len, wl.scale)
+    ref_abs = O.tree_attention(wl.q, wl.k, np.abs(wl.v), wl.parent, wl.cu_nodes, wl.kv_start, wl.prefix_len,
+                               wl.scale)
+    assert_attn_close(to_np(out), ref, ref_abs, "f32", stated=True, what=f"fp32 slices {splits}")

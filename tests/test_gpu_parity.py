@@ -202,7 +202,7 @@ EDGE = {
                           W.random_tree(np.random.default_rng(15), 6, 16), W.chain_tree(1)],
                          [4000, 10, 2500, 600, 0], 32, 8, 128, "bf16"),
     "fp32_d128": ([W.random_tree(np.random.default_rng(7), 20, 16)], [65], 4, 2, 128, "f32"),
-    # fp32 over long prefixes: the vector kernel's sixteen-wave form
+    # fp32 over long prefixes: the vector kernel cuts the key axis into slices and merges them
     "fp32_long_prefix_d128": ([W.random_tree(np.random.default_rng(12), 6, 16)], [5000], 8, 2, 128, "f32"),
     "fp32_long_prefix_d64": ([W.chain_tree(3), W.random_tree(np.random.default_rng(13), 9, 16)], [4500, 37],
                              4, 4, 64, "f32"),

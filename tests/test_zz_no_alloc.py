@@ -50,8 +50,25 @@ def test_noalloc_matches_workspace_call(first, second):
 
 
 def test_noalloc_fp32_and_single_slice():
-    """Plans that need no scratch (the vector kernel for fp32) go through too."""
+    """Plans that need no scratch (an unsliced vector-kernel call) go through too."""
     announce("noalloc c1 fp32")
     wl = W.make_workload("c1", seed=2)
     got, ref = _both(wl)
     assert np.array_equal(got.cpu().numpy().view(np.uint32), ref.cpu().numpy().view(np.uint32))
+
+
+def test_noalloc_fp32_slices():
+    """fp32 calls whose key axis the vector kernel cuts into slices keep their
+    partials in the scratch: two such calls in a row, the second smaller,
+    each bit-identical to the call with its own workspace."""
+    from tree_attention_verification_bitmask_amd import binding as B
+    cases = [([W.random_tree(np.random.default_rng(90), 7, 16)], [8192]),
+             ([W.chain_tree(3)], [3000])]
+    for i, (trees, prefixes) in enumerate(cases):
+        wl = W.make_from_trees(trees, prefixes, hq=32, hkv=8, d=128, dtype="f32", seed=i, values="qwen")
+        plan = B.tree_attn_verify_plan(wl.batch, wl.total_nodes, wl.max_nodes, wl.max_prefix, wl.hq, wl.hkv,
+                                       wl.d, B.TV_F32)
+        announce(f"noalloc fp32 slices case {i}: plan {plan}")
+        assert plan["splits"] > 1 and plan["workspace_bytes"] > 0
+        got, ref = _both(wl)
+        assert np.array_equal(got.cpu().numpy().view(np.uint32), ref.cpu().numpy().view(np.uint32)), i

@@ -18,10 +18,17 @@
 // i (parents precede children), so node i's keys stop at P + i + 1.  All
 // arithmetic is fp32; exp is expf.
 //
+// A grid of few tiles (a few nodes, a long prefix) cuts the key axis into
+// slices, one workgroup each: a slice's workgroup writes its rows' (max, sum,
+// unnormalised output) to the workspace, and attn_valu_merge_kernel combines
+// the slices of each row, as the waves of a workgroup are combined.
+//
 // Optional inputs: with a token table the cache row of key position p is
 // req_to_token[b][p] (each lane looks up its own key; the V loop takes key
 // u's row from lane u); with RoPE on, q is rotated as it is staged in LDS,
 // from the per-node (cos, sin) pairs that the RoPE pre-pass stored.
+#include <algorithm>
+
 #include "tv_device.h"
 #include "tv_launch.h"
 
@@ -57,13 +64,15 @@ __global__ void __launch_bounds__(64 * W) attn_valu_tile_kernel(
     const int32_t *__restrict__ prefix_len, const uint64_t *__restrict__ anc, int total_nodes,
     int max_nodes, int max_prefix, int64_t kv_rows, int hq, int hkv, float scale, T *__restrict__ out,
     int32_t *__restrict__ err, const int32_t *__restrict__ table, int64_t table_stride,
-    const float2 *__restrict__ rope_cs) {
+    const float2 *__restrict__ rope_cs, int splits, int keys_per_split, float2 *__restrict__ part_ml,
+    float *__restrict__ part_o) {
     constexpr int CPL = D / 64;  // output channels per lane
     constexpr int ROWS = GQ * R;
     __shared__ float qs[ROWS][D];
     __shared__ float wm[W][ROWS], wl[W][ROWS];
     __shared__ float wacc[W][ROWS][D];
-    const int i0 = blockIdx.x * R;  // first request-local node of the tile
+    const int split = blockIdx.x % splits;  // key-axis slice (0 when unsliced)
+    const int i0 = blockIdx.x / splits * R;  // first request-local node of the tile
     const int h0 = blockIdx.y * GQ; // first query head of the tile
     const int g = h0 / (hq / hkv);  // their KV head (GQ divides the group)
     const int b = blockIdx.z;       // request
@@ -105,7 +114,9 @@ __global__ void __launch_bounds__(64 * W) attn_valu_tile_kernel(
     const T *kbase = k + (int64_t)g * D;
     const T *vbase = v + (int64_t)g * D;
     const int32_t *trow = table ? table + (int64_t)b * table_stride : nullptr;
-    const int nkeys = P + i0 + nr;  // keys of the tile's last node
+    // the slice's keys, up to those of the tile's last node
+    const int kbeg = split * keys_per_split;
+    const int kend = splits > 1 ? min(P + i0 + nr, kbeg + keys_per_split) : P + i0 + nr;
 
     float m[ROWS], l[ROWS], acc[ROWS][CPL];
 #pragma unroll
@@ -116,14 +127,14 @@ __global__ void __launch_bounds__(64 * W) attn_valu_tile_kernel(
         for (int c = 0; c < CPL; ++c) acc[r][c] = 0.f;
     }
 
-    for (int c0 = 64 * wv; c0 < nkeys; c0 += 64 * W) {
+    for (int c0 = kbeg + 64 * wv; c0 < kend; c0 += 64 * W) {
         const int key = c0 + lane;
         // visibility of this lane's key to each node of the tile: the whole
         // prefix, then the node's ancestors (itself included) among the tree
         bool okn[R];
 #pragma unroll
         for (int ri = 0; ri < R; ++ri) {
-            bool ok = ri < nr && key < P + i0 + ri + 1;
+            bool ok = ri < nr && key < kend && key < P + i0 + ri + 1;
             if (ok && key >= P) {
                 const int j = key - P;
                 ok = (anc[(t0 + ri) * words + (j >> 6)] >> (j & 63)) & 1ull;
@@ -135,7 +146,7 @@ __global__ void __launch_bounds__(64 * W) attn_valu_tile_kernel(
         for (int ri = 0; ri < R; ++ri) any = any || okn[ri];
         // cache row of this lane's key (key u's row is read from lane u below)
         int64_t krow = ks + key;
-        if (trow && key < nkeys) {
+        if (trow && key < kend) {
             krow = trow[key];
             if (krow < 0 || krow >= kv_rows) {
                 report(err, TV_DEVERR_BAD_SLOT, b);
@@ -221,64 +232,185 @@ __global__ void __launch_bounds__(64 * W) attn_valu_tile_kernel(
                 o = fmaf(a, wacc[w][r][ch], o);
             }
         }
-        Elem<T>::st(out, ((t0 + r / GQ) * hq + h0 + r % GQ) * D + ch, o / L);
+        const int64_t row = (t0 + r / GQ) * hq + h0 + r % GQ;
+        if (splits == 1) {
+            Elem<T>::st(out, row * D + ch, o / L);
+        } else {
+            // a slice with no visible key writes (-inf, 0, 0)
+            part_o[(row * splits + split) * D + ch] = o;
+            if (ch == 0) part_ml[row * splits + split] = make_float2(M, L);
+        }
     }
 }
 
+// Combines the key-axis slices of each (node, query head) row: one workgroup
+// of D threads per row, one output channel per thread.  M = max of the
+// slices' maxima, out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s (every
+// row sees at least its own node, so the sum is positive).  Requests that the
+// tile kernel rejected (and reported) are skipped here too.
+template <typename T, int D>
+__global__ void __launch_bounds__(D) attn_valu_merge_kernel(
+    const int32_t *__restrict__ cu_nodes, const int32_t *__restrict__ kv_start,
+    const int32_t *__restrict__ prefix_len, int total_nodes, int max_nodes, int max_prefix, int64_t kv_rows,
+    int hq, const int32_t *__restrict__ table, int64_t table_stride, int splits,
+    const float2 *__restrict__ part_ml, const float *__restrict__ part_o, T *__restrict__ out) {
+    const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z, ch = threadIdx.x;
+    int lo;
+    const int n = request_nodes(cu_nodes, b, total_nodes, max_nodes, &lo);
+    const int P = prefix_len[b];
+    const int64_t ks = table ? 0 : kv_start[b];
+    const bool rows_bad = table ? ((int64_t)P + n > table_stride) : (ks < 0 || ks + P + n > kv_rows);
+    if (n < 0 || P < 0 || P > max_prefix || rows_bad || i >= n) return;
+    const int64_t row = ((int64_t)lo + i) * hq + h;
+    const float2 *ml = part_ml + row * splits;
+    const float *po = part_o + row * splits * D + ch;
+    float M = -INFINITY;
+    for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[s].x);
+    float L = 0.f, o = 0.f;
+    for (int s = 0; s < splits; ++s) {
+        const float2 x = ml[s];
+        if (x.y > 0.f) {
+            const float a = expf(x.x - M);
+            L = fmaf(a, x.y, L);
+            o = fmaf(a, po[(int64_t)s * D], o);
+        }
+    }
+    Elem<T>::st(out, row * D + ch, o / L);
+}
+
+// Key-axis slices of a launch: count, keys per slice, and the workspace
+// arrays of the slices' (max, sum) and outputs (null when unsliced).
+struct Slices {
+    int count = 1, keys = 0;
+    float2 *ml = nullptr;
+    float *o = nullptr;
+};
+
 template <typename T, int D, int W, int GQ, int R>
-hipError_t launch_tile(const AttnArgs &a, hipStream_t stream) {
-    dim3 grid((a.max_nodes + R - 1) / R, a.hq / GQ, a.batch);
+hipError_t launch_tile(const AttnArgs &a, const Slices &sl, hipStream_t stream) {
+    dim3 grid((a.max_nodes + R - 1) / R * sl.count, a.hq / GQ, a.batch);
     hipLaunchKernelGGL((attn_valu_tile_kernel<T, D, W, GQ, R>), grid, dim3(64 * W), 0, stream, (const T *)a.q,
                        (const T *)a.k, (const T *)a.v, a.cu_nodes, a.kv_start, a.prefix_len, a.anc,
                        a.total_nodes, a.max_nodes, a.max_prefix, a.kv_rows, a.hq, a.hkv, a.scale,
-                       (T *)a.out, a.err, a.table, a.table_stride, a.rope_cs);
+                       (T *)a.out, a.err, a.table, a.table_stride, a.rope_cs, sl.count, sl.keys, sl.ml, sl.o);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || sl.count == 1) return e;
+    hipLaunchKernelGGL((attn_valu_merge_kernel<T, D>), dim3(a.max_nodes, a.hq, a.batch), dim3(D), 0, stream,
+                       a.cu_nodes, a.kv_start, a.prefix_len, a.total_nodes, a.max_nodes, a.max_prefix,
+                       a.kv_rows, a.hq, a.table, a.table_stride, sl.count, sl.ml, sl.o, (T *)a.out);
     return hipGetLastError();
 }
 // Nodes per tile: the most (4, 2 or 1) that keep R * GQ <= 16 rows (register
 // budget) and still leave kTileMinWgs workgroups for the 256 CUs.  Eight waves
-// per workgroup; sixteen for an untiled grid over a long key axis, where the
-// workgroups are few and each needs more keys in flight (not for GQ 8, whose
+// per workgroup; sixteen for an untiled, unsliced grid over a long key axis,
+// where each workgroup needs more keys in flight (not for GQ 8, whose
 // per-wave partials would fill the LDS).  Measured, fp32, 32 query / 8 KV
 // heads, d 128, us per call (R 1 / R 2 / R 4): 64 nodes over 1024 keys 79 /
 // 78 / 105; 128 nodes over 4096 keys 523 / - / 341; 4 requests of 32 nodes
 // over 2048 keys 276 / - / 195.
 constexpr long kTileMinWgs = 256;
+// A grid of fewer than kTileMinWgs one-node tiles whose key axis holds at
+// least two slices of kMinSliceKeys keys is cut into slices, as many as bring
+// it to kSliceWgs workgroups; its tiles then take as many nodes as the rows
+// allow, since the slices restore the parallelism and larger tiles read each
+// K/V row fewer times.  Measured, fp32, 32 query / 8 KV heads, d 128, us per
+// call (one-node tiles unsliced / sliced / largest tiles sliced): 1 node over
+// 8192 keys 279 / 46 / 46; 7 nodes over 8192 keys 283 / 147 / 95.  Slicing
+// to 512 or 1024 workgroups, or into slices of 128 keys, was slower for
+// every such shape tried except 1 node over 32768 keys (106 against 118).
+constexpr long kSliceWgs = 256;
+constexpr long kMinSliceKeys = 256;
+
+// GQ: the largest divisor of the GQA group size hq / hkv up to 8.
+int group_tile(int G) {
+    for (int x = 8; x > 1; --x)
+        if (G % x == 0) return x;
+    return 1;
+}
+bool sliced_grid(int max_nodes, int max_prefix, int hq, int gq, int batch) {
+    return (long)max_nodes * (hq / gq) * batch < kTileMinWgs &&
+           (long)max_prefix + max_nodes >= 2 * kMinSliceKeys;
+}
+int nodes_per_tile(int max_nodes, int max_prefix, int hq, int gq, int batch) {
+    const long per_node = (long)(hq / gq) * batch;  // workgroups per node of the grid
+    const bool sliced = sliced_grid(max_nodes, max_prefix, hq, gq, batch);
+    for (int r = 4; r > 1; r /= 2) {
+        if (r * gq > 16) continue;
+        if (sliced ? r / 2 < max_nodes : (long)((max_nodes + r - 1) / r) * per_node >= kTileMinWgs) return r;
+    }
+    return 1;
+}
+
 template <typename T, int D, int GQ>
-hipError_t launch_group(const AttnArgs &a, hipStream_t stream) {
-    const long per_node = (long)(a.hq / GQ) * a.batch;  // workgroups per node of the grid
-    auto wgs = [&](int r) { return (long)((a.max_nodes + r - 1) / r) * per_node; };
+hipError_t launch_group(const AttnArgs &a, const Slices &sl, hipStream_t stream) {
+    const int r = nodes_per_tile(a.max_nodes, a.max_prefix, a.hq, GQ, a.batch);
     if constexpr (4 * GQ <= 16) {
-        if (wgs(4) >= kTileMinWgs) return launch_tile<T, D, 8, GQ, 4>(a, stream);
+        if (r == 4) return launch_tile<T, D, 8, GQ, 4>(a, sl, stream);
     }
     if constexpr (2 * GQ <= 16) {
-        if (wgs(2) >= kTileMinWgs) return launch_tile<T, D, 8, GQ, 2>(a, stream);
+        if (r == 2) return launch_tile<T, D, 8, GQ, 2>(a, sl, stream);
     }
     if constexpr (GQ < 8) {
-        if ((int64_t)a.max_prefix + a.max_nodes >= 4096) return launch_tile<T, D, 16, GQ, 1>(a, stream);
+        if (sl.count == 1 && (int64_t)a.max_prefix + a.max_nodes >= 4096)
+            return launch_tile<T, D, 16, GQ, 1>(a, sl, stream);
     }
-    return launch_tile<T, D, 8, GQ, 1>(a, stream);
+    return launch_tile<T, D, 8, GQ, 1>(a, sl, stream);
 }
-// GQ: the largest divisor of the GQA group size hq / hkv up to 8.
 template <typename T, int D>
-hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
-    const int G = a.hq / a.hkv;
-    if (G % 8 == 0) return launch_group<T, D, 8>(a, stream);
-    if (G % 7 == 0) return launch_group<T, D, 7>(a, stream);
-    if (G % 6 == 0) return launch_group<T, D, 6>(a, stream);
-    if (G % 5 == 0) return launch_group<T, D, 5>(a, stream);
-    if (G % 4 == 0) return launch_group<T, D, 4>(a, stream);
-    if (G % 3 == 0) return launch_group<T, D, 3>(a, stream);
-    if (G % 2 == 0) return launch_group<T, D, 2>(a, stream);
-    return launch_group<T, D, 1>(a, stream);
+hipError_t launch_typed(const AttnArgs &a, const Slices &sl, hipStream_t stream) {
+    switch (group_tile(a.hq / a.hkv)) {
+        case 8: return launch_group<T, D, 8>(a, sl, stream);
+        case 7: return launch_group<T, D, 7>(a, sl, stream);
+        case 6: return launch_group<T, D, 6>(a, sl, stream);
+        case 5: return launch_group<T, D, 5>(a, sl, stream);
+        case 4: return launch_group<T, D, 4>(a, sl, stream);
+        case 3: return launch_group<T, D, 3>(a, sl, stream);
+        case 2: return launch_group<T, D, 2>(a, sl, stream);
+        default: return launch_group<T, D, 1>(a, sl, stream);
+    }
 }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-hipError_t launch_attn_valu(const AttnArgs &a, hipStream_t stream) {
+void plan_attn_valu(int batch, int total_nodes, int max_nodes, int max_prefix, int hq, int hkv, int head_dim,
+                    const tv_attn_plan_override *ov, MfmaPlan *plan) {
+    plan->splits = 1;
+    plan->keys_per_split = 0;
+    plan->ws_bytes = 0;
+    if (batch <= 0 || max_nodes <= 0 || total_nodes <= 0 || hkv <= 0 || hq < hkv) return;
+    const int gq = group_tile(hq / hkv);
+    const int r = nodes_per_tile(max_nodes, max_prefix, hq, gq, batch);
+    const long span = (long)max_prefix + max_nodes;  // longest key axis
+    const long wgs = (long)((max_nodes + r - 1) / r) * (hq / gq) * batch;
+    long s = 1;
+    if (ov && ov->splits > 0)
+        s = std::min<long>(ov->splits, (span + 63) / 64);
+    else if (sliced_grid(max_nodes, max_prefix, hq, gq, batch))
+        s = std::min<long>((kSliceWgs + wgs - 1) / wgs, span / kMinSliceKeys);
+    if (s <= 1) return;
+    const long keys = ((span + s - 1) / s + 63) / 64 * 64;  // whole 64-key chunks
+    s = (span + keys - 1) / keys;
+    if (s <= 1) return;
+    plan->splits = (int)s;
+    plan->keys_per_split = (int)keys;
+    const size_t rows = (size_t)total_nodes * hq * s;
+    plan->ws_bytes = align256(rows * sizeof(float2)) + rows * head_dim * sizeof(float);
+}
+
+hipError_t launch_attn_valu(const AttnArgs &a, const MfmaPlan &plan, void *workspace, hipStream_t stream) {
     if (a.batch == 0 || a.max_nodes == 0) return hipSuccess;
     // bf16 calls with work always take the matrix-core kernel
     if (a.dtype != TV_F32) return hipErrorInvalidValue;
-    return a.head_dim == 64 ? launch_typed<float, 64>(a, stream) : launch_typed<float, 128>(a, stream);
+    Slices sl;
+    if (plan.splits > 1) {
+        sl.count = plan.splits;
+        sl.keys = plan.keys_per_split;
+        sl.ml = (float2 *)workspace;
+        sl.o = (float *)((char *)workspace + align256((size_t)a.total_nodes * a.hq * sl.count * sizeof(float2)));
+    }
+    return a.head_dim == 64 ? launch_typed<float, 64>(a, sl, stream) : launch_typed<float, 128>(a, sl, stream);
 }
 
 }  // namespace tv

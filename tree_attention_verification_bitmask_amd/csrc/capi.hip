@@ -63,6 +63,16 @@ bool override_ok(const tv_attn_plan_override *ov) {
            (ov->waves == 0 || ov->waves == 4 || ov->waves == 8);
 }
 
+// The plan of a call: the matrix-core kernel's (bf16), else the vector
+// kernel's key-axis slices (fp32).
+tv::MfmaPlan attn_plan(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_prefix, int32_t hq,
+                       int32_t hkv, int32_t head_dim, tv_dtype dtype, const tv_attn_plan_override *ov) {
+    tv::MfmaPlan plan =
+        tv::plan_attn_mfma(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype, ov);
+    if (!plan.use) tv::plan_attn_valu(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, ov, &plan);
+    return plan;
+}
+
 // The size checks shared by the call and its plan query; fills *plan.
 tv_status attn_plan_checked(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_prefix,
                             int32_t hq, int32_t hkv, int32_t head_dim, tv_dtype dtype,
@@ -70,7 +80,9 @@ tv_status attn_plan_checked(int32_t batch, int32_t total_nodes, int32_t max_node
     tv_status st = check_attn_sizes(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype);
     if (st != TV_OK) return st;
     if (!override_ok(ov)) return TV_ERR_SHAPE;
-    *plan = tv::plan_attn_mfma(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype, ov);
+    *plan = attn_plan(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype, ov);
+    // the vector kernel's grid: (nodes x slices, head tiles, requests)
+    if (!plan->use && (int64_t)max_nodes * plan->splits > INT32_MAX) return TV_ERR_LIMIT;
     if (plan->use) {
         // workgroup and merge-wave indices are int on the device
         const int64_t groups = (int64_t)batch * hkv * plan->splits;
@@ -97,7 +109,7 @@ bool rope_on(const tv_attn_inputs *in) { return in && in->rope_base > 0.f; }
 // pairs (8 bytes per channel pair) at the next 256-byte boundary.
 size_t attn_ws_bytes(const tv::MfmaPlan &plan, const tv_attn_inputs *in, int32_t total_nodes, int32_t head_dim,
                      size_t *rope_off) {
-    const size_t ws = plan.use ? plan.ws_bytes : 0;
+    const size_t ws = plan.ws_bytes;
     const size_t off = (ws + 255) & ~(size_t)255;
     if (rope_off) *rope_off = off;
     if (rope_on(in) && total_nodes > 0) return off + (size_t)total_nodes * (size_t)(head_dim / 2) * 8;
@@ -174,7 +186,7 @@ tv_status attn_launch(const void *q, void *k_cache, const void *v_cache, const i
     a.out = out;
     a.err = err;
     if (plan.use) return launch_status(tv::launch_attn_mfma(a, plan, workspace, (hipStream_t)stream));
-    return launch_status(tv::launch_attn_valu(a, (hipStream_t)stream));
+    return launch_status(tv::launch_attn_valu(a, plan, workspace, (hipStream_t)stream));
 }
 
 // Scratch of tree_attn_verify_noalloc: one copy per GPU, for the whole
@@ -253,7 +265,7 @@ size_t tree_attn_verify_workspace_size_ex(int32_t batch, int32_t total_nodes, in
         return 0;
     if (!override_ok(ov) || !inputs_ok(in)) return 0;
     const tv::MfmaPlan plan =
-        tv::plan_attn_mfma(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype, ov);
+        attn_plan(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype, ov);
     return attn_ws_bytes(plan, in, total_nodes, head_dim, nullptr);
 }
 
@@ -275,11 +287,11 @@ tv_status tree_attn_verify_plan(int32_t batch, int32_t total_nodes, int32_t max_
     info[0] = plan.use ? 1 : 0;
     info[1] = plan.use ? plan.rows_per_tile : 0;
     info[2] = plan.use ? plan.row_tiles : 0;
-    info[3] = plan.use ? plan.splits : 0;
-    info[4] = plan.use ? plan.keys_per_split : 0;
+    info[3] = plan.splits;
+    info[4] = plan.keys_per_split;
     info[5] = plan.use ? (plan.balanced ? 2 : plan.table ? 1 : 0) : 0;
     info[6] = plan.use ? tv::attn_mfma_lookahead(plan) : 0;
-    info[7] = plan.use ? (int32_t)(plan.ws_bytes > (size_t)INT32_MAX ? INT32_MAX : plan.ws_bytes) : 0;
+    info[7] = (int32_t)(plan.ws_bytes > (size_t)INT32_MAX ? INT32_MAX : plan.ws_bytes);
     return TV_OK;
 }
 
@@ -319,12 +331,12 @@ tv_status tree_attn_verify_noalloc(const void *q, const void *k_cache, const voi
                                            total_nodes, max_nodes, max_prefix, kv_rows, hq, hkv, head_dim, scale,
                                            dtype, nullptr, out, nullptr, &plan);
     if (st != TV_OK) return st;
-    if (plan.use && plan.ws_bytes > (size_t)TV_NOALLOC_SCRATCH_BYTES) return TV_ERR_SCRATCH;
+    if (plan.ws_bytes > (size_t)TV_NOALLOC_SCRATCH_BYTES) return TV_ERR_SCRATCH;
     if (batch == 0 || total_nodes == 0) return TV_OK;
     // The current device's buffer (looked up once per device) when the plan
     // needs a workspace at all.
     void *ws = nullptr;
-    if (plan.use && plan.ws_bytes > 0 && scratch_address(&ws) != hipSuccess) return TV_ERR_LAUNCH;
+    if (plan.ws_bytes > 0 && scratch_address(&ws) != hipSuccess) return TV_ERR_LAUNCH;
     return attn_launch(q, const_cast<void *>(k_cache), v_cache, cu_nodes, kv_start, prefix_len, anc_bits, batch,
                        total_nodes, max_nodes, max_prefix, kv_rows, hq, hkv, head_dim, scale, dtype, nullptr, out, ws,
                        0, err, plan, stream);

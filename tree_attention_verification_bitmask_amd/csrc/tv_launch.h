@@ -99,9 +99,6 @@ struct AttnArgs {
     const float2 *rope_cs = nullptr;
 };
 
-// Generic VALU path: one wavefront per (node, query head); fp32 or bf16.
-hipError_t launch_attn_valu(const AttnArgs &a, hipStream_t stream);
-
 // Plan of the MFMA path (split over the key axis, fp32 partials, combine).
 struct MfmaPlan {
     bool use = false;      // MFMA path selected for these sizes
@@ -125,5 +122,13 @@ MfmaPlan plan_attn_mfma(int batch, int total_nodes, int max_nodes, int max_prefi
 int attn_mfma_lookahead(const MfmaPlan &plan);
 hipError_t launch_attn_mfma(const AttnArgs &a, const MfmaPlan &plan, void *workspace,
                             hipStream_t stream);
+
+// fp32 path (vector units): one workgroup per tile of nodes x query heads of
+// one KV head.  plan_attn_valu fills splits, keys_per_split and ws_bytes of a
+// plan that does not use the matrix cores: splits > 1 cuts the key axis into
+// slices whose partials the workspace holds (a merge kernel combines them).
+void plan_attn_valu(int batch, int total_nodes, int max_nodes, int max_prefix, int hq, int hkv, int head_dim,
+                    const tv_attn_plan_override *ov, MfmaPlan *plan);
+hipError_t launch_attn_valu(const AttnArgs &a, const MfmaPlan &plan, void *workspace, hipStream_t stream);
 
 }  // namespace tv
