@@ -102,6 +102,16 @@ def test_workspace_sizes(L):
     for B, T, n, P in ((1, 64, 64, 1024), (1, 128, 128, 4096), (1, 256, 256, 8192), (8, 1024, 128, 8192)):
         ws = L.tree_attn_verify_workspace_size(B, T, n, P, 32, 8, 128, 1)
         assert ws % 8 == 0 and ws >= 8 * 4 * n * 264
+    # fp32 grids of few tiles over a long key axis are cut into key-axis
+    # slices: (max, sum) and d outputs per (node, query head, slice), in whole
+    # 64-key chunks; one node at 32/8 heads over 8192 keys takes 26 slices of
+    # 320 keys (8 head tiles x 26 = 208 workgroups)
+    for B, T, n, P, d, S in ((1, 1, 1, 8192, 128, 26), (1, 3, 3, 16384, 128, 29), (1, 6, 6, 5000, 64, 16)):
+        rows = T * 32 * S
+        assert L.tree_attn_verify_workspace_size(B, T, n, P, 32, 8, d, 0) == (rows * 8 + 255) // 256 * 256 + rows * d * 4
+    info = (C.c_int32 * 8)()
+    assert L.tree_attn_verify_plan(1, 1, 1, 8192, 32, 8, 128, 0, None, info) == OK
+    assert list(info) == [0, 0, 0, 26, 320, 0, 0, 432640]
     # invalid sizes report 0
     assert L.tree_attn_verify_workspace_size(1, 16, 16, 128, 3, 2, 64, 1) == 0
 
