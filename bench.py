@@ -13,7 +13,9 @@ head layout (32 query / 8 KV heads, head_dim 128) with ragged prefixes of
 run then measures the two other Qwen3-8B-shaped layers, c3 (prefix 4096,
 128-node best-first tree) and c4 (prefix 8192, 256-node width-first tree), the
 same way and reports them under "per_config"; --secondary none skips them and
---workload picks another headline.
+--workload picks another headline.  --dtype f32 runs the same workloads with
+fp32 inputs (the vector kernel; roofline against the fp32 vector peak when the
+call is compute-bound there).
 
 Timing:
   * cold cache: inputs rotate over R copies with R x footprint >= 512 MiB, so
@@ -250,6 +252,9 @@ def main(argv=None):
                     help="comma-separated workloads measured after the headline and reported under "
                          "per_config (default c3,c4; 'none' for none)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--dtype", default="config", choices=("config", "f32"),
+                    help="element type of the attention inputs: the workload's own (config), or fp32 "
+                         "(the vector kernel, roofline against the fp32 vector peak)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--waves", type=int, default=0,
                     help="tuning: plan override for tree_attn_verify, waves per workgroup (4 or 8; 0 = library)")
@@ -341,7 +346,7 @@ def main(argv=None):
     lines = {}
     for name in names:
         seed = args.seed if name == args.workload else 0
-        wl = W.make_workload(name, seed=seed, force_path=True)
+        wl = W.make_workload(name, seed=seed, force_path=True, **dtype_override(args))
         lines[name] = time_pass(args, torch, BND, L, dev, wl, args.steps, args.warmup)
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
@@ -367,10 +372,14 @@ def main(argv=None):
                    "roofline": ln["roofline"]}
             for name, ln in lines.items()}
     if not args.no_cpu_baseline:
-        wl = W.make_workload(args.workload, seed=args.seed, force_path=True)
+        wl = W.make_workload(args.workload, seed=args.seed, force_path=True, **dtype_override(args))
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def dtype_override(args) -> dict:
+    return {} if args.dtype == "config" else {"dtype": args.dtype}
 
 
 def time_pass(args, torch, BND, L, dev, wl, steps: int, warmup: int) -> dict:
@@ -527,13 +536,20 @@ def time_pass(args, torch, BND, L, dev, wl, steps: int, warmup: int) -> dict:
     byts, flops = algorithmic_work(wl)
     ai = flops / byts
     ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    # fp32 runs on the vector units: 256 CUs x 4 SIMDs x 16 lanes x 2 flops
+    # per fused multiply-add x 2.4 GHz = 157.3 TFLOP/s
+    valu_ridge = FP32_VECTOR_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if wl.dtype == "bf16" and ai >= ridge:
         roof = {"bound": "mfma", "achieved": flops / (attn_us * 1e-6) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    elif wl.dtype == "f32" and ai >= valu_ridge:
+        roof = {"bound": "alu", "achieved": flops / (attn_us * 1e-6) / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": byts / (attn_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    traffic, tdetail = load_traffic(wl.name)
+    # (the committed counter summaries are of the bf16 kernel)
+    traffic, tdetail = load_traffic(wl.name) if wl.dtype == "bf16" else (None, "no counter summary for fp32")
     roof["traffic"] = traffic
     roof["traffic_detail"] = tdetail
     roof.update({"kernel": "tree_attn_verify", "avg_us": attn_us,
