@@ -526,6 +526,36 @@ def test_attn_device_error_in_batch(order):
                       stated=True, what="batch with a bad request")
 
 
+@pytest.mark.parametrize("splits", [0, 5])
+def test_attn_fp32_sliced_bad_request(splits):
+    """fp32 with the key axis in slices (the plan's own for a few nodes over a
+    long prefix, and a fixed count): a request whose prefix_len exceeds
+    max_prefix is reported, and neither the slice kernel nor the merge writes
+    its rows (they keep the sentinel); the other requests match the oracle."""
+    announce(f"attn fp32 sliced, bad request, splits {splits}")
+    trees = [W.random_tree(np.random.default_rng(70), 5, 16), W.chain_tree(4), W.random_tree(np.random.default_rng(71), 6, 16)]
+    wl = W.make_from_trees(trees, [3000, 5000, 1200], hq=8, hkv=2, d=128, dtype="f32", seed=7, values="qwen")
+    maxp = 3000  # request 1 (prefix 5000) is beyond it
+    plan = B().tree_attn_verify_plan(wl.batch, wl.total_nodes, wl.max_nodes, maxp, wl.hq, wl.hkv, wl.d, B().TV_F32,
+                                     splits=splits)
+    assert plan["splits"] > 1
+    d = dev_workload(wl)
+    anc, _, _, merr = B().tree_mask_build(d["parent"], d["cu"], d["P"], wl.max_nodes, 64)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.full((wl.total_nodes, wl.hq, wl.d), -123.0, dtype=torch.float32, device="cuda")
+    B().tree_attn_verify(d["q"], d["k"], d["v"], d["cu"], d["ks"], d["P"], anc, wl.max_nodes, maxp, out=out,
+                         err=err, splits=splits)
+    torch.cuda.synchronize()
+    assert int(merr.item()) == 0
+    assert int(err.item()) == (O.ERR_BAD_REQUEST << 24) | 1
+    got = to_np(out)
+    lo, hi = int(wl.cu_nodes[1]), int(wl.cu_nodes[2])
+    assert (got[lo:hi] == -123.0).all()
+    rows = [(t, h) for t in range(wl.total_nodes) if not lo <= t < hi for h in range(wl.hq)]
+    assert_attn_close(np.stack([got[t, h] for t, h in rows]), *oracle_attn(wl, rows=rows), "f32",
+                      stated=True, what="fp32 sliced batch with a bad request")
+
+
 # ---------------------------------------------------------------------------
 # tree_accept_greedy and kv_compact_path
 # ---------------------------------------------------------------------------
