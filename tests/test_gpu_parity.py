@@ -526,6 +526,25 @@ def test_attn_device_error_in_batch(order):
                       stated=True, what="batch with a bad request")
 
 
+@pytest.mark.parametrize("seed", [0, 1])
+def test_attn_fp32_large_batch(seed):
+    """c5's shapes with fp32 inputs: a grid of 2016 tiles of 4 nodes, which the
+    vector kernel runs as 4-wave workgroups; sampled rows against the oracle."""
+    announce(f"attn fp32 c5 shapes, seed {seed}")
+    wl = W.make_workload("c5", seed=seed, dtype="f32")
+    d = dev_workload(wl)
+    anc, _, _, merr = B().tree_mask_build(d["parent"], d["cu"], d["P"], wl.max_nodes, wl.max_depth)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = B().tree_attn_verify(d["q"], d["k"], d["v"], d["cu"], d["ks"], d["P"], anc, wl.max_nodes, wl.max_prefix,
+                               err=err)
+    torch.cuda.synchronize()
+    assert int(merr.item()) == 0 and int(err.item()) == 0
+    rows = sample_rows(wl, 200, seed)
+    got = to_np(out)
+    assert_attn_close(np.stack([got[t, h] for t, h in rows]), *oracle_attn(wl, rows=rows), "f32",
+                      stated=True, what=f"fp32 c5 seed {seed}")
+
+
 @pytest.mark.parametrize("splits", [0, 5])
 def test_attn_fp32_sliced_bad_request(splits):
     """fp32 with the key axis in slices (the plan's own for a few nodes over a

@@ -309,6 +309,12 @@ hipError_t launch_tile(const AttnArgs &a, const Slices &sl, hipStream_t stream) 
 // 78 / 105; 128 nodes over 4096 keys 523 / - / 341; 4 requests of 32 nodes
 // over 2048 keys 276 / - / 195.
 constexpr long kTileMinWgs = 256;
+// A grid of at least kManyWgs 4-node tiles runs them as 4-wave workgroups:
+// at about 150 VGPRs a CU then holds three workgroups (12 waves) instead of
+// one 8-wave workgroup, and hides more of the K/V reads' latency.  Measured,
+// fp32, c5 (eight requests, prefixes 2048-8192, 32-128 nodes): 3324 us with
+// 8 waves, 2269 us with 4; c3 and c4 (256 and 512 workgroups) keep 8.
+constexpr long kManyWgs = 768;
 // A grid of fewer than kTileMinWgs one-node tiles whose key axis holds at
 // least two slices of kMinSliceKeys keys is cut into slices, as many as bring
 // it to kSliceWgs workgroups; its tiles then take as many nodes as the rows
@@ -345,7 +351,11 @@ template <typename T, int D, int GQ>
 hipError_t launch_group(const AttnArgs &a, const Slices &sl, hipStream_t stream) {
     const int r = nodes_per_tile(a.max_nodes, a.max_prefix, a.hq, GQ, a.batch);
     if constexpr (4 * GQ <= 16) {
-        if (r == 4) return launch_tile<T, D, 8, GQ, 4>(a, sl, stream);
+        if (r == 4) {
+            if ((long)((a.max_nodes + 3) / 4) * (a.hq / GQ) * a.batch >= kManyWgs)
+                return launch_tile<T, D, 4, GQ, 4>(a, sl, stream);
+            return launch_tile<T, D, 8, GQ, 4>(a, sl, stream);
+        }
     }
     if constexpr (2 * GQ <= 16) {
         if (r == 2) return launch_tile<T, D, 8, GQ, 2>(a, sl, stream);
