@@ -206,9 +206,13 @@ def test_attn_inputs_checked(L):
     assert L.tree_attn_verify_workspace_size_ex(*sizes, C.byref(inp(tab=FA, stride=9000)), None) == base
     assert L.tree_attn_verify_workspace_size_ex(*sizes, C.byref(inp(res=1)), None) == 0
     assert ex(inp(base=1e6), ws=rope - 1) == WS
-    # the vector path (fp32) needs only the pairs
+    # the vector path (fp32): its key-axis slice partials (c3's 256 tiles take 3
+    # slices), then the pairs at a 256-byte boundary
     f32 = (1, T, 128, 4096, 32, 8, d, 0)
-    assert L.tree_attn_verify_workspace_size_ex(*f32, C.byref(inp(base=1e6)), None) == T * (d // 2) * 8
+    base32 = L.tree_attn_verify_workspace_size(*f32)
+    assert base32 == (T * 32 * 3 * 8 + 255) // 256 * 256 + T * 32 * 3 * d * 4
+    assert L.tree_attn_verify_workspace_size_ex(*f32, C.byref(inp(base=1e6)), None) == \
+        ((base32 + 255) // 256 * 256) + T * (d // 2) * 8
 
 
 def test_attn_noalloc_host_checks(L):

@@ -309,12 +309,16 @@ hipError_t launch_tile(const AttnArgs &a, const Slices &sl, hipStream_t stream) 
 // 78 / 105; 128 nodes over 4096 keys 523 / - / 341; 4 requests of 32 nodes
 // over 2048 keys 276 / - / 195.
 constexpr long kTileMinWgs = 256;
-// A grid of at least kManyWgs 4-node tiles runs them as 4-wave workgroups:
-// at about 150 VGPRs a CU then holds three workgroups (12 waves) instead of
-// one 8-wave workgroup, and hides more of the K/V reads' latency.  Measured,
-// fp32, c5 (eight requests, prefixes 2048-8192, 32-128 nodes): 3324 us with
-// 8 waves, 2269 us with 4; c3 and c4 (256 and 512 workgroups) keep 8.
+// A grid of at least kManyWgs 4-node tiles (slices counted) runs them as
+// 4-wave workgroups: at about 150 VGPRs a CU then holds three workgroups (12
+// waves) instead of one 8-wave workgroup, and hides more of the K/V reads'
+// latency.  A grid of at most kTileMinWgs such tiles over a key axis of at
+// least 2 * kMinOccSliceKeys is cut into slices to get there.  Measured, fp32,
+// us per call: c5 (2016 tiles) 3324 with 8 waves, 2269 with 4; c3 (256 tiles,
+// 4224 keys) 404 unsliced, 336 in 3 slices; c4 (512 tiles) 1573 unsliced,
+// 1608 in 2 slices, so it stays unsliced with 8 waves.
 constexpr long kManyWgs = 768;
+constexpr long kMinOccSliceKeys = 1024;
 // A grid of fewer than kTileMinWgs one-node tiles whose key axis holds at
 // least two slices of kMinSliceKeys keys is cut into slices, as many as bring
 // it to kSliceWgs workgroups; its tiles then take as many nodes as the rows
@@ -352,7 +356,7 @@ hipError_t launch_group(const AttnArgs &a, const Slices &sl, hipStream_t stream)
     const int r = nodes_per_tile(a.max_nodes, a.max_prefix, a.hq, GQ, a.batch);
     if constexpr (4 * GQ <= 16) {
         if (r == 4) {
-            if ((long)((a.max_nodes + 3) / 4) * (a.hq / GQ) * a.batch >= kManyWgs)
+            if ((long)((a.max_nodes + 3) / 4) * (a.hq / GQ) * a.batch * sl.count >= kManyWgs)
                 return launch_tile<T, D, 4, GQ, 4>(a, sl, stream);
             return launch_tile<T, D, 8, GQ, 4>(a, sl, stream);
         }
@@ -399,6 +403,8 @@ void plan_attn_valu(int batch, int total_nodes, int max_nodes, int max_prefix, i
         s = std::min<long>(ov->splits, (span + 63) / 64);
     else if (sliced_grid(max_nodes, max_prefix, hq, gq, batch))
         s = std::min<long>((kSliceWgs + wgs - 1) / wgs, span / kMinSliceKeys);
+    else if (r == 4 && wgs <= kTileMinWgs && span >= 2 * kMinOccSliceKeys)
+        s = std::min<long>((kManyWgs + wgs - 1) / wgs, span / kMinOccSliceKeys);
     if (s <= 1) return;
     const long keys = ((span + s - 1) / s + 63) / 64 * 64;  // whole 64-key chunks
     s = (span + keys - 1) / keys;
