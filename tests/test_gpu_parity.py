@@ -526,12 +526,17 @@ def test_attn_device_error_in_batch(order):
                       stated=True, what="batch with a bad request")
 
 
-@pytest.mark.parametrize("seed", [0, 1])
-def test_attn_fp32_large_batch(seed):
-    """c5's shapes with fp32 inputs: a grid of 2016 tiles of 4 nodes, which the
-    vector kernel runs as 4-wave workgroups; sampled rows against the oracle."""
-    announce(f"attn fp32 c5 shapes, seed {seed}")
-    wl = W.make_workload("c5", seed=seed, dtype="f32")
+@pytest.mark.parametrize("name,seed", [("c5", 0), ("c5", 1), ("c3", 0), ("c3", 2)])
+def test_attn_fp32_large_batch(name, seed):
+    """Qwen3-shaped layers with fp32 inputs.  c5: a grid of 2016 tiles of 4
+    nodes, which the vector kernel runs as 4-wave workgroups.  c3: 256 tiles,
+    each key axis cut into 3 slices of 4-wave workgroups and merged.  Sampled
+    rows against the oracle."""
+    announce(f"attn fp32 {name} shapes, seed {seed}")
+    wl = W.make_workload(name, seed=seed, dtype="f32")
+    plan = B().tree_attn_verify_plan(wl.batch, wl.total_nodes, wl.max_nodes, wl.max_prefix, wl.hq, wl.hkv, wl.d,
+                                     B().TV_F32)
+    assert plan["mfma"] == 0 and plan["splits"] == (3 if name == "c3" else 1)
     d = dev_workload(wl)
     anc, _, _, merr = B().tree_mask_build(d["parent"], d["cu"], d["P"], wl.max_nodes, wl.max_depth)
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -542,7 +547,7 @@ def test_attn_fp32_large_batch(seed):
     rows = sample_rows(wl, 200, seed)
     got = to_np(out)
     assert_attn_close(np.stack([got[t, h] for t, h in rows]), *oracle_attn(wl, rows=rows), "f32",
-                      stated=True, what=f"fp32 c5 seed {seed}")
+                      stated=True, what=f"fp32 {name} seed {seed}")
 
 
 @pytest.mark.parametrize("splits", [0, 5])
